@@ -1,0 +1,411 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every check here is independent of the oracle's own formulas: values printed
+on the pages (tests/golden), closed forms, special cases, a library routine
+(torch's scaled_dot_product_attention in float64), brute force with scalar
+Python arithmetic, and invariants the pages state.  The last group plants
+plausible mistakes in a copy of the oracle and checks that some pin fails.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import harness as OH
+from oracle import pa_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- sizing
+
+def test_sizing_matches_printed_figures():
+    g = _golden("sizing.json")
+    m = g["model"]
+    per_tok = O.kv_bytes_per_token(m["layers"], m["kv_heads"], m["head_dim"], m["bytes_per_elem"])
+    assert per_tok == g["bytes_per_token"] == 327680
+    prompt = O.kv_cache_bytes(g["prompt_tokens"], m["layers"], m["kv_heads"], m["head_dim"], m["bytes_per_elem"])
+    assert prompt == 1_342_177_280
+    assert round(prompt / 1e9, 2) == g["prompt_gb_decimal_2dp"]
+    long = O.kv_cache_bytes(g["long_context_tokens"], m["layers"], m["kv_heads"], m["head_dim"], m["bytes_per_elem"])
+    assert long / 2**30 == 39.0625
+    assert round(long / 2**30, 2) == g["long_context_gib_2dp"]
+
+
+def test_sizing_per_layer_and_dtype():
+    # one layer of the decode configs: 8 KV heads x 128 dims
+    assert O.kv_bytes_per_token(1, 8, 128, 2) == 4096
+    assert O.kv_bytes_per_token(1, 8, 128, 1) == 2048
+    assert O.kv_bytes_per_token(1, 4, 64, 2) == 1024
+
+
+# ---------------------------------------------------------------- block table
+
+def test_worked_block_table_example():
+    g = _golden("block_table_example.json")
+    bs = g["tokens_per_block"]
+    table = [g["block_table"][str(j)] for j in range(len(g["logical_blocks"]))]
+    pos = 0
+    for j, toks in enumerate(g["logical_blocks"]):
+        for r, name in enumerate(toks):
+            assert name == f"t{pos}"
+            slot = O.slot_of(table, pos, bs)
+            assert slot // bs == g["block_table"][str(j)]
+            assert slot % bs == r
+            pos += 1
+    assert O.slot_of(table, 9, bs) == 42 * 4 + 1 == 169
+
+
+def test_gather_follows_the_table_of_the_worked_example():
+    # a 50-block pool whose row r of block b holds the value 1000*b + r
+    pool = np.zeros((50, 1, 4, 1), np.float16)
+    for b in range(50):
+        for r in range(4):
+            pool[b, 0, r, 0] = b * 10 + r
+    rows = O.gather_kv(pool, [17, 3, 42], 10)[:, 0, 0].astype(int).tolist()
+    assert rows == [170, 171, 172, 173, 30, 31, 32, 33, 420, 421]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "fp8"])
+def test_scatter_gather_round_trip_is_bit_exact(dtype):
+    rng = np.random.default_rng(7)
+    Hkv, D, bs = 3, 16, 8
+    lens = [1, 7, 8, 9, 23]
+    nblk = sum((L + bs - 1) // bs for L in lens)
+    perm = rng.permutation(nblk + 5)
+    kc = O.new_pool(nblk + 5, Hkv, bs, D, dtype)
+    vc = O.new_pool(nblk + 5, Hkv, bs, D, dtype)
+    src = []
+    off = 0
+    tables = []
+    for L in lens:
+        n = (L + bs - 1) // bs
+        tables.append(perm[off:off + n])
+        off += n
+        if dtype == "fp8":
+            k = rng.integers(0, 256, (L, Hkv, D)).astype(np.uint8)
+            k[(k & 0x7F) == 0x7F] = 0  # keep NaN codes out of the source
+            v = k[::-1].copy()
+        else:
+            k = W.to_storage(rng.standard_normal((L, Hkv, D), dtype=np.float32), dtype)
+            v = W.to_storage(rng.standard_normal((L, Hkv, D), dtype=np.float32), dtype)
+        src.append((k, v))
+        slots = O.slots_for(tables[-1], 0, L, bs)
+        # an fp8 source is already coded: store as bytes
+        kc[slots // bs, :, slots % bs, :] = k
+        vc[slots // bs, :, slots % bs, :] = v
+    for (k, v), t, L in zip(src, tables, lens):
+        assert O.gather_kv(kc, t, L).tobytes() == k.tobytes()
+        assert O.gather_kv(vc, t, L).tobytes() == v.tobytes()
+
+
+def test_reshape_and_cache_skips_negative_slots_and_writes_rows():
+    kc = O.new_pool(4, 2, 4, 3, "f16")
+    vc = O.new_pool(4, 2, 4, 3, "f16")
+    key = np.arange(3 * 2 * 3, dtype=np.float16).reshape(3, 2, 3)
+    val = -key
+    O.reshape_and_cache(key, val, kc, vc, [5, -1, 12], 4, "f16")
+    assert np.array_equal(kc[1, :, 1, :], key[0]) and np.array_equal(vc[1, :, 1, :], val[0])
+    assert np.array_equal(kc[3, :, 0, :], key[2])
+    assert int(np.isnan(kc).sum()) == kc.size - 2 * 2 * 3
+
+
+def test_tail_waste_closed_form():
+    lens = np.array([1, 15, 16, 17, 2304])
+    w = O.tail_waste(lens, 16)
+    assert w == (15 + 1 + 0 + 15 + 0) / (16 + 16 + 16 + 32 + 2304)
+    # only the last block's tail: each sequence wastes < bs slots
+    w2 = W.llama8b()
+    assert O.tail_waste(w2.context_lens, 16) < 16 / 512
+    assert O.tail_waste(w2.context_lens, 16) < 0.04
+
+
+# ---------------------------------------------------------------- attention
+
+def _tiny_pools():
+    w = W.tiny()
+    kc, vc = OH.build_pools(w)
+    return w, kc, vc
+
+
+def test_context_of_one_returns_that_value_row():
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((4, 8))
+    k = rng.standard_normal((1, 2, 8))
+    v = rng.standard_normal((1, 2, 8))
+    out = O.attend(q, k, v, 0.3, 2)
+    assert np.array_equal(out, v[0].repeat(2, axis=0))
+
+
+@pytest.mark.parametrize("zero", ["q", "scale"])
+def test_uniform_weights_give_the_mean_of_values(zero):
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((6, 16))
+    k = rng.standard_normal((37, 3, 16))
+    v = rng.standard_normal((37, 3, 16))
+    if zero == "q":
+        q[:] = 0
+        out = O.attend(q, k, v, 0.25, 2)
+    else:
+        out = O.attend(q, k, v, 0.0, 2)
+    mean = v.mean(axis=0).repeat(2, axis=0)
+    assert np.max(np.abs(out - mean)) <= 1e-15
+
+
+def test_empty_context_gives_zeros():
+    out = O.attend(np.ones((4, 8)), np.zeros((0, 2, 8)), np.zeros((0, 2, 8)), 1.0, 2)
+    assert np.array_equal(out, np.zeros((4, 8)))
+
+
+def _sdpa(q, k, v, scale, group):
+    """torch float64 scaled_dot_product_attention, KV heads repeated per group."""
+    qt = torch.from_numpy(q)[:, None, :]  # [Hq, 1, D]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(group, dim=0)  # [Hq, L, D]
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[:, 0, :].numpy()
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_attention_matches_torch_sdpa_float64(group):
+    rng = np.random.default_rng(10 + group)
+    Hkv, D = 2, 32
+    for L in (1, 5, 64, 301):
+        q = rng.standard_normal((Hkv * group, D))
+        k = rng.standard_normal((L, Hkv, D)) * 2
+        v = rng.standard_normal((L, Hkv, D))
+        out = O.attend(q, k, v, 1 / math.sqrt(D), group)
+        ref = _sdpa(q, k, v, 1 / math.sqrt(D), group)
+        assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def test_tiny_decode_matches_sdpa_over_explicit_block_walk():
+    w, kc, vc = _tiny_pools()
+    out = OH.decode(w, kc, vc)
+    q = O.widen(w.query(), w.q_dtype)
+    for s in range(w.B):
+        L = int(w.context_lens[s])
+        # explicit walk: one row at a time through the table
+        k = np.stack([kc[w.block_tables[s][t // w.bs], :, t % w.bs, :] for t in range(L)]).astype(np.float64)
+        v = np.stack([vc[w.block_tables[s][t // w.bs], :, t % w.bs, :] for t in range(L)]).astype(np.float64)
+        ref = _sdpa(q[s], k, v, w.scale, w.group)
+        assert np.max(np.abs(out[s] - ref)) <= 1e-12
+
+
+def _brute_force(q, k, v, scale, group):
+    """Scalar Python: math.exp and math.fsum only."""
+    Hq, D = len(q), len(q[0])
+    L = len(k)
+    out = []
+    for i in range(Hq):
+        h = i // group
+        sc = [scale * math.fsum(q[i][d] * k[t][h][d] for d in range(D)) for t in range(L)]
+        m = max(sc)
+        e = [math.exp(x - m) for x in sc]
+        z = math.fsum(e)
+        out.append([math.fsum(e[t] * v[t][h][d] for t in range(L)) / z for d in range(D)])
+    return out
+
+
+def test_tiny_decode_matches_brute_force():
+    w, kc, vc = _tiny_pools()
+    out = OH.decode(w, kc, vc)
+    q = O.widen(w.query(), "f16").tolist()
+    for s in range(w.B):
+        L = int(w.context_lens[s])
+        k = [[[float(x) for x in kc[w.block_tables[s][t // 16], h, t % 16, :]] for h in range(4)] for t in range(L)]
+        v = [[[float(x) for x in vc[w.block_tables[s][t // 16], h, t % 16, :]] for h in range(4)] for t in range(L)]
+        ref = np.array(_brute_force(q[s], k, v, w.scale, w.group))
+        assert np.max(np.abs(out[s] - ref)) <= 1e-13
+
+
+def test_tiny_pool_uses_a_permutation_without_reuse():
+    w = W.tiny()
+    assert w.num_blocks == 32
+    used = np.concatenate([w.block_tables[s, :(int(L) + 15) // 16] for s, L in enumerate(w.context_lens)])
+    assert len(used) == 3 + 7 and len(set(used.tolist())) == len(used)
+    assert used.min() >= 0 and used.max() < 32
+
+
+# ---------------------------------------------------------------- invariants the pages state
+
+def test_paged_equals_contiguous_for_any_block_permutation():
+    w = W.custom("perm", 11, [1, 16, 17, 50, 129], 8, 2, 32, 16, "bf16")
+    kc, vc = OH.build_pools(w)
+    paged = OH.decode(w, kc, vc)
+    keys = [w.seq_kv(s)[0] for s in range(w.B)]
+    vals = [w.seq_kv(s)[1] for s in range(w.B)]
+    contig = O.decode_contiguous(w.query(), keys, vals, w.scale, w.group, "bf16", "bf16")
+    assert np.array_equal(paged, contig)
+    # a different permutation of the same pool: identical result
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(w.num_blocks)
+    inv = np.argsort(perm)
+    kc2, vc2 = kc[perm], vc[perm]
+    tables2 = np.where(w.block_tables >= 0, inv[np.maximum(w.block_tables, 0)], -1)
+    out2 = O.decode(w.query(), kc2, vc2, tables2, w.context_lens, w.scale, w.group, "bf16", "bf16")
+    assert np.array_equal(out2, paged)
+
+
+def _small_shared():
+    return W.shared_prefix(seed=99, prompts=2, samples=3, prefix=64, max_tail=40)
+
+
+def test_shared_prefix_tables_equal_private_copies():
+    w = _small_shared()
+    kc, vc = OH.build_pools(w)
+    shared = OH.decode(w, kc, vc)
+    keys = [w.seq_kv(s)[0] for s in range(w.B)]
+    vals = [w.seq_kv(s)[1] for s in range(w.B)]
+    private = O.decode_contiguous(w.query(), keys, vals, w.scale, w.group, "bf16", "bf16")
+    assert np.array_equal(shared, private)
+    # the prompt's full prefix blocks really are shared
+    s0, s1 = 0, 1
+    nfull = 64 // 16
+    assert np.array_equal(w.block_tables[s0, :nfull], w.block_tables[s1, :nfull])
+
+
+def test_copy_on_write_copies_bytes_and_leaves_source():
+    w = _small_shared()
+    kc, vc = OH.build_pools(w)
+    pairs = w.meta["cow_pairs"]
+    assert len(pairs) == 2 * 2
+    kc2, vc2 = kc.copy(), vc.copy()
+    src = int(pairs[0][0])
+    before = kc2[src].tobytes()
+    # copy again onto a fresh block and check it
+    used = set(w.block_tables[w.block_tables >= 0].ravel().tolist())
+    fresh = min(set(range(w.num_blocks)) - used)
+    O.copy_blocks(kc2, vc2, [[src, fresh]])
+    assert kc2[fresh].tobytes() == kc2[src].tobytes() == before
+    assert vc2[fresh].tobytes() == vc2[src].tobytes()
+
+
+def test_cow_isolates_samples_after_divergence():
+    w = _small_shared()
+    kc, vc = OH.build_pools(w)
+    base = OH.decode(w, kc, vc)
+    # overwrite the last sample's rows in its (original) partial block: the
+    # other samples of that prompt hold copies and must not change
+    s_last = w.meta["samples"] - 1
+    nb = (int(w.meta["shared_len"][0]) + 15) // 16
+    blk = w.block_tables[s_last, nb - 1]
+    kc[blk, :, :, :] = np.float16(0).view(np.uint16)  # zero bits
+    out = OH.decode(w, kc, vc)
+    for s in range(w.meta["samples"] - 1):
+        assert np.array_equal(out[s], base[s])
+    assert not np.array_equal(out[s_last], base[s_last])
+
+
+def test_poisoned_slots_are_never_read():
+    for name in ("tiny",):
+        w = W.make(name)
+        kc, vc = OH.build_pools(w, poison=True)
+        assert np.isnan(O.widen(kc, w.cache_dtype)).any()  # the poison is there
+        out = OH.decode(w, kc, vc)
+        assert np.isfinite(out).all()
+
+
+# ---------------------------------------------------------------- fp8 codec
+
+def test_e4m3_decode_table_against_torch_and_spec_points():
+    vals = O.e4m3_values()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(vals), np.isnan(ref))
+    ok = ~np.isnan(vals)
+    assert np.array_equal(vals[ok], ref[ok])
+    assert vals[0x7E] == 448.0 and vals[0x01] == 2.0 ** -9 and vals[0x08] == 2.0 ** -6
+    assert vals[0x80] == 0.0 and math.copysign(1, vals[0x80]) == -1
+    assert np.isnan(vals[0x7F]) and np.isnan(vals[0xFF])
+
+
+def _torch_encode(x_f32, scale):
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = torch.from_numpy(np.asarray(x_f32, np.float32) / np.float32(scale))
+    y = torch.where(torch.isnan(y), y, y.clamp(-448.0, 448.0))
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 4.75 / 448.0, 2.0 ** -4])
+def test_e4m3_encode_exhaustive_against_torch(src, scale):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = bits.view(np.float16).astype(np.float32) if src == "f16" else W.storage_to_f32(bits, "bf16")
+    ours = O.e4m3_encode(x, scale)
+    ref = _torch_encode(x, scale)
+    nan = np.isnan(x)
+    # NaN: sign kept, NaN code
+    assert np.array_equal(ours[nan] & 0x7F, np.full(nan.sum(), 0x7F, np.uint8))
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_e4m3_encode_ties_and_saturation():
+    enc = lambda v: int(O.e4m3_encode(np.array([v], np.float32), 1.0)[0])
+    assert enc(448.0) == 0x7E and enc(464.0) == 0x7E and enc(1e30) == 0x7E and enc(np.inf) == 0x7E
+    assert enc(-np.inf) == 0xFE
+    assert enc(2.0 ** -10) == 0x00  # half of the smallest subnormal: tie to even (0)
+    assert enc(3 * 2.0 ** -10) == 0x02  # 1.5 x smallest: tie to even code 2
+    assert enc(1.0625) == 0x38  # halfway between 1 (0x38) and 1.125 (0x39): even
+    assert enc(1.1875) == 0x3A  # halfway between 1.125 and 1.25: even (0x3A)
+    assert enc(-0.0) == 0x80 and enc(-1e-9) == 0x80
+
+
+def test_round_to_bf16_matches_torch():
+    x = np.random.default_rng(3).standard_normal(10000) * 10.0 ** np.random.default_rng(4).integers(-30, 30, 10000)
+    ours = O.round_to(x, "bf16")
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.uint16).numpy()
+    assert np.array_equal(ours, ref)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _pins_pass(attend):
+    """Run the attention pins against an alternative attend(); True if all hold."""
+    rng = np.random.default_rng(123)
+    try:
+        for group in (1, 4):
+            q = rng.standard_normal((2 * group, 16))
+            k = rng.standard_normal((21, 2, 16))
+            v = rng.standard_normal((21, 2, 16))
+            if np.max(np.abs(attend(q, k, v, 0.25, group) - _sdpa(q, k, v, 0.25, group))) > 1e-12:
+                return False
+            if not np.array_equal(attend(q, k[:1], v[:1], 0.25, group), v[0].repeat(group, axis=0)):
+                return False
+    except Exception:
+        return False
+    return True
+
+
+def test_pins_accept_the_oracle():
+    assert _pins_pass(O.attend)
+
+
+@pytest.mark.parametrize("mistake", ["no_scale", "gqa_modulo", "no_normalize", "k_for_v", "sum_over_heads"])
+def test_pins_catch_planted_mistakes(mistake):
+    def bad(q, k, v, scale, group):
+        Hq, D = q.shape
+        L, Hkv, _ = k.shape
+        out = np.zeros((Hq, D))
+        for i in range(Hq):
+            h = i // group
+            if mistake == "gqa_modulo":
+                h = i % Hkv
+            kk = k[:, h, :]
+            vv = (k if mistake == "k_for_v" else v)[:, h, :]
+            sc = (1.0 if mistake == "no_scale" else scale) * kk @ q[i]
+            sc = sc + sc.max() if mistake == "no_normalize" else sc - sc.max()
+            e = np.exp(sc)
+            if mistake == "sum_over_heads":
+                e = np.exp(scale * k.sum(axis=1) @ q[i] - (scale * k.sum(axis=1) @ q[i]).max())
+            out[i] = (e if mistake == "no_normalize" else e / e.sum()) @ vv
+        return out
+
+    assert not _pins_pass(bad)

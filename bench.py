@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+A step is one pass of the decode hot path over one synthetic batch: append
+the batch's new token rows into their slots (pa_reshape_and_cache), then paged
+decode attention over every sequence's blocks (pa_decode).  The default
+workload is the Llama-3-8B-shaped decode layer: 64 sequences, 32 query / 8 KV
+heads, head_dim 128, bf16, block size 16, context lengths U{512..4096}.
+
+Reported: KV GB/s (algorithmic K+V bytes of the batch per step time) and
+sequence-heads per second, the decode call's roofline fraction against the
+8 TB/s HBM peak, and the CPU oracle on a bounded sample of the same batch.
+
+    python bench.py [--steps K] [--warmup W] [--config llama8b|llama70b|...]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "pa_decode KV GB/s (fraction of HBM peak) + seq·heads/s on 1 MI355X"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle over whole sequences of the same batch, until the time budget is spent."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import harness as OH
+    from oracle import pa_oracle as O
+
+    log("cpu baseline: building oracle pools")
+    kc, vc = OH.build_pools(w)
+    q = w.query()
+    done_seqs = 0
+    kv = 0
+    t_total = 0.0
+    passes = 0
+    while t_total < budget_s and passes < 50:
+        for s in range(w.B):
+            t0 = time.perf_counter()
+            O.decode_one(q[s], kc, vc, w.block_tables[s], int(w.context_lens[s]), w.scale, w.group,
+                         w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale)
+            t_total += time.perf_counter() - t0
+            done_seqs += 1
+            kv += int(w.context_lens[s]) * w.Hkv * w.D * 2 * (1 if w.cache_dtype == "fp8" else 2)
+            if t_total >= budget_s:
+                break
+        passes += 1
+    threads = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {
+        "value": kv / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done_seqs} whole sequences of the same batch ({kv} KV bytes) in {t_total:.1f} s of "
+                  f"fp64 NumPy gather + attention; seq*heads/s = {done_seqs * w.Hq / t_total:.1f}; cpu: {cpu}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama8b")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict L2/MALL between steps")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path is single-GPU by design)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_342_amd as pa
+    import workloads as W
+    from workloads.device import DeviceBatch
+
+    dev = torch.device("cuda:0")
+    w = W.make(args.config)
+    log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} bs={w.bs} cache={w.cache_dtype} "
+        f"sum(L)={int(w.context_lens.sum())}")
+    batch = DeviceBatch(w, device=dev, skip_last_append=True)
+    k_new, v_new, slots_new = batch.rows_for(w.ops[-1])
+    log("pools filled")
+    out = torch.empty((w.B, w.Hq, w.D), dtype=batch.q.dtype, device=dev)
+    ws_bytes = pa.decode_workspace_size(w.B, w.Hkv, w.group, w.D, w.bs, w.max_context_len)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def append():
+        pa.reshape_and_cache(k_new, v_new, batch.kc, batch.vc, slots_new, w.k_scale, w.v_scale)
+
+    def decode():
+        pa.decode(batch.q, batch.kc, batch.vc, batch.tables, batch.lens, w.scale, max_context_len=w.max_context_len,
+                  k_scale=w.k_scale, v_scale=w.v_scale, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        append()
+        decode()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)  # evicts L2 and the MALL; outside the step's events
+        ev[i][0].record()
+        append()
+        ev[i][1].record()
+        decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    ms_step = float(np.mean(step_ms))
+    ms_dec = float(np.mean(dec_ms))
+    kv_bytes = w.kv_bytes()
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = kv_bytes / (ms_dec * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us (median {np.median(step_ms) * 1e3:.1f}), decode {ms_dec * 1e3:.1f} us "
+        f"(median {np.median(dec_ms) * 1e3:.1f}), wall/step incl. flush {wall / args.steps * 1e3:.3f} ms")
+
+    cpu = None
+    if args.cpu_budget > 0:
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f16": "f16", "bf16": "bf16", "fp8": "fp8e4m3"}[w.cache_dtype],
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+            "block_size": w.bs, "cache_dtype": w.cache_dtype, "q_dtype": w.q_dtype, "seed": w.seed,
+            "sum_context_len": int(w.context_lens.sum()), "kv_bytes": kv_bytes, "parallelism": "single-gpu",
+            "l2_mall_flush_between_steps": flush is not None,
+        },
+        "seq_heads_per_s": round(w.B * w.Hq / (ms_step * 1e-3), 1),
+        "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
+        "decode_us": round(ms_dec * 1e3, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "pa_decode (work-list + partition + reduce kernels, one call)",
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * pa.h - C ABI of the paged decode-attention library (libpa.so) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library implements the GPU hot path of PagedAttention decode:
+ *   - pa_reshape_and_cache: append new tokens' key/value rows into the slots
+ *     the block manager assigned them (the KV cache grows by one row per
+ *     generated token; blocks are allocated on demand):
+ *       "Paged Attention and Memory Efficiency in Production LLM Serving",
+ *       sections "Why KV cache memory was the bottleneck ..." and "How
+ *       PagedAttention borrows OS paging ...";
+ *       "PagedAttention in Production", section "Core Principle".
+ *   - pa_decode: one query token per sequence attends over that sequence's
+ *     keys/values, which live in fixed-size physical blocks found through the
+ *     sequence's block table at run time; the result is ordinary softmax
+ *     attention:
+ *       "Paged Attention and Memory Efficiency ...", section "How
+ *       PagedAttention borrows OS paging ...";
+ *       "PagedAttention in Production", section "Relationship with Continuous
+ *       Batching" (flow figure: the attention kernel reads blocks by block
+ *       table);
+ *       "PagedAttention - The KV Cache Problem", section "How It Works".
+ *   - pa_copy_blocks: copy-on-write duplication of a shared block once a
+ *     sequence diverges from a shared prefix:
+ *       "Paged Attention and Memory Efficiency ...", section "How
+ *       PagedAttention borrows OS paging ..." (sharing and copy-on-write);
+ *       "PagedAttention - The KV Cache Problem", section "Why This Matters for
+ *       Production" (copy-on-write for parallel sampling and beam search).
+ *
+ * Conventions shared by every call
+ *   - KV cache layout (one tensor for K, one for V, per layer):
+ *       [num_blocks, num_kv_heads, block_size, head_dim], row-major, so one
+ *       (block, kv head) chunk is block_size*head_dim contiguous elements.
+ *   - Slot of a token = physical_block * block_size + row within the block.
+ *   - Query head i reads KV head i / gqa_group (consecutive grouping).
+ *   - Element dtypes: PA_F16 / PA_BF16 are IEEE half / bfloat16;
+ *     PA_FP8_E4M3 is the OCP E4M3FN 8-bit format (bias 7, max 448, no
+ *     infinities, S.1111.111 = NaN) with one fp32 scale per tensor:
+ *     value = decode(code) * scale.
+ *   - Ownership: the caller allocates and owns every buffer.  All pointers
+ *     are device pointers except where stated; each must be 16-byte aligned.
+ *     The library never allocates, frees or synchronises device memory and
+ *     never changes the current device.  Work is enqueued asynchronously on
+ *     `stream` (NULL = the default stream).
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued, so a call that returns an error has no effect.  A failed
+ *     kernel launch returns PA_ERR_HIP.  pa_last_error_message() gives a
+ *     thread-local description of the last error.
+ *   - Device-side contract (not checked on the host, since checking would
+ *     need the device data): block ids in block tables and copy pairs lie in
+ *     [0, num_blocks); slots are unique within one call; copy pairs have
+ *     distinct destinations and no destination is also a source in the same
+ *     call; 0 <= context_lens[s] <= max_context_len.  The kernels never read
+ *     or write outside the buffers when these are violated (out-of-range ids
+ *     and slots are skipped, lengths are clamped), but results are then
+ *     unspecified.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* pa_stream_t; /* a hipStream_t */
+
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_FP8_E4M3 = 3
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
+  PA_ERR_UNSUPPORTED = -2, /* valid but not built: dtype combination, head_dim, block size */
+  PA_ERR_WORKSPACE = -3,   /* workspace smaller than pa_decode_workspace_size() */
+  PA_ERR_HIP = -4          /* the HIP runtime refused a launch */
+} pa_status;
+
+/*
+ * Append rows: for every token n in [0, T) with slot = slot_mapping[n] >= 0,
+ *   k_cache[slot / block_size, h, slot % block_size, :] = enc(key[n, h, :])
+ *   v_cache[...same...]                                  = enc(value[n, h, :])
+ * for every kv head h.  enc is a bit copy when cache_dtype == src_dtype; for
+ * an FP8 cache it is the E4M3FN code of fp32(x) / k_scale (v_scale for V)
+ * with IEEE fp32 division, round-to-nearest-even, magnitudes beyond 448
+ * saturating to 448 and NaN kept as NaN.
+ *   key, value     [T, num_kv_heads, head_dim], src_dtype (PA_F16 | PA_BF16)
+ *   k_cache, v_cache [num_blocks, num_kv_heads, block_size, head_dim], cache_dtype
+ *                  (== src_dtype, or PA_FP8_E4M3)
+ *   slot_mapping   [T] int64; a negative slot skips the token (padding)
+ *   head_dim in {64, 128}; block_size in {8, 16, 32}; T >= 0 (T == 0 is a no-op).
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int32_t T, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               pa_dtype src_dtype, pa_dtype cache_dtype, float k_scale,
+                               float v_scale, pa_stream_t stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes (split-K
+ * partial results and the work list).  Depends only on its arguments.
+ */
+size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_group,
+                                int32_t head_dim, int32_t block_size, int32_t max_context_len);
+
+/*
+ * Paged decode attention.  For each sequence s < B and query head
+ * i < num_kv_heads * gqa_group, with h = i / gqa_group and L = context_lens[s]:
+ *   score[t] = scale * dot(q[s, i, :], K[t, h, :])                 for t < L
+ *   out[s, i, :] = sum_t softmax(score)[t] * V[t, h, :]
+ * where K[t, h, :] = k_scale * k_cache[block_tables[s][t / bs], h, t % bs, :]
+ * (k_scale/v_scale apply to FP8 caches only; they are ignored otherwise).
+ * L == 0 gives an all-zero row.  The result does not depend on where the
+ * blocks sit in the pool: reduction order depends only on logical positions.
+ *   out            [B, num_kv_heads*gqa_group, head_dim], out_dtype (F32 | F16 | BF16);
+ *                  16-bit outputs are the fp32 result rounded to nearest even
+ *   q              [B, num_kv_heads*gqa_group, head_dim], q_dtype (F16 | BF16)
+ *   k_cache, v_cache [num_blocks, num_kv_heads, block_size, head_dim], cache_dtype
+ *                  (== q_dtype, or PA_FP8_E4M3 with either q dtype)
+ *   block_tables   [B, max_blocks_per_seq] int32; entries past a sequence's
+ *                  last block are never read
+ *   context_lens   [B] int32
+ *   max_context_len host-side upper bound of context_lens (<= 0 means
+ *                  max_blocks_per_seq * block_size); sizes the split-K plan
+ *   workspace      device buffer of at least pa_decode_workspace_size(B,
+ *                  num_kv_heads, gqa_group, head_dim, block_size,
+ *                  max_context_len) bytes; its contents need no
+ *                  initialisation and are scratch after the call.
+ * Environment: PA_DECODE_VARIANT=valu|mfma forces one of the two kernel
+ * families (default: VALU/DPP for gqa_group <= 2, MFMA otherwise).
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, float k_scale, float v_scale, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
+                    size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * Copy-on-write: for each n < N with (src, dst) = block_mapping[n],
+ *   k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src]
+ * byte for byte (whole [num_kv_heads, block_size, head_dim] chunks).
+ *   block_mapping  [N, 2] int64, device; pairs with an id outside
+ *                  [0, num_blocks) or src == dst are skipped.
+ * N == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int32_t N,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, pa_dtype cache_dtype, pa_stream_t stream);
+
+/* Static description of a status code. */
+const char* pa_status_string(pa_status s);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char* pa_last_error_message(void);
+
+/* Library version string. */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,157 @@
+"""Paged decode attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libpa.so (see include/pa.h): it marshals torch
+tensors into device pointers and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  The library must be built
+first (``python -m paged_kv_cache_342_amd.build``); nothing here falls back to
+another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .blocks import slot_mapping  # noqa: F401
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+
+_TORCH_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
+
+_lib = None
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libpa.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_342_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    p, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.pa_reshape_and_cache.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i64, i32, i32, f32, f32, p]
+    lib.pa_reshape_and_cache.restype = ctypes.c_int
+    lib.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_workspace_size.restype = sz
+    lib.pa_decode.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32, f32, f32,
+                              i32, i32, i32, p, sz, p]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, p]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_last_error_message.argtypes = []
+    lib.pa_last_error_message.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != OK:
+        lib = library()
+        msg = lib.pa_last_error_message().decode() or lib.pa_status_string(status).decode()
+        raise PagedAttentionError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      slot_mapping: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Write key/value rows [T, Hkv, D] into the slots slot_mapping[T] (int64, negative = skip)
+    of the caches [num_blocks, Hkv, block_size, D] (same dtype as the rows, or float8_e4m3fn)."""
+    for t, n in ((key, "key"), (value, "value"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(t, n)
+    _require(slot_mapping, "slot_mapping", torch.int64)
+    T, Hkv, D = key.shape
+    nb, Hkv2, bs, D2 = k_cache.shape
+    if value.shape != key.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D) or slot_mapping.shape != (T,):
+        raise ValueError("shape mismatch between key/value, caches and slot_mapping")
+    _check(library().pa_reshape_and_cache(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, Hkv, D, bs, nb,
+        _TORCH_CODE.get(key.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), k_scale, v_scale, _stream(k_cache)))
+
+
+def decode_workspace_size(B: int, num_kv_heads: int, group: int, head_dim: int, block_size: int,
+                          max_context_len: int) -> int:
+    return int(library().pa_decode_workspace_size(B, num_kv_heads, group, head_dim, block_size, max_context_len))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+           context_lens: torch.Tensor, scale: float, max_context_len: Optional[int] = None,
+           k_scale: float = 1.0, v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+           out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Paged decode attention: q [B, Hq, D] over the caches through block_tables [B, M] (int32)
+    and context_lens [B] (int32).  Returns out [B, Hq, D] (out_dtype, default q's dtype)."""
+    _require(q, "q")
+    _require(k_cache, "k_cache")
+    _require(v_cache, "v_cache")
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or Hq % Hkv:
+        raise ValueError("q, k_cache and v_cache shapes do not agree")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, M] and context_lens [B]")
+    M = block_tables.shape[1]
+    mcl = M * bs if max_context_len is None else int(max_context_len)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _require(out, "out")
+    need = decode_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl) if B else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_decode(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
+        _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
+        _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """Copy-on-write: k_cache[dst] = k_cache[src] (and V) for each (src, dst) row of block_mapping [N, 2] int64."""
+    _require(k_cache, "k_cache")
+    _require(v_cache, "v_cache")
+    _require(block_mapping, "block_mapping", torch.int64)
+    nb, Hkv, bs, D = k_cache.shape
+    N = block_mapping.shape[0] if block_mapping.numel() else 0
+    _check(library().pa_copy_blocks(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping) if N else None, N, Hkv, D, bs, nb,
+        _TORCH_CODE.get(k_cache.dtype, -9), _stream(k_cache)))
+
+
+def version() -> str:
+    return library().pa_version().decode()

@@ -1,0 +1,129 @@
+// Slot scatter (appending new tokens' K/V rows) and copy-on-write block copy.
+#include <type_traits>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+// E4M3FN code of fp32(x) / scale: IEEE division, round to nearest even in
+// the hardware convert, magnitudes beyond 448 saturate, NaN stays NaN.
+__device__ __forceinline__ float fp8_prescale(float x, float scale) {
+  const float y = x / scale;
+  return y != y ? y : fminf(fmaxf(y, -448.0f), 448.0f);
+}
+
+__device__ __forceinline__ i32x2 encode8_fp8(const float* x, float scale) {
+  int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prescale(x[0], scale), fp8_prescale(x[1], scale), 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prescale(x[2], scale), fp8_prescale(x[3], scale), w0, true);
+  int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prescale(x[4], scale), fp8_prescale(x[5], scale), 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prescale(x[6], scale), fp8_prescale(x[7], scale), w1, true);
+  return i32x2{w0, w1};
+}
+
+// One thread per 8 elements of one (token, kv head) row.
+template <class ST, bool kFp8>
+__global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict__ key,
+                                                      const uint8_t* __restrict__ value,
+                                                      uint8_t* __restrict__ k_cache,
+                                                      uint8_t* __restrict__ v_cache,
+                                                      const int64_t* __restrict__ slots, int T,
+                                                      int Hkv, int D, int bs, int64_t num_blocks,
+                                                      float k_scale, float v_scale) {
+  const int per_row = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / per_row;  // token * Hkv + head
+  const int chunk = (int)(gid - row * per_row);
+  if (row >= (int64_t)T * Hkv) return;
+  const int64_t n = row / Hkv;
+  const int h = (int)(row - n * Hkv);
+  const int64_t slot = slots[n];
+  if (slot < 0 || slot >= num_blocks * bs) return;
+  const int64_t b = slot / bs;
+  const int o = (int)(slot - b * bs);
+  const int64_t src = (row * D + chunk * 8) * 2;
+  const int64_t dst_elem = ((b * Hkv + h) * bs + o) * D + chunk * 8;
+  const i32x4 kx = ld16(key + src);
+  const i32x4 vx = ld16(value + src);
+  if constexpr (!kFp8) {
+    *reinterpret_cast<i32x4*>(k_cache + dst_elem * 2) = kx;
+    *reinterpret_cast<i32x4*>(v_cache + dst_elem * 2) = vx;
+  } else {
+    float kf[8], vf[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      unpack2<ST>((uint32_t)kx[w], kf[2 * w], kf[2 * w + 1]);
+      unpack2<ST>((uint32_t)vx[w], vf[2 * w], vf[2 * w + 1]);
+    }
+    *reinterpret_cast<i32x2*>(k_cache + dst_elem) = encode8_fp8(kf, k_scale);
+    *reinterpret_cast<i32x2*>(v_cache + dst_elem) = encode8_fp8(vf, v_scale);
+  }
+}
+
+pa_status scatter_launch(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slots, int T, int Hkv, int D, int bs, int64_t num_blocks,
+                         int src_dtype, int cache_dtype, float k_scale, float v_scale,
+                         hipStream_t stream) {
+  if (T == 0) return PA_OK;
+  const int64_t threads = (int64_t)T * Hkv * (D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  auto K = reinterpret_cast<const uint8_t*>(key);
+  auto V = reinterpret_cast<const uint8_t*>(value);
+  auto KC = reinterpret_cast<uint8_t*>(k_cache);
+  auto VC = reinterpret_cast<uint8_t*>(v_cache);
+  if (cache_dtype != PA_FP8_E4M3) {
+    hipLaunchKernelGGL((scatter_kernel<F16, false>), grid, block, 0, stream, K, V, KC, VC, slots, T,
+                       Hkv, D, bs, num_blocks, k_scale, v_scale);
+  } else if (src_dtype == PA_F16) {
+    hipLaunchKernelGGL((scatter_kernel<F16, true>), grid, block, 0, stream, K, V, KC, VC, slots, T,
+                       Hkv, D, bs, num_blocks, k_scale, v_scale);
+  } else {
+    hipLaunchKernelGGL((scatter_kernel<BF16, true>), grid, block, 0, stream, K, V, KC, VC, slots, T,
+                       Hkv, D, bs, num_blocks, k_scale, v_scale);
+  }
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    set_error("pa_reshape_and_cache: launch failed: %s", hipGetErrorString(err));
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+// Copy whole blocks, 16 bytes per thread; grid.y = pair.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_cache,
+                                                          uint8_t* __restrict__ v_cache,
+                                                          const int64_t* __restrict__ pairs,
+                                                          int64_t units, int64_t num_blocks) {
+  const int64_t src = pairs[2 * (int64_t)blockIdx.y];
+  const int64_t dst = pairs[2 * (int64_t)blockIdx.y + 1];
+  if (src < 0 || dst < 0 || src >= num_blocks || dst >= num_blocks || src == dst) return;
+  const int64_t so = src * units, d0 = dst * units;
+  i32x4* kc = reinterpret_cast<i32x4*>(k_cache);
+  i32x4* vc = reinterpret_cast<i32x4*>(v_cache);
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += (int64_t)gridDim.x * blockDim.x) {
+    kc[d0 + u] = kc[so + u];
+    vc[d0 + u] = vc[so + u];
+  }
+}
+
+pa_status copy_blocks_launch(void* k_cache, void* v_cache, const int64_t* pairs, int N,
+                             int64_t block_bytes, int64_t num_blocks, hipStream_t stream) {
+  if (N == 0) return PA_OK;
+  const int64_t units = block_bytes / 16;
+  int64_t gx = (units + 255) / 256;
+  if (gx > 16) gx = 16;
+  for (int first = 0; first < N; first += 65535) {  // grid.y limit
+    const int n = N - first < 65535 ? N - first : 65535;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n), dim3(256), 0, stream,
+                       reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
+                       pairs + 2 * (int64_t)first, units, num_blocks);
+  }
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    set_error("pa_copy_blocks: launch failed: %s", hipGetErrorString(err));
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+}  // namespace pa

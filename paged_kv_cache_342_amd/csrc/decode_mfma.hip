@@ -1,0 +1,317 @@
+// Paged decode attention on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}).
+//
+// One wavefront handles one (sequence, partition, KV head, tile of up to 16
+// query heads) item and walks the partition 32 positions at a time.  Per
+// 32-position chunk:
+//   QK:  S^T[tok, head] = K[tok, :] . Q[head, :]  as two 16x16 output tiles,
+//        K rows are the A operand (one position per lane row), the group's
+//        query heads are the B operand (padded to 16 columns).
+//   PV:  O^T[d, head] += V^T[d, tok] . P^T[tok, head] with the probabilities
+//        as the B operand straight from the QK accumulator registers.
+// Both products sum over an index (head_dim for QK, position for PV) whose
+// order inside one MFMA is free as long as A and B agree, which lets every
+// lane fetch contiguous 16-byte pieces: K rows give 64 contiguous bytes per
+// row per load instruction, and V is fetched as whole rows (16 lanes x 16 B)
+// and transposed inside each lane's registers (8 positions x head_dim/16
+// values) with byte permutes, so nothing is staged through LDS.
+//
+// Softmax runs online in fp32 in the log2 domain.  The running maximum of a
+// head only moves when some score exceeds it by more than kRescaleThreshold
+// (a wave-uniform branch); otherwise probabilities are 2^(s - m) <= 2^8,
+// so the accumulator is rescaled rarely.  The result is exact regardless,
+// since numerator and denominator share the same reference.
+//
+// P for the PV product: fp16 when V is fp16 or fp8 (fp8 -> fp16 is exact),
+// and a two-term bf16 split (hi + lo) when V is bf16, so the probabilities
+// keep ~16 bits.  Scores use q * k products of the 16-bit inputs, exact in
+// the fp32 accumulator; scale * log2(e) is applied in fp32 afterwards.
+#include <type_traits>
+
+#include "decode_common.h"
+
+namespace pa {
+
+template <class T>
+__device__ __forceinline__ f32x4 mfma32(i32x4 a, i32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma32<F16>(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma32<BF16>(i32x4 a, i32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Registers of one 32-position chunk, as loaded from memory.
+template <class CT, int D>
+struct ChunkRaw {
+  static constexpr int KR = D * CT::bytes / 64;  // 16-byte K loads per lane per 16-row tile
+  static constexpr int VD = D * CT::bytes / 64;  // dwords of V per lane per position
+  i32x4 k[2][KR];
+  uint32_t v[8][VD];
+};
+
+template <int N>
+__device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t* o) {
+  if constexpr (N == 4) {
+    i32x4 x = ld16(p);
+    o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
+  } else if constexpr (N == 2) {
+    i32x2 x = ld8(p);
+    o[0] = x[0]; o[1] = x[1];
+  } else {
+    o[0] = ld4(p);
+  }
+}
+
+template <class CT, class QT, int D, int BS>
+__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int e = CT::bytes;
+  constexpr int KK = D / 32;   // MFMAs per QK tile
+  constexpr int W = D / 16;    // V values per lane per position (one output d-run)
+  constexpr bool kFp8 = std::is_same<CT, FP8>::value;
+  constexpr bool kBf16V = std::is_same<CT, BF16>::value;
+  using PT = typename std::conditional<kBf16V, BF16, F16>::type;  // PV operand type
+  using Raw = ChunkRaw<CT, D>;
+  constexpr int VD = Raw::VD;
+  constexpr int64_t kChunkBytes = (int64_t)BS * D * e;  // one (block, head) chunk
+
+  const int lane = threadIdx.x;
+  const int r = lane & 15;   // A-operand row / B-operand column / C column
+  const int gq = lane >> 4;  // k-slot group
+  const int Hq = a.Hkv * a.G;
+  const int64_t blk_stride = (int64_t)a.Hkv * kChunkBytes;
+  const int total = item_count(a) * a.Hkv * a.head_tiles;
+
+  for (int flat = blockIdx.x; flat < total; flat += gridDim.x) {
+    const Item t = item_at(a, flat);
+    const int col_head = 16 * t.ht + r;  // head within the group this lane's column carries
+    const bool col_ok = col_head < a.G;
+    const int head = t.h * a.G + col_head;
+
+    if (t.L == 0) {  // empty context: zeros
+      if (col_ok) {
+        float z[4 * W];
+#pragma unroll
+        for (int i = 0; i < 4 * W; ++i) z[i] = 0.f;
+        store_out(a, t.s, head, D, 4 * W * gq, z, 4 * W);
+      }
+      continue;
+    }
+
+    // ---- Q as the B operand of QK, in the k-slot order the K loads use
+    i32x4 qop[KK];
+    {
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)t.s * Hq + head) * D * 2;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int d = kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
+        qop[kk] = col_ok ? ld16(qrow + d * 2) : i32x4{0, 0, 0, 0};
+      }
+    }
+
+    const int ids = load_block_ids(a, t, BS);
+    const uint8_t* kbase = a.k_cache + (int64_t)t.h * kChunkBytes;
+    const uint8_t* vbase = a.v_cache + (int64_t)t.h * kChunkBytes;
+    const int nchunks = (t.tok_end - t.tok0 + 31) / 32;
+
+    auto load_chunk = [&](int c, Raw& raw) {
+      const int ctok = t.tok0 + 32 * c;  // first position of the chunk
+      const int cb = 32 * c / BS;        // its first block, relative to the partition
+      int id[4];
+      if constexpr (BS == 32) {
+        id[0] = __builtin_amdgcn_readlane(ids, cb);
+      } else if constexpr (BS == 16) {
+        id[0] = __builtin_amdgcn_readlane(ids, cb);
+        id[1] = __builtin_amdgcn_readlane(ids, cb + 1);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) id[i] = __builtin_amdgcn_readlane(ids, cb + i);
+      }
+      // K: rows 16*tt + r
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int tc = 16 * tt + r;
+        const int bsel = BS == 32 ? 0 : (BS == 16 ? tt : 2 * tt + (r >> 3));
+        const bool ok = ctok + tc < t.tok_end;
+        const uint8_t* row = kbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e;
+#pragma unroll
+        for (int u = 0; u < Raw::KR; ++u) {
+          const int off = kFp8 ? 64 * u + 16 * gq : (32 * u + 8 * gq) * 2;
+          raw.k[tt][u] = ok ? ld16(row + off) : i32x4{0, 0, 0, 0};
+        }
+      }
+      // V: whole rows, position slot j -> 16*(j>>2) + 4*gq + (j&3)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
+        const int bsel = BS == 32 ? 0 : (BS == 16 ? (j >> 2) : 2 * (j >> 2) + (gq >> 1));
+        const bool ok = ctok + tc < t.tok_end;
+        const uint8_t* row = vbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e + W * r * e;
+        if (ok) {
+          load_dwords<VD>(row, raw.v[j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < VD; ++i) raw.v[j][i] = 0;
+        }
+      }
+    };
+
+    float m = -INFINITY, l = 0.f;
+    f32x4 acc[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute_chunk = [&](int c, const Raw& raw) {
+      const int ctok = t.tok0 + 32 * c;
+      // ---- QK
+      i32x4 kop[2][KK];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        if constexpr (kFp8) {
+#pragma unroll
+          for (int u = 0; u < Raw::KR; ++u) {
+            const i32x2 lo = fp8x4_to_16<QT>((uint32_t)raw.k[tt][u][0]);
+            const i32x2 lo2 = fp8x4_to_16<QT>((uint32_t)raw.k[tt][u][1]);
+            const i32x2 hi = fp8x4_to_16<QT>((uint32_t)raw.k[tt][u][2]);
+            const i32x2 hi2 = fp8x4_to_16<QT>((uint32_t)raw.k[tt][u][3]);
+            kop[tt][2 * u] = i32x4{lo[0], lo[1], lo2[0], lo2[1]};
+            kop[tt][2 * u + 1] = i32x4{hi[0], hi[1], hi2[0], hi2[1]};
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < KK; ++u) kop[tt][u] = raw.k[tt][u];
+        }
+      }
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s0 = mfma32<QT>(kop[0][kk], qop[kk], s0);
+        s1 = mfma32<QT>(kop[1][kk], qop[kk], s1);
+      }
+      // ---- online softmax for this lane's column (head), positions j
+      float sc[8];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float raw_s = (j < 4 ? s0[j & 3] : s1[j & 3]) * a.qk_scale_log2;
+        const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
+        sc[j] = ctok + tc < t.tok_end ? raw_s : -INFINITY;
+        mx = fmaxf(mx, sc[j]);
+      }
+      if (wave_any(mx > m + kRescaleThreshold)) {
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2(m - mn);
+#pragma unroll
+        for (int i = 0; i < W; ++i) acc[i] *= alpha;
+        l *= alpha;
+        m = mn;
+      }
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = fast_exp2(sc[j] - m);
+        l += p[j];
+      }
+      // ---- P as the B operand of PV
+      i32x4 pop, plo;
+#pragma unroll
+      for (int jp = 0; jp < 4; ++jp) {
+        if constexpr (kBf16V) {
+          const uint16_t h0 = f32_to_bf16_rne(p[2 * jp]), h1 = f32_to_bf16_rne(p[2 * jp + 1]);
+          const uint16_t l0 = f32_to_bf16_rne(p[2 * jp] - bf16_bits_to_f32(h0));
+          const uint16_t l1 = f32_to_bf16_rne(p[2 * jp + 1] - bf16_bits_to_f32(h1));
+          pop[jp] = (int)(h0 | ((uint32_t)h1 << 16));
+          plo[jp] = (int)(l0 | ((uint32_t)l1 << 16));
+        } else {
+          pop[jp] = (int)(f32_to_f16_rne(p[2 * jp]) | ((uint32_t)f32_to_f16_rne(p[2 * jp + 1]) << 16));
+        }
+      }
+      // ---- V^T as the A operand: 16-bit values per position, then transpose
+      uint32_t vt[8][W / 2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (kFp8) {
+#pragma unroll
+          for (int i = 0; i < VD; ++i) {
+            const i32x2 x = fp8x4_to_16<F16>(raw.v[j][i]);
+            vt[j][2 * i] = (uint32_t)x[0];
+            vt[j][2 * i + 1] = (uint32_t)x[1];
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < W / 2; ++i) vt[j][i] = raw.v[j][i];
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < W; ++dt) {
+        i32x4 vop;
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+          const uint32_t a0 = vt[2 * jp][dt >> 1], a1 = vt[2 * jp + 1][dt >> 1];
+          vop[jp] = (dt & 1) ? (int)((a0 >> 16) | (a1 & 0xFFFF0000u)) : (int)((a0 & 0xFFFFu) | (a1 << 16));
+        }
+        acc[dt] = mfma32<PT>(vop, pop, acc[dt]);
+        if constexpr (kBf16V) acc[dt] = mfma32<PT>(vop, plo, acc[dt]);
+      }
+    };
+
+    // double-buffered walk over the partition's chunks
+    Raw buf0, buf1;
+    load_chunk(0, buf0);
+    for (int c = 0; c < nchunks; c += 2) {
+      if (c + 1 < nchunks) load_chunk(c + 1, buf1);
+      compute_chunk(c, buf0);
+      if (c + 1 >= nchunks) break;
+      if (c + 2 < nchunks) load_chunk(c + 2, buf0);
+      compute_chunk(c + 1, buf1);
+    }
+
+    // ---- epilogue: the lane holds head col_head, d = 4W*gq + W*jj + dt
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (col_ok) {
+      float v[4 * W];
+      const bool final = t.nparts == 1;
+      const float f = final ? a.v_scale / l : 1.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int dt = 0; dt < W; ++dt) v[W * jj + dt] = acc[dt][jj] * f;
+      if (final) {
+        store_out(a, t.s, head, D, 4 * W * gq, v, 4 * W);
+      } else {
+        store_partial(a, t.s, head, t.p, D, 4 * W * gq, v, 4 * W);
+        if (gq == 0) store_ml(a, t.s, head, t.p, m, l);
+      }
+    }
+  }
+}
+
+#define PA_MFMA_CASE(CT, QT, D, BS)                                                    \
+  if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS) {                 \
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS>), grid, dim3(64), 0, stream, a); \
+    return true;                                                                       \
+  }
+
+#define PA_MFMA_BS(CT, QT, D) \
+  PA_MFMA_CASE(CT, QT, D, 8)  \
+  PA_MFMA_CASE(CT, QT, D, 16) \
+  PA_MFMA_CASE(CT, QT, D, 32)
+
+bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, dim3 grid,
+                        hipStream_t stream) {
+  PA_MFMA_BS(F16, F16, 64)
+  PA_MFMA_BS(F16, F16, 128)
+  PA_MFMA_BS(BF16, BF16, 64)
+  PA_MFMA_BS(BF16, BF16, 128)
+  PA_MFMA_BS(FP8, F16, 64)
+  PA_MFMA_BS(FP8, F16, 128)
+  PA_MFMA_BS(FP8, BF16, 64)
+  PA_MFMA_BS(FP8, BF16, 128)
+  return false;
+}
+
+}  // namespace pa

@@ -1,0 +1,180 @@
+// C entry points of libpa.so: argument validation and dispatch.  Every
+// check runs before anything is enqueued, so a call that fails has no effect.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+static thread_local char g_error[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+}
+
+static pa_status fail(pa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+static bool known_dtype(int d) { return d >= PA_F32 && d <= PA_FP8_E4M3; }
+static int elem_bytes(int d) { return d == PA_FP8_E4M3 ? 1 : (d == PA_F32 ? 4 : 2); }
+
+#define PA_CHECK_SHAPE(fn, Hkv, D, bs, num_blocks)                                                  \
+  do {                                                                                              \
+    if ((Hkv) < 1) return fail(PA_ERR_INVALID_ARG, fn ": num_kv_heads must be >= 1 (got %d)", (Hkv)); \
+    if ((num_blocks) < 1) return fail(PA_ERR_INVALID_ARG, fn ": num_blocks must be >= 1");          \
+    if ((D) != 64 && (D) != 128) return fail(PA_ERR_UNSUPPORTED, fn ": head_dim must be 64 or 128 (got %d)", (D)); \
+    if ((bs) != 8 && (bs) != 16 && (bs) != 32)                                                      \
+      return fail(PA_ERR_UNSUPPORTED, fn ": block_size must be 8, 16 or 32 (got %d)", (bs));        \
+  } while (0)
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_version(void) { return "pa-mi355x 0.1 (gfx950)"; }
+
+const char* pa_last_error_message(void) { return g_error; }
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PA_ERR_WORKSPACE: return "workspace too small";
+    case PA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int32_t T, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               pa_dtype src_dtype, pa_dtype cache_dtype, float k_scale,
+                               float v_scale, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_reshape_and_cache";
+  if (T < 0) return fail(PA_ERR_INVALID_ARG, "%s: T must be >= 0", fn);
+  PA_CHECK_SHAPE("pa_reshape_and_cache", num_kv_heads, head_dim, block_size, num_blocks);
+  if (!known_dtype(src_dtype) || !known_dtype(cache_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (src_dtype != PA_F16 && src_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: source rows must be f16 or bf16", fn);
+  if (cache_dtype != src_dtype && cache_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "%s: cache dtype must equal the source dtype or be fp8-e4m3", fn);
+  if (cache_dtype == PA_FP8_E4M3 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "%s: fp8 scales must be finite and > 0", fn);
+  if (!k_cache || !v_cache) return fail(PA_ERR_INVALID_ARG, "%s: null cache pointer", fn);
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return fail(PA_ERR_INVALID_ARG, "%s: cache pointers must be 16-byte aligned", fn);
+  if (T == 0) return PA_OK;
+  if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "%s: null key/value/slot_mapping", fn);
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "%s: misaligned key/value/slot_mapping", fn);
+  return scatter_launch(key, value, k_cache, v_cache, slot_mapping, T, num_kv_heads, head_dim, block_size,
+                        num_blocks, src_dtype, cache_dtype, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                                int32_t block_size, int32_t max_context_len) {
+  if (B <= 0 || num_kv_heads <= 0 || gqa_group <= 0 || max_context_len <= 0) return 0;
+  if ((head_dim != 64 && head_dim != 128) || (block_size != 8 && block_size != 16 && block_size != 32)) return 0;
+  return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len).bytes;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, float k_scale, float v_scale, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
+                    size_t workspace_bytes, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_decode";
+  if (B < 0) return fail(PA_ERR_INVALID_ARG, "%s: B must be >= 0", fn);
+  if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: at most 65535 sequences per call", fn);
+  PA_CHECK_SHAPE("pa_decode", num_kv_heads, head_dim, block_size, num_blocks);
+  if (gqa_group < 1) return fail(PA_ERR_INVALID_ARG, "%s: gqa_group must be >= 1", fn);
+  if ((int64_t)num_kv_heads * gqa_group > 65536) return fail(PA_ERR_UNSUPPORTED, "%s: too many query heads", fn);
+  if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be >= 1", fn);
+  if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return fail(PA_ERR_UNSUPPORTED, "%s: block table too long", fn);
+  if (!known_dtype(q_dtype) || !known_dtype(cache_dtype) || !known_dtype(out_dtype))
+    return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (q_dtype != PA_F16 && q_dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: q must be f16 or bf16", fn);
+  if (cache_dtype != q_dtype && cache_dtype != PA_FP8_E4M3)
+    return fail(PA_ERR_UNSUPPORTED, "%s: cache dtype must equal the q dtype or be fp8-e4m3", fn);
+  if (out_dtype == PA_FP8_E4M3) return fail(PA_ERR_UNSUPPORTED, "%s: out must be f32, f16 or bf16", fn);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (cache_dtype == PA_FP8_E4M3 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PA_ERR_INVALID_ARG, "%s: fp8 scales must be finite and > 0", fn);
+  if (B == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer argument", fn);
+  const int full = max_blocks_per_seq * block_size;
+  const int plan_ctx = max_context_len > 0 ? max_context_len : full;
+  const DecodePlan plan = plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx);
+  if (plan.bytes > 0) {
+    if (!workspace || workspace_bytes < plan.bytes)
+      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  }
+  DecodeRequest r{};
+  r.out = out;
+  r.q = q;
+  r.k_cache = k_cache;
+  r.v_cache = v_cache;
+  r.block_tables = block_tables;
+  r.context_lens = context_lens;
+  r.B = B;
+  r.Hkv = num_kv_heads;
+  r.G = gqa_group;
+  r.D = head_dim;
+  r.bs = block_size;
+  r.M = max_blocks_per_seq;
+  r.plan_ctx = plan_ctx;
+  r.max_ctx = plan_ctx < full ? plan_ctx : full;
+  r.num_blocks = num_blocks;
+  r.scale = scale;
+  r.k_scale = k_scale;
+  r.v_scale = v_scale;
+  r.q_dtype = q_dtype;
+  r.cache_dtype = cache_dtype;
+  r.out_dtype = out_dtype;
+  r.workspace = workspace;
+  r.workspace_bytes = workspace_bytes;
+  return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int32_t N,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, pa_dtype cache_dtype, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_copy_blocks";
+  if (N < 0) return fail(PA_ERR_INVALID_ARG, "%s: N must be >= 0", fn);
+  PA_CHECK_SHAPE("pa_copy_blocks", num_kv_heads, head_dim, block_size, num_blocks);
+  if (!known_dtype(cache_dtype) || cache_dtype == PA_F32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: cache dtype must be f16, bf16 or fp8-e4m3", fn);
+  if (!k_cache || !v_cache) return fail(PA_ERR_INVALID_ARG, "%s: null cache pointer", fn);
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return fail(PA_ERR_INVALID_ARG, "%s: cache pointers must be 16-byte aligned", fn);
+  if (N == 0) return PA_OK;
+  if (!block_mapping || !aligned(block_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned block_mapping", fn);
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(cache_dtype);
+  return copy_blocks_launch(k_cache, v_cache, block_mapping, N, block_bytes, num_blocks,
+                            reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

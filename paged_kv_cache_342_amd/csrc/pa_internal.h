@@ -1,0 +1,55 @@
+// Host-side interfaces between the C entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// thread-local error text behind pa_last_error_message()
+void set_error(const char* fmt, ...);
+
+struct DecodePlan {
+  int part_tokens;    // positions per split-K partition
+  int nparts;         // partitions per sequence the workspace holds
+  size_t work_off, ml_off, acc_off, bytes;  // workspace layout
+};
+
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx);
+
+struct DecodeRequest {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int B, Hkv, G, D, bs, M;
+  int max_ctx;   // lengths are clamped to this: min(plan_ctx, M * bs)
+  int plan_ctx;  // the caller's max_context_len (M * bs when not given); sizes the plan
+  int64_t num_blocks;
+  float scale, k_scale, v_scale;
+  int q_dtype, cache_dtype, out_dtype;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+// 0 = default choice, 1 = VALU/DPP kernel, 2 = MFMA kernel
+int decode_variant_override();
+bool decode_uses_valu(int variant, int G);
+bool decode_valu_supported(int ct, int qt, int D, int bs, int G);
+
+pa_status decode_launch(const DecodeRequest& r, hipStream_t stream);
+
+pa_status scatter_launch(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slots, int T, int Hkv, int D, int bs, int64_t num_blocks,
+                         int src_dtype, int cache_dtype, float k_scale, float v_scale,
+                         hipStream_t stream);
+
+pa_status copy_blocks_launch(void* k_cache, void* v_cache, const int64_t* pairs, int N,
+                             int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,339 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle, element by element.
+
+Scatter and copy-on-write must be bit-exact; decode (fp32 output) must be
+within max-abs 2e-3 and relative L2 1e-3 of the oracle for fp16/bf16 caches
+and within max-abs 3e-2 for fp8 caches.  Every pool is poisoned with NaN
+before it is filled, so a read of an unwritten slot fails the comparison.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_342_amd as pa
+import workloads as W
+from oracle import harness as OH
+from oracle import pa_oracle as O
+from tests.gpu_util import GpuBatch, errors, log, set_variant, storage_to_torch, tolerance, torch_to_bytes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _default_variant():
+    set_variant(None)
+    yield
+    set_variant(None)
+
+
+def _check_decode(w, batch=None, seqs=None, variant=None, label=""):
+    set_variant(variant)
+    batch = batch or GpuBatch(w)
+    out = batch.decode().cpu().numpy().astype(np.float64)
+    kc, vc = OH.build_pools(w, seqs=seqs)
+    ref = OH.decode(w, kc, vc, seqs=seqs)
+    got = out if seqs is None else out[list(seqs)]
+    ma, rel = errors(got, ref)
+    tol_abs, tol_rel = tolerance(w.cache_dtype)
+    log(f"[decode {w.name}{label} variant={variant}] max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert np.isfinite(got).all()
+    assert ma <= tol_abs
+    if tol_rel is not None:
+        assert rel <= tol_rel
+    return batch, out
+
+
+# ------------------------------------------------------------------ scatter / copy
+
+@pytest.mark.parametrize("make", [
+    lambda: W.tiny(),
+    lambda: W.llama8b(B=4),
+    lambda: W.shared_prefix(prompts=2, samples=3, prefix=96, max_tail=40),
+    lambda: W.heavy_tail(bs=8, B=16),
+    lambda: W.custom("edge_d64_bs32", 5, [1, 31, 32, 33, 300], 8, 8, 64, 32, "fp8", "f16"),
+], ids=["tiny", "llama8b", "shared_prefix", "heavy_tail_fp8", "fp8_f16src"])
+def test_scatter_and_copy_are_bit_exact(make):
+    w = make()
+    log(f"[scatter {w.name}]")
+    g = GpuBatch(w)
+    kc, vc = OH.build_pools(w)
+    assert np.array_equal(torch_to_bytes(g.kc), kc.reshape(-1).view(np.uint8))
+    assert np.array_equal(torch_to_bytes(g.vc), vc.reshape(-1).view(np.uint8))
+
+
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 4.75 / 448.0, 2.0 ** -4])
+def test_fp8_encode_exhaustive(src, scale):
+    """All 65536 16-bit inputs through the scatter into an fp8 cache."""
+    log(f"[fp8 encode {src} scale={scale}]")
+    Hkv, D, bs = 2, 128, 16
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    rows = bits.reshape(-1, Hkv, D)  # 256 tokens
+    T = rows.shape[0]
+    key = storage_to_torch(rows.view(np.float16) if src == "f16" else rows, src).cuda()
+    value = storage_to_torch(rows[::-1].copy().view(np.float16) if src == "f16" else rows[::-1].copy(), src).cuda()
+    nb = T // bs
+    kc = torch.zeros((nb, Hkv, bs, D), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    vc = torch.zeros((nb, Hkv, bs, D), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    slots = torch.arange(T, dtype=torch.int64, device="cuda")
+    pa.reshape_and_cache(key, value, kc, vc, slots, scale, scale)
+    got_k = kc.view(torch.uint8).cpu().numpy().transpose(0, 2, 1, 3).reshape(-1)
+    got_v = vc.view(torch.uint8).cpu().numpy().transpose(0, 2, 1, 3).reshape(-1)
+    x = O.widen(bits, src).astype(np.float32)
+    ref_k = O.e4m3_encode(x, scale)
+    ref_v = O.e4m3_encode(O.widen(rows[::-1].reshape(-1), src).astype(np.float32), scale)
+    bad = np.nonzero(got_k != ref_k)[0]
+    if len(bad):
+        log(f"  first mismatches: {[(hex(int(bits[i])), hex(int(got_k[i])), hex(int(ref_k[i]))) for i in bad[:8]]}")
+    assert len(bad) == 0
+    assert np.array_equal(got_v, ref_v)
+
+
+def test_copy_blocks_pairs_and_skips():
+    w = W.custom("copy", 9, [40, 70], 4, 4, 64, 16, "bf16")
+    g = GpuBatch(w)
+    used = set(w.block_tables[w.block_tables >= 0].ravel().tolist())
+    free = sorted(set(range(w.num_blocks)) - used)
+    src = int(w.block_tables[1, 2])
+    before_src = torch_to_bytes(g.kc[src]).copy()
+    pairs = torch.tensor([[src, free[0]], [int(w.block_tables[0, 0]), free[1]], [src, src], [-1, free[0]],
+                          [src, w.num_blocks]], dtype=torch.int64, device="cuda")
+    before_all = torch_to_bytes(g.kc).copy()
+    pa.copy_blocks(g.kc, g.vc, pairs)
+    assert np.array_equal(torch_to_bytes(g.kc[free[0]]), before_src)
+    assert np.array_equal(torch_to_bytes(g.vc[free[0]]), torch_to_bytes(g.vc[src]))
+    assert np.array_equal(torch_to_bytes(g.kc[free[1]]), torch_to_bytes(g.kc[int(w.block_tables[0, 0])]))
+    assert np.array_equal(torch_to_bytes(g.kc[src]), before_src)
+    # nothing else changed
+    after = torch_to_bytes(g.kc).reshape(w.num_blocks, -1)
+    before = before_all.reshape(w.num_blocks, -1)
+    others = [b for b in range(w.num_blocks) if b not in (free[0], free[1])]
+    assert np.array_equal(after[others], before[others])
+
+
+# ------------------------------------------------------------------ decode parity on the workloads
+
+def test_decode_tiny():
+    for v in (None, "mfma"):
+        _check_decode(W.tiny(), variant=v)
+
+
+@pytest.mark.parametrize("variant", [None, "valu"])
+def test_decode_llama8b_reduced(variant):
+    _check_decode(W.llama8b(B=6), variant=variant, label="[B=6]")
+
+
+def test_decode_llama8b_full_size_sampled():
+    w = W.llama8b()
+    g = GpuBatch(w)
+    seqs = [int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens)), 17, 40]
+    _check_decode(w, batch=g, seqs=seqs, label="[full, sampled]")
+
+
+def test_decode_llama70b_reduced():
+    _check_decode(W.llama70b(B=2), label="[B=2]")
+
+
+def test_decode_llama70b_full_size_sampled():
+    w = W.llama70b()
+    _check_decode(w, seqs=[0, 13, 31], label="[full, sampled]")
+
+
+def test_decode_shared_prefix_reduced():
+    _check_decode(W.shared_prefix(prompts=2, samples=4, prefix=256, max_tail=100), label="[2x4]")
+
+
+def test_decode_shared_prefix_full_size_sampled():
+    w = W.shared_prefix()
+    _check_decode(w, seqs=[0, 7, 8, 127], label="[full, sampled]")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_decode_heavy_tail_reduced(bs):
+    _check_decode(W.heavy_tail(bs=bs, B=24), label=f"[B=24]")
+
+
+def test_decode_heavy_tail_full_size_sampled():
+    w = W.heavy_tail(bs=16)
+    order = np.argsort(w.context_lens)
+    seqs = sorted({int(order[-1]), int(order[-2]), int(order[0]), int(order[len(order) // 2])})
+    _check_decode(w, seqs=seqs, label="[full, sampled]")
+
+
+# ------------------------------------------------------------------ edge-case sweep
+
+SWEEP_LENS = [1, 2, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,
+              511, 512, 513, 1031]
+
+
+@pytest.mark.parametrize("cache,q", [("f16", "f16"), ("bf16", "bf16"), ("fp8", "bf16"), ("fp8", "f16")])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_decode_edge_sweep(cache, q, D, bs):
+    for g in (1, 2, 4, 8):
+        w = W.custom(f"sweep_{cache}_{q}_D{D}_bs{bs}_g{g}", 100 + g, SWEEP_LENS, 2 * g, 2, D, bs, cache, q)
+        batch = GpuBatch(w)
+        variants = ["valu", "mfma"] if g <= 2 else ["mfma"]
+        for v in variants:
+            _check_decode(w, batch=batch, variant=v)
+
+
+@pytest.mark.parametrize("G", [16, 24, 32])
+def test_decode_many_heads_per_kv_head(G):
+    w = W.custom(f"heads{G}", 7, [5, 300, 777], G, 1, 128, 16, "bf16")
+    _check_decode(w)
+
+
+def test_decode_forced_valu_group4():
+    _check_decode(W.llama8b(B=4), variant="valu", label="[valu g4]")
+
+
+def test_decode_empty_context_rows_are_zero():
+    lens = [0, 5, 0, 300]
+    w = W.custom("empty", 3, lens, 8, 2, 128, 16, "bf16")
+    for v in ("valu", "mfma"):
+        set_variant(v)
+        out = GpuBatch(w).decode().cpu()
+        assert torch.equal(out[0], torch.zeros_like(out[0])) and torch.equal(out[2], torch.zeros_like(out[2]))
+        assert torch.isfinite(out).all()
+    _check_decode(w)
+
+
+# ------------------------------------------------------------------ output dtypes
+
+@pytest.mark.parametrize("make", [lambda: W.tiny(), lambda: W.llama8b(B=4), lambda: W.heavy_tail(B=12)],
+                         ids=["f16", "bf16", "fp8"])
+def test_native_dtype_output_is_rne_of_fp32(make):
+    w = make()
+    g = GpuBatch(w)
+    f32 = g.decode(out_dtype=torch.float32).cpu()
+    for dt in (torch.float16, torch.bfloat16):
+        nat = g.decode(out_dtype=dt).cpu()
+        assert torch.equal(nat.view(torch.int16), f32.to(dt).view(torch.int16))
+
+
+# ------------------------------------------------------------------ invariants the pages state
+
+def _raw(t):
+    return t.view(torch.uint8) if t.element_size() == 1 else t.view(torch.int16)
+
+
+def _permuted(g, perm):
+    """The same logical contents in a pool whose block b moved to perm[b]."""
+    kc = torch.empty_like(_raw(g.kc))
+    vc = torch.empty_like(_raw(g.vc))
+    kc[perm] = _raw(g.kc)
+    vc[perm] = _raw(g.vc)
+    tables = torch.where(g.tables >= 0, perm[g.tables.clamp(min=0).long()].int(), g.tables)
+    return kc.view(g.kc.dtype), vc.view(g.vc.dtype), tables
+
+
+@pytest.mark.parametrize("make", [lambda: W.llama8b(B=8), lambda: W.heavy_tail(bs=8, B=32), lambda: W.tiny()],
+                         ids=["bf16", "fp8", "f16_valu"])
+def test_paged_layout_does_not_change_the_bits(make):
+    w = make()
+    g = GpuBatch(w)
+    base = g.decode()
+    again = g.decode()
+    assert torch.equal(base, again)  # deterministic
+    for seed in (1, 2):
+        perm = torch.from_numpy(np.random.default_rng(seed).permutation(w.num_blocks)).cuda()
+        kc, vc, tables = _permuted(g, perm)
+        out = pa.decode(g.q, kc, vc, tables, g.lens, w.scale, max_context_len=w.max_context_len,
+                        k_scale=w.k_scale, v_scale=w.v_scale, out_dtype=torch.float32)
+        assert torch.equal(out, base)
+    # identity layout: each sequence's blocks laid out contiguously in order
+    order = [int(b) for s in range(w.B) for b in w.block_tables[s, :(int(w.context_lens[s]) + w.bs - 1) // w.bs]]
+    rest = [b for b in range(w.num_blocks) if b not in set(order)]
+    perm_np = np.empty(w.num_blocks, np.int64)
+    perm_np[np.array(order + rest)] = np.arange(w.num_blocks)
+    kc, vc, tables = _permuted(g, torch.from_numpy(perm_np).cuda())
+    out = pa.decode(g.q, kc, vc, tables, g.lens, w.scale, max_context_len=w.max_context_len,
+                    k_scale=w.k_scale, v_scale=w.v_scale, out_dtype=torch.float32)
+    assert torch.equal(out, base)
+
+
+def test_shared_prefix_equals_private_copies_bitwise():
+    w = W.shared_prefix(prompts=2, samples=4, prefix=256, max_tail=60)
+    g = GpuBatch(w)
+    shared = g.decode()
+    # give every sequence private copies of all its blocks
+    nblk = (w.context_lens + w.bs - 1) // w.bs
+    total = int(nblk.sum())
+    kc = torch.empty((total,) + tuple(g.kc.shape[1:]), dtype=_raw(g.kc).dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    tables = np.full_like(w.block_tables, -1)
+    off = 0
+    for s in range(w.B):
+        n = int(nblk[s])
+        src = torch.from_numpy(w.block_tables[s, :n].astype(np.int64)).cuda()
+        kc[off:off + n] = _raw(g.kc)[src]
+        vc[off:off + n] = _raw(g.vc)[src]
+        tables[s, :n] = np.arange(off, off + n)
+        off += n
+    kc, vc = kc.view(g.kc.dtype), vc.view(g.vc.dtype)
+    private = pa.decode(g.q, kc, vc, torch.from_numpy(tables).cuda(), g.lens, w.scale,
+                        max_context_len=w.max_context_len, out_dtype=torch.float32)
+    assert torch.equal(shared, private)
+
+
+@pytest.mark.parametrize("cache,D,bs", [("f16", 64, 16), ("bf16", 128, 8), ("fp8", 128, 32)])
+def test_gather_probe_is_exact(cache, D, bs):
+    """One position scores far above all others, so softmax is exactly one-hot
+    in fp32 and the output must equal that position's value row bit for bit."""
+    Hkv, G = 2, 2
+    q_dt = "f16" if cache == "f16" else "bf16"
+    targets = list(range(37)) + list(range(0, 700, 53)) + [699]
+    lens = [37] * 37 + [700] * (len(targets) - 37)
+    B = len(lens)
+    nblk = [(L + bs - 1) // bs for L in lens]
+    num_blocks = sum(nblk) + 3
+    perm = np.random.default_rng(4).permutation(num_blocks)
+    tables = np.full((B, max(nblk)), -1, np.int32)
+    off = 0
+    for s in range(B):
+        tables[s, :nblk[s]] = perm[off:off + nblk[s]]
+        off += nblk[s]
+    rng = np.random.default_rng(8)
+    c = 32.0
+    ks, vs, slots = [], [], []
+    for s, (L, tstar) in enumerate(zip(lens, targets)):
+        k = np.zeros((L, Hkv, D), np.float32)
+        k[:, :, 0] = -c
+        k[tstar, :, 0] = c
+        ks.append(k)
+        vs.append(rng.standard_normal((L, Hkv, D)).astype(np.float32))
+        slots.append(pa.slot_mapping(tables, [s], [0], [L], bs))
+    src = "bf16" if cache == "fp8" else cache
+    key = storage_to_torch(W.to_storage(np.concatenate(ks), src), src).cuda()
+    val_st = W.to_storage(np.concatenate(vs), src)
+    value = storage_to_torch(val_st, src).cuda()
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}[cache]
+    raw_dt = torch.uint8 if cache == "fp8" else torch.int16
+    kc = torch.zeros((num_blocks, Hkv, bs, D), dtype=raw_dt, device="cuda").view(dt)
+    vc = torch.zeros((num_blocks, Hkv, bs, D), dtype=raw_dt, device="cuda").view(dt)
+    ksc = vsc = 1.0
+    if cache == "fp8":
+        ksc = c / 448.0
+        vsc = float(np.float32(np.abs(W.storage_to_f32(val_st, "bf16")).max()) / np.float32(448.0))
+    pa.reshape_and_cache(key, value, kc, vc, torch.from_numpy(np.concatenate(slots)).cuda(), ksc, vsc)
+    q = np.zeros((B, Hkv * G, D), np.float32)
+    q[:, :, 0] = c
+    qt = storage_to_torch(W.to_storage(q, q_dt), q_dt).cuda()
+    tab = torch.from_numpy(tables).cuda()
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for v in (["valu", "mfma"] if G <= 2 else ["mfma"]):
+        set_variant(v)
+        out = pa.decode(qt, kc, vc, tab, lt, 1.0 / math.sqrt(D), k_scale=ksc, v_scale=vsc,
+                        out_dtype=torch.float32).cpu().numpy()
+        vcache = vc.view(torch.uint8).cpu().numpy() if cache == "fp8" else None
+        for s, tstar in enumerate(targets):
+            blk, row = int(tables[s, tstar // bs]), tstar % bs
+            for h in range(Hkv):
+                if cache == "fp8":
+                    expect = (O.e4m3_decode(vcache[blk, h, row], 1.0).astype(np.float32) * np.float32(vsc))
+                else:
+                    expect = W.storage_to_f32(val_st[sum(lens[:s]) + tstar, h], src)
+                for i in range(G):
+                    assert np.array_equal(out[s, h * G + i], expect), (s, tstar, h, i)

@@ -76,6 +76,33 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def _identity_layout(w, batch, slots_new):
+    """Renumber physical blocks so each sequence's blocks are consecutive and in
+    logical order (block tables become ranges); returns the new token slots."""
+    import numpy as np
+    import torch
+
+    nblk = (w.context_lens.astype(np.int64) + w.bs - 1) // w.bs
+    order = [int(b) for s in range(w.B) for b in w.block_tables[s, :nblk[s]]]
+    if len(set(order)) != len(order):
+        raise SystemExit("--identity-tables needs a workload whose sequences share no blocks")
+    rest = sorted(set(range(w.num_blocks)) - set(order))
+    perm = np.empty(w.num_blocks, np.int64)
+    perm[np.array(order + rest, np.int64)] = np.arange(w.num_blocks)
+    pt = torch.from_numpy(perm).to(batch.kc.device)
+    raw = (lambda t: t.view(torch.uint8)) if batch.kc.element_size() == 1 else (lambda t: t.view(torch.int16))
+    for name in ("kc", "vc"):
+        old = getattr(batch, name)
+        new = torch.empty_like(raw(old))
+        new[pt] = raw(old)
+        setattr(batch, name, new.view(old.dtype))
+    tables = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    w.block_tables = tables
+    batch.tables = torch.from_numpy(tables).to(batch.kc.device)
+    b = slots_new // w.bs
+    return pt[b] * w.bs + slots_new % w.bs
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +111,12 @@ def main():
     ap.add_argument("--config", default="llama8b")
     ap.add_argument("--no-flush", action="store_true", help="do not evict L2/MALL between steps")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0 = skip)")
+    ap.add_argument("--identity-tables", action="store_true",
+                    help="ablation: move every sequence's blocks into consecutive physical blocks, in order "
+                         "(same values, no scattered indirection)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MiB a few times (outside the timed region), "
+                         "to scale profiler byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this path is single-GPU by design)",
@@ -103,11 +136,29 @@ def main():
         f"sum(L)={int(w.context_lens.sum())}")
     batch = DeviceBatch(w, device=dev, skip_last_append=True)
     k_new, v_new, slots_new = batch.rows_for(w.ops[-1])
+    if args.identity_tables:
+        slots_new = _identity_layout(w, batch, slots_new)
     log("pools filled")
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy: 3 x {args.calib_copy_mb} MiB read + written")
     out = torch.empty((w.B, w.Hq, w.D), dtype=batch.q.dtype, device=dev)
     ws_bytes = pa.decode_workspace_size(w.B, w.Hkv, w.group, w.D, w.bs, w.max_context_len)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # Cache eviction between steps: READ a 1 GiB buffer (larger than the 256 MB
+    # MALL plus the L2s).  A write-based flush would leave dirty lines whose
+    # write-back then competes with the decode's reads inside the timed region.
+    flush = None if args.no_flush else torch.ones(1 << 27, dtype=torch.int64, device=dev)
+
+    def evict():
+        if flush is not None:
+            flush.sum()
 
     def append():
         pa.reshape_and_cache(k_new, v_new, batch.kc, batch.vc, slots_new, w.k_scale, w.v_scale)
@@ -117,8 +168,7 @@ def main():
                   k_scale=w.k_scale, v_scale=w.v_scale, out=out, workspace=ws)
 
     for i in range(args.warmup):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
+        evict()
         append()
         decode()
     torch.cuda.synchronize()
@@ -128,8 +178,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)  # evicts L2 and the MALL; outside the step's events
+        evict()  # outside the step's events
         ev[i][0].record()
         append()
         ev[i][1].record()
@@ -168,7 +217,7 @@ def main():
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
             "block_size": w.bs, "cache_dtype": w.cache_dtype, "q_dtype": w.q_dtype, "seed": w.seed,
             "sum_context_len": int(w.context_lens.sum()), "kv_bytes": kv_bytes, "parallelism": "single-gpu",
-            "l2_mall_flush_between_steps": flush is not None,
+            "l2_mall_flush_between_steps": flush is not None, "identity_tables": args.identity_tables,
         },
         "seq_heads_per_s": round(w.B * w.Hq / (ms_step * 1e-3), 1),
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),

@@ -89,7 +89,8 @@ typedef enum {
  * for every kv head h.  enc is a bit copy when cache_dtype == src_dtype; for
  * an FP8 cache it is the E4M3FN code of fp32(x) / k_scale (v_scale for V)
  * with IEEE fp32 division, round-to-nearest-even, magnitudes beyond 448
- * saturating to 448 and NaN kept as NaN.
+ * saturating to 448 and a NaN input stored as the NaN code of its sign
+ * (0x7F or 0xFF).
  *   key, value     [T, num_kv_heads, head_dim], src_dtype (PA_F16 | PA_BF16)
  *   k_cache, v_cache [num_blocks, num_kv_heads, block_size, head_dim], cache_dtype
  *                  (== src_dtype, or PA_FP8_E4M3)

@@ -13,12 +13,26 @@ __device__ __forceinline__ float fp8_prescale(float x, float scale) {
   return y != y ? y : fminf(fmaxf(y, -448.0f), 448.0f);
 }
 
+// The hardware convert writes every NaN as the negative NaN code (0xFF);
+// E4M3FN has a NaN of each sign (S.1111.111), so the input's sign is put
+// back for NaN inputs.
+__device__ __forceinline__ uint32_t keep_nan_sign(uint32_t w, const float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (x[i] != x[i]) {
+      const uint32_t code = 0x7Fu | ((__float_as_uint(x[i]) >> 24) & 0x80u);
+      w = (w & ~(0xFFu << (8 * i))) | (code << (8 * i));
+    }
+  }
+  return w;
+}
+
 __device__ __forceinline__ i32x2 encode8_fp8(const float* x, float scale) {
   int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prescale(x[0], scale), fp8_prescale(x[1], scale), 0, false);
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prescale(x[2], scale), fp8_prescale(x[3], scale), w0, true);
   int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prescale(x[4], scale), fp8_prescale(x[5], scale), 0, false);
   w1 = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_prescale(x[6], scale), fp8_prescale(x[7], scale), w1, true);
-  return i32x2{w0, w1};
+  return i32x2{(int)keep_nan_sign((uint32_t)w0, x), (int)keep_nan_sign((uint32_t)w1, x + 4)};
 }
 
 // One thread per 8 elements of one (token, kv head) row.

@@ -96,6 +96,19 @@ __device__ __forceinline__ int load_block_ids(const DecodeArgs& a, const Item& t
   return id;
 }
 
+// Byte offset, from the start of a KV head's first chunk, of the partition's
+// last position (tok_end - 1), which always holds written data.  Lanes whose
+// position lies past the end load this row instead of predicating the load:
+// every load stays unconditional (so the compiler can keep several chunks in
+// flight and wait on them one at a time), and the masked lanes' scores are
+// set to -inf, so the row they read adds exactly zero.
+__device__ __forceinline__ int64_t last_row_offset(const Item& t, int ids, int bs, int64_t blk_stride,
+                                                   int row_bytes) {
+  const int last = t.tok_end - 1;
+  const int id = __builtin_amdgcn_readlane(ids, last / bs - t.tok0 / bs);
+  return (int64_t)id * blk_stride + (int64_t)(last % bs) * row_bytes;
+}
+
 // Store n consecutive outputs of (s, head) starting at d0.
 __device__ __forceinline__ void store_out(const DecodeArgs& a, int s, int head, int D, int d0,
                                           const float* v, int n) {

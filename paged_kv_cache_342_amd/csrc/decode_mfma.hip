@@ -54,13 +54,13 @@ struct ChunkRaw {
 template <int N>
 __device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t* o) {
   if constexpr (N == 4) {
-    i32x4 x = ld16(p);
+    i32x4 x = ld16_stream(p);
     o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
   } else if constexpr (N == 2) {
-    i32x2 x = ld8(p);
+    i32x2 x = ld8_stream(p);
     o[0] = x[0]; o[1] = x[1];
   } else {
-    o[0] = ld4(p);
+    o[0] = ld4_stream(p);
   }
 }
 
@@ -114,10 +114,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const uint8_t* kbase = a.k_cache + (int64_t)t.h * kChunkBytes;
     const uint8_t* vbase = a.v_cache + (int64_t)t.h * kChunkBytes;
     const int nchunks = (t.tok_end - t.tok0 + 31) / 32;
+    const int64_t last_off = last_row_offset(t, ids, BS, blk_stride, D * e);
 
     auto load_chunk = [&](int c, Raw& raw) {
       const int ctok = t.tok0 + 32 * c;  // first position of the chunk
-      const int cb = 32 * c / BS;        // its first block, relative to the partition
+      // its first block, relative to the partition (clamped so that the
+      // chunk just past the end still names lanes of `ids`)
+      const int cb = min(32 * c / BS, 64 - (32 + BS - 1) / BS);
       int id[4];
       if constexpr (BS == 32) {
         id[0] = __builtin_amdgcn_readlane(ids, cb);
@@ -134,11 +137,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         const int tc = 16 * tt + r;
         const int bsel = BS == 32 ? 0 : (BS == 16 ? tt : 2 * tt + (r >> 3));
         const bool ok = ctok + tc < t.tok_end;
-        const uint8_t* row = kbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e;
+        const int64_t roff = ok ? (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : last_off;
+        const uint8_t* row = kbase + roff;
 #pragma unroll
         for (int u = 0; u < Raw::KR; ++u) {
           const int off = kFp8 ? 64 * u + 16 * gq : (32 * u + 8 * gq) * 2;
-          raw.k[tt][u] = ok ? ld16(row + off) : i32x4{0, 0, 0, 0};
+          raw.k[tt][u] = ld16_stream(row + off);
         }
       }
       // V: whole rows, position slot j -> 16*(j>>2) + 4*gq + (j&3)
@@ -147,13 +151,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
         const int bsel = BS == 32 ? 0 : (BS == 16 ? (j >> 2) : 2 * (j >> 2) + (gq >> 1));
         const bool ok = ctok + tc < t.tok_end;
-        const uint8_t* row = vbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e + W * r * e;
-        if (ok) {
-          load_dwords<VD>(row, raw.v[j]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < VD; ++i) raw.v[j][i] = 0;
-        }
+        const int64_t roff = ok ? (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : last_off;
+        load_dwords<VD>(vbase + roff + W * r * e, raw.v[j]);
       }
     };
 
@@ -258,14 +257,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       }
     };
 
-    // double-buffered walk over the partition's chunks
+    // Double-buffered walk over the partition's chunks.  The next chunk is
+    // always requested (past the end every lane reads the last row), so no
+    // load sits under a branch and each wait covers only the chunk it needs.
     Raw buf0, buf1;
     load_chunk(0, buf0);
     for (int c = 0; c < nchunks; c += 2) {
-      if (c + 1 < nchunks) load_chunk(c + 1, buf1);
+      load_chunk(c + 1, buf1);
       compute_chunk(c, buf0);
       if (c + 1 >= nchunks) break;
-      if (c + 2 < nchunks) load_chunk(c + 2, buf0);
+      load_chunk(c + 2, buf0);
       compute_chunk(c + 1, buf1);
     }
 

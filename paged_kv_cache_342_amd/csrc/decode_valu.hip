@@ -113,17 +113,18 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     const uint8_t* kbase = a.k_cache + (int64_t)t.h * kChunkBytes;
     const uint8_t* vbase = a.v_cache + (int64_t)t.h * kChunkBytes;
     const int ntiles = (t.tok_end - t.tok0 + TT - 1) / TT;
+    const int64_t last_off = last_row_offset(t, ids, BS, blk_stride, D * e);
 
     auto load_tile = [&](int tile, Raw& raw) {
       const int tc = TT * tile + row;  // position relative to the partition
       const int id = __shfl(ids, tc / BS);
       const bool ok = t.tok0 + tc < t.tok_end;
-      const int64_t off = (int64_t)id * blk_stride + (tc % BS) * D * e;
+      const int64_t off = ok ? (int64_t)id * blk_stride + (tc % BS) * D * e : last_off;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int col = 16 * (c + R * u);
-        raw.k[u] = ok ? ld16(kbase + off + col) : i32x4{0, 0, 0, 0};
-        raw.v[u] = ok ? ld16(vbase + off + col) : i32x4{0, 0, 0, 0};
+        raw.k[u] = ld16_stream(kbase + off + col);
+        raw.v[u] = ld16_stream(vbase + off + col);
       }
     };
 
@@ -169,13 +170,15 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
       }
     };
 
+    // Double-buffered; the next tile is always requested (past the end every
+    // lane reads the last row), so no load sits under a branch.
     Raw buf0, buf1;
     load_tile(0, buf0);
     for (int tile = 0; tile < ntiles; tile += 2) {
-      if (tile + 1 < ntiles) load_tile(tile + 1, buf1);
+      load_tile(tile + 1, buf1);
       compute_tile(tile, buf0);
       if (tile + 1 >= ntiles) break;
-      if (tile + 2 < ntiles) load_tile(tile + 2, buf0);
+      load_tile(tile + 2, buf0);
       compute_tile(tile + 1, buf1);
     }
 

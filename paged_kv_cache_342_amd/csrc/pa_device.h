@@ -121,6 +121,17 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // ---- memory --------------------------------------------------------------
 __device__ __forceinline__ i32x4 ld16(const void* p) { return *reinterpret_cast<const i32x4*>(p); }
+// KV cache rows are read once per call: nontemporal loads keep them from
+// displacing reusable lines and stream better from HBM.
+__device__ __forceinline__ i32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(p));
+}
+__device__ __forceinline__ i32x2 ld8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const i32x2*>(p));
+}
+__device__ __forceinline__ int ld4_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const int*>(p));
+}
 __device__ __forceinline__ i32x2 ld8(const void* p) { return *reinterpret_cast<const i32x2*>(p); }
 __device__ __forceinline__ int ld4(const void* p) { return *reinterpret_cast<const int*>(p); }
 

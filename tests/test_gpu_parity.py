@@ -80,9 +80,11 @@ def test_fp8_encode_exhaustive(src, scale):
     pa.reshape_and_cache(key, value, kc, vc, slots, scale, scale)
     got_k = kc.view(torch.uint8).cpu().numpy().transpose(0, 2, 1, 3).reshape(-1)
     got_v = vc.view(torch.uint8).cpu().numpy().transpose(0, 2, 1, 3).reshape(-1)
-    x = O.widen(bits, src).astype(np.float32)
+    # oracle storage convention: f16 as numpy.float16, bf16 as uint16 bit patterns
+    as_src = (lambda b: b.view(np.float16)) if src == "f16" else (lambda b: b)
+    x = O.widen(as_src(bits), src).astype(np.float32)
     ref_k = O.e4m3_encode(x, scale)
-    ref_v = O.e4m3_encode(O.widen(rows[::-1].reshape(-1), src).astype(np.float32), scale)
+    ref_v = O.e4m3_encode(O.widen(as_src(rows[::-1].reshape(-1).copy()), src).astype(np.float32), scale)
     bad = np.nonzero(got_k != ref_k)[0]
     if len(bad):
         log(f"  first mismatches: {[(hex(int(bits[i])), hex(int(got_k[i])), hex(int(ref_k[i]))) for i in bad[:8]]}")

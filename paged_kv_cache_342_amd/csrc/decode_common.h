@@ -1,56 +1,59 @@
-// Shared definitions of the paged decode kernels: launch arguments, work
-// items and the epilogue stores.
+// Shared parts of the paged decode kernels: launch arguments, the balanced
+// split of the batch over wavefronts, the block-id prefetcher and the
+// epilogue stores.
 //
-// Work decomposition.  A sequence of L tokens is cut into partitions of
-// `part_tokens` consecutive positions (split-K over the context).  One
-// wavefront handles one (sequence, partition, KV head[, head tile]) item and
-// produces, for each query head of that KV head, the running maximum m (log2
-// domain), the sum l of 2^(score - m) and the unnormalised accumulator
-// acc = sum 2^(score - m) * V.  A sequence that fits in one partition is
-// normalised and written to `out` directly; otherwise the partials go to the
-// workspace and the reduce kernel merges them:
-//   M = max_p m_p,  out = v_scale * sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// Work split.  Every sequence is cut into chunks of kChunk consecutive
+// positions (the last chunk may be partial) and the chunks of all sequences
+// are laid end to end, sequence after sequence.  That line of C chunks is
+// cut into equal slices of S chunks, and one wavefront handles one slice for
+// one KV head (and one tile of up to 16 query heads): every wave streams the
+// same number of K/V bytes, whatever the mix of context lengths, and it
+// streams them as one long run.  A slice may hold the tail of one sequence,
+// several whole sequences and the head of another; each such piece is a
+// segment.  A segment that is a whole sequence is normalised and written to
+// `out` directly.  A sequence cut by slice boundaries leaves one partial
+// result per slice -- the running maximum m (log2 domain), the sum
+// l = sum 2^(score - m) and acc = sum 2^(score - m) V for each query head --
+// and the merge kernel combines them in slice order:
+//   M = max_k m_k,  out = v_scale * sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
+// The partial of sequence s from slice k is stored in row k + s, which is
+// unique: the slices that cut s and those that cut s + 1 overlap in at most
+// one slice.
+//
+// Each wave computes the prefix sum of chunk counts itself (the lengths are
+// read once into LDS), so no separate planning kernel runs before it.
 #pragma once
 
 #include "pa_device.h"
 
 namespace pa {
 
+constexpr int kChunk = 32;        // positions per chunk, the unit of the split
+constexpr int kScanMax = 4096;    // sequences one launch scans in LDS
+constexpr int kIdAhead = 6;       // chunks of block ids held ahead of the loads
+
 struct DecodeArgs {
-  void* out;
-  const void* q;
+  void* out;                   // [B, Hq, D] (already offset to this launch's first sequence)
+  const void* q;               // [B, Hq, D]
   const uint8_t* k_cache;
   const uint8_t* v_cache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  const int32_t* work;  // [0] = item count; items as (seq, partition) int pairs from work + 2
-  float* part_acc;      // [B, Hq, nparts, D]
-  float* part_ml;       // [B, Hq, nparts, 2] = (m, l)
+  const int32_t* block_tables; // [B, M]
+  const int32_t* context_lens; // [B]
+  int32_t* meta;               // workspace: [0] = S, [1] = slices used, [2 + s] = first chunk of s (B + 1 entries)
+  float* part_acc;             // workspace: [rows, Hq, D], rows = nslices + B
+  float* part_ml;              // workspace: [rows, Hq, 2] = (m, l)
   int64_t num_blocks;
-  int32_t B, Hkv, G, M;  // M = max_blocks_per_seq
-  int32_t max_ctx;       // effective bound: min(max_context_len, M * bs)
-  int32_t nparts;        // partitions per sequence the workspace holds
-  int32_t part_tokens;
-  int32_t head_tiles;    // query-head tiles of 16 per KV head (MFMA kernel), 1 otherwise
-  int32_t dense;         // 1: item i is (sequence i, partition 0) and there are B items
-  int32_t out_dtype;     // 0 f32, 1 f16, 2 bf16
-  float qk_scale_log2;   // scale * k_scale * log2(e)
+  int32_t B, Hkv, G, M;        // M = max_blocks_per_seq
+  int32_t max_ctx;             // lengths are clamped to [0, max_ctx]
+  int32_t nslices;             // slices per (KV head, head tile) in the grid
+  int32_t min_slice;           // fewest chunks per slice
+  int32_t head_tiles;          // query-head tiles of 16 per KV head (MFMA kernel), 1 otherwise
+  int32_t out_dtype;           // 0 f32, 1 f16, 2 bf16
+  float qk_scale_log2;         // scale * k_scale * log2(e)
   float v_scale;
 };
 
-struct Item {
-  int s, p, h, ht;
-  int L;        // clamped context length
-  int nparts;   // partitions of this sequence (>= 1)
-  int tok0;     // first position of the partition
-  int tok_end;  // one past its last position
-};
-
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
-__device__ __forceinline__ int item_count(const DecodeArgs& a) {
-  return a.dense ? a.B : uniform(a.work[0]);
-}
 
 // context length of sequence s, clamped to [0, max_ctx]
 __device__ __forceinline__ int context_len(const DecodeArgs& a, int s) {
@@ -58,56 +61,130 @@ __device__ __forceinline__ int context_len(const DecodeArgs& a, int s) {
   return L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
 }
 
-__device__ __forceinline__ Item item_at(const DecodeArgs& a, int flat) {
-  const int per = a.Hkv * a.head_tiles;
-  const int it = flat / per;
-  const int rem = flat - it * per;
-  Item t;
-  t.h = rem / a.head_tiles;
-  t.ht = rem - t.h * a.head_tiles;
-  if (a.dense) {
-    t.s = it;
-    t.p = 0;
-  } else {
-    t.s = uniform(a.work[2 + 2 * it]);
-    t.p = uniform(a.work[3 + 2 * it]);
-  }
-  const int L = context_len(a, t.s);
-  t.L = L;
-  t.nparts = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
-  t.tok0 = t.p * a.part_tokens;
-  int e = t.tok0 + a.part_tokens;
-  t.tok_end = e < L ? e : L;
-  return t;
-}
-
-// The partition's block ids, one per lane (lane j holds logical block
-// tok0 / bs + j); ids outside the pool read as block 0 so no access leaves
-// the pool.  A partition spans at most 64 blocks.
-__device__ __forceinline__ int load_block_ids(const DecodeArgs& a, const Item& t, int bs) {
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
   const int lane = __lane_id();
-  const int blk0 = t.tok0 / bs;
-  const int nblk = (t.tok_end + bs - 1) / bs - blk0;
-  int id = 0;
-  if (lane < nblk) {
-    id = a.block_tables[(int64_t)t.s * a.M + blk0 + lane];
-    if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  return id;
+  return x;
 }
 
-// Byte offset, from the start of a KV head's first chunk, of the partition's
-// last position (tok_end - 1), which always holds written data.  Lanes whose
-// position lies past the end load this row instead of predicating the load:
-// every load stays unconditional (so the compiler can keep several chunks in
-// flight and wait on them one at a time), and the masked lanes' scores are
-// set to -inf, so the row they read adds exactly zero.
-__device__ __forceinline__ int64_t last_row_offset(const Item& t, int ids, int bs, int64_t blk_stride,
-                                                   int row_bytes) {
-  const int last = t.tok_end - 1;
-  const int id = __builtin_amdgcn_readlane(ids, last / bs - t.tok0 / bs);
-  return (int64_t)id * blk_stride + (int64_t)(last % bs) * row_bytes;
+// This wave's slice [c0, c1) of the chunk line, and the first sequence it
+// visits.  cum[s] (LDS) = first chunk of sequence s, cum[B] = C.
+struct Slice {
+  int k;        // slice index
+  int S;        // chunks per slice
+  int neff;     // slices that hold work (>= 1)
+  int c0, c1;   // chunk range
+  bool last;    // the last slice also owns empty sequences at the very end
+  int s_first;  // first sequence it visits
+};
+
+// Fills cum[] and sl; returns false when the slice holds nothing.  Wave 0
+// also publishes S, the slice count and cum[] for the merge kernel.
+__device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int k, Slice& sl) {
+  const int lane = __lane_id();
+  int carry = 0;
+  for (int base = 0; base < a.B; base += 64) {
+    const int s = base + lane;
+    int n = 0;
+    if (s < a.B) {
+      int L = a.context_lens[s];
+      L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+      n = (L + kChunk - 1) / kChunk;
+    }
+    const int inc = wave_inclusive_sum(n);
+    if (s < a.B) cum[s + 1] = carry + inc;
+    carry += __builtin_amdgcn_readlane(inc, 63);
+  }
+  if (lane == 0) cum[0] = 0;
+  __syncthreads();
+  const int C = carry;
+  const int S = max(a.min_slice, (C + a.nslices - 1) / a.nslices);
+  const int neff = max(1, (C + S - 1) / S);
+  if (blockIdx.x == 0) {
+    if (lane == 0) {
+      a.meta[0] = S;
+      a.meta[1] = neff;
+    }
+    for (int s = lane; s <= a.B; s += 64) a.meta[2 + s] = cum[s];
+  }
+  if (k >= neff) return false;
+  sl.k = k;
+  sl.S = S;
+  sl.neff = neff;
+  sl.c0 = k * S;
+  sl.c1 = min(C, sl.c0 + S);
+  sl.last = k == neff - 1;
+  // first s that does not lie wholly before c0; an empty sequence at c0
+  // belongs to this slice (binary search over a monotone predicate)
+  int lo = 0, hi = a.B;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int e = cum[mid + 1];
+    const bool before = e < sl.c0 || (e == sl.c0 && e > cum[mid]);
+    if (before) lo = mid + 1; else hi = mid;
+  }
+  sl.s_first = uniform(lo);
+  return true;
 }
+
+// Does sequence s (chunks [cs, ce)) lie beyond this slice?  An empty
+// sequence at c1 belongs to the next slice, except at the very end.
+__device__ __forceinline__ bool past_slice(const Slice& sl, int cs, int ce) {
+  return cs > sl.c1 || (cs == sl.c1 && (ce > cs || !sl.last));
+}
+
+// Pieces sequence s is cut into, and whether this slice's piece is the whole.
+__device__ __forceinline__ bool whole_sequence(const Slice& sl, int cs, int ce) {
+  return cs / sl.S == (ce - 1) / sl.S;
+}
+
+// Block ids of a segment, held in one register as a ring of 64 slots: block
+// j of the segment (counted from its first block) sits in lane j % 64.  The
+// ring holds the blocks of the next kIdAhead + 1 chunks; each step requests
+// one more chunk's ids (an unconditional load whose lanes that do not take
+// part re-read a valid entry), and that load is merged one step later, so no
+// wait ever falls on a table read that was just issued.
+template <int BS>
+struct IdRing {
+  static constexpr int NB = kChunk / BS;  // blocks per chunk
+  static_assert((kIdAhead + 2) * NB <= 64, "ring too small for the lookahead");
+  const int32_t* row;  // block table row of the sequence, from the segment's first block
+  int nblk;            // blocks in the segment
+  int ids;             // the ring
+  int pending;         // ids of chunk `next`, not merged yet
+  int next;            // chunk whose ids are pending
+
+  __device__ __forceinline__ int fetch(int chunk) const {
+    const int lane = __lane_id();
+    const int slot0 = (chunk * NB) & 63;
+    const int j = chunk * NB + ((lane - slot0) & 63);
+    return row[j < nblk ? j : nblk - 1];
+  }
+  __device__ __forceinline__ void start(const int32_t* table_row, int blocks) {
+    row = table_row;
+    nblk = blocks;
+    const int lane = __lane_id();
+    ids = row[lane < nblk ? lane : nblk - 1];  // chunks 0 .. 64/NB - 1
+    next = kIdAhead + 1;
+    pending = fetch(next);
+  }
+  // merge the pending chunk's ids, then request the one after it
+  __device__ __forceinline__ void advance() {
+    const int lane = __lane_id();
+    const int slot0 = (next * NB) & 63;
+    if (((lane - slot0) & 63) < NB) ids = pending;
+    ++next;
+    pending = fetch(next);
+  }
+  // id of block i (< NB) of chunk c; valid for chunks within the lookahead
+  __device__ __forceinline__ int id(int c, int i) const {
+    return __builtin_amdgcn_readlane(ids, (c * NB + i) & 63);
+  }
+};
 
 // Store n consecutive outputs of (s, head) starting at d0.
 __device__ __forceinline__ void store_out(const DecodeArgs& a, int s, int head, int D, int d0,
@@ -132,18 +209,19 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int s, int head, 
   }
 }
 
-__device__ __forceinline__ int64_t part_index(const DecodeArgs& a, int s, int head, int p) {
-  return ((int64_t)s * a.Hkv * a.G + head) * a.nparts + p;
+// workspace row of the partial of sequence s from slice k, query head `head`
+__device__ __forceinline__ int64_t part_row(const DecodeArgs& a, int k, int s, int head) {
+  return (int64_t)(k + s) * a.Hkv * a.G + head;
 }
 
-__device__ __forceinline__ void store_partial(const DecodeArgs& a, int s, int head, int p, int D,
-                                              int d0, const float* v, int n) {
-  float* o = a.part_acc + part_index(a, s, head, p) * D + d0;
+__device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t row, int D, int d0,
+                                              const float* v, int n) {
+  float* o = a.part_acc + row * D + d0;
   for (int i = 0; i < n; i += 4) *reinterpret_cast<f32x4*>(o + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
 }
 
-__device__ __forceinline__ void store_ml(const DecodeArgs& a, int s, int head, int p, float m, float l) {
-  *reinterpret_cast<f32x2*>(a.part_ml + 2 * part_index(a, s, head, p)) = f32x2{m, l};
+__device__ __forceinline__ void store_ml(const DecodeArgs& a, int64_t row, float m, float l) {
+  *reinterpret_cast<f32x2*>(a.part_ml + 2 * row) = f32x2{m, l};
 }
 
 }  // namespace pa

@@ -1,5 +1,7 @@
-// Split-K planning, the work-list and reduce kernels, and the host side of
-// pa_decode: partition sizing, workspace layout and kernel choice.
+// Host side of pa_decode (slice count, workspace layout, kernel choice,
+// launches) and the kernel that merges the partial results of sequences cut
+// by slice boundaries.
+#include <climits>
 #include <cstdlib>
 #include <cstring>
 
@@ -14,73 +16,63 @@ bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int b
                         dim3 grid, hipStream_t stream);
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
 
-// Work list: one (sequence, partition) pair per partition that holds at
-// least one position; an empty sequence gets one item (it writes zeros).
-// One workgroup; sequences are taken 1024 at a time with an LDS scan.
-__global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* context_lens, int B,
-                                                           int max_ctx, int part_tokens,
-                                                           int32_t* work) {
-  __shared__ int scan[1024];
-  const int tid = threadIdx.x;
-  int total = 0;
-  for (int base = 0; base < B; base += 1024) {
-    const int s = base + tid;
-    int n = 0;
-    if (s < B) {
-      int L = context_lens[s];
-      L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
-      n = L > 0 ? (L + part_tokens - 1) / part_tokens : 1;
-    }
-    scan[tid] = n;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int first = total + scan[tid] - n;
-    for (int k = 0; k < n; ++k) {
-      work[2 + 2 * (first + k)] = s;
-      work[3 + 2 * (first + k)] = k;
-    }
-    total += scan[1023];
-    __syncthreads();
-  }
-  if (tid == 0) work[0] = total;
-}
-
-// Merge the partitions of one (sequence, KV head) for every query head of
-// the group:  M = max m_p;  out = v_scale * sum 2^(m_p-M) acc_p / sum 2^(m_p-M) l_p.
-// Partitions are visited in increasing order, so the result does not depend
-// on where the blocks sit in the pool.
+// One wave per (KV head, sequence): merge the slices' partials of each query
+// head of the group, in slice order, with an online rescale:
+//   M = max_k m_k;  out = v_scale * sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
+// Lane j handles four consecutive outputs of one query head; 64 / (D / 4)
+// heads are merged side by side.  Sequences that are whole in one slice were
+// written by the decode kernel and are skipped here.
 template <int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int LPH = D / 4;    // lanes per head
+  constexpr int HPP = 64 / LPH; // heads per pass
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int L = context_len(a, s);
-  const int n = L > 0 ? (L + a.part_tokens - 1) / a.part_tokens : 1;
-  if (n <= 1) return;  // written directly by the partition kernel
-  constexpr int D4 = D / 4;
-  for (int idx = threadIdx.x; idx < a.G * D4; idx += blockDim.x) {
-    const int i = idx / D4;
-    const int d = 4 * (idx - i * D4);
-    const int head = h * a.G + i;
-    const int64_t base = part_index(a, s, head, 0);
-    float M = -INFINITY;
-    for (int p = 0; p < n; ++p) M = fmaxf(M, a.part_ml[2 * (base + p)]);
+  const int S = a.meta[0];
+  const int neff = a.meta[1];
+  const int cs = a.meta[2 + s], ce = a.meta[3 + s];
+  if (ce <= cs) return;
+  const int kf = cs / S;
+  const int kl = min((ce - 1) / S, neff - 1);
+  if (kl <= kf) return;
+  const int np = kl - kf + 1;
+  const int lane = threadIdx.x;
+  const int sub = lane / LPH;
+  const int d = 4 * (lane % LPH);
+  for (int i0 = 0; i0 < a.G; i0 += HPP) {
+    const int i = i0 + sub;
+    const bool act = i < a.G;
+    const int head = h * a.G + (act ? i : 0);
+    float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    for (int p = 0; p < n; ++p) {
-      const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * (base + p));
-      const float w = fast_exp2(ml[0] - M);
-      den = fmaf(w, ml[1], den);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(a.part_acc + (base + p) * D + d);
-      num += w * x;
+    constexpr int UNR = 4;
+    for (int p0 = 0; p0 < np; p0 += UNR) {
+      f32x2 ml[UNR];
+      f32x4 x[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int p = min(p0 + u, np - 1);
+        const int64_t row = part_row(a, kf + p, s, head);
+        ml[u] = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * row);
+        x[u] = *reinterpret_cast<const f32x4*>(a.part_acc + row * D + d);
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        if (p0 + u < np) {
+          const float Mn = fmaxf(M, ml[u][0]);
+          const float ca = fast_exp2(M - Mn);
+          const float cb = fast_exp2(ml[u][0] - Mn);
+          den = den * ca + ml[u][1] * cb;
+          num = num * ca + x[u] * cb;
+          M = Mn;
+        }
+      }
     }
-    const float f = a.v_scale / den;
-    const float v[4] = {num[0] * f, num[1] * f, num[2] * f, num[3] * f};
-    store_out(a, s, head, D, d, v, 4);
+    if (act) {
+      const float f = a.v_scale / den;
+      const float v[4] = {num[0] * f, num[1] * f, num[2] * f, num[3] * f};
+      store_out(a, s, head, D, d, v, 4);
+    }
   }
 }
 
@@ -88,27 +80,39 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx) {
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev] = n;
+  return n;
+}
+
+static int waves_per_cu() {
+  const char* v = std::getenv("PA_DECODE_WAVES_PER_CU");
+  const int n = v ? std::atoi(v) : 0;
+  return n >= 1 && n <= 32 ? n : 4;
+}
+
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu) {
+  (void)bs;
   DecodePlan p{};
-  // Partition length: 256 positions, shorter while the batch would give
-  // fewer than ~4096 items (16 per compute unit), longer while a sequence
-  // would need more than 64 partitions (bounded by 64 blocks per partition).
-  int P = 256;
-  auto parts = [&](int len) { return max_ctx > 0 ? (max_ctx + len - 1) / len : 1; };
-  while (P > 64 && (int64_t)B * Hkv * parts(P) < 4096) P /= 2;
-  while (parts(P) > 64 && P * 2 <= 64 * bs) P *= 2;
-  p.part_tokens = P;
-  p.nparts = parts(P);
-  if (p.nparts <= 1) {
-    p.nparts = 1;
-    return p;  // every sequence fits in one partition: no workspace
-  }
+  const int64_t waves = (int64_t)waves_per_cu() * num_cu;
+  const int64_t per = (int64_t)Hkv * head_tiles;
+  p.nslices = (int)std::max<int64_t>(1, (waves + per - 1) / per);
+  p.min_slice = 4;
+  const int64_t chunks = std::max<int64_t>(1, ((int64_t)std::max(max_ctx, 1) + kChunk - 1) / kChunk);
+  int64_t sub = std::min<int64_t>(kScanMax, INT_MAX / chunks);
+  p.sub_batch = (int)std::max<int64_t>(1, std::min<int64_t>(sub, std::max(B, 1)));
   const size_t Hq = (size_t)Hkv * G;
-  const size_t rows = (size_t)B * Hq * p.nparts;
-  p.work_off = 0;
-  p.ml_off = align256(sizeof(int32_t) * (2 + 2 * (size_t)B * p.nparts));
-  p.acc_off = p.ml_off + align256(sizeof(float) * 2 * rows);
-  p.bytes = p.acc_off + align256(sizeof(float) * (size_t)D * rows);
+  const size_t rows = (size_t)p.nslices + p.sub_batch;
+  p.meta_off = 0;
+  p.ml_off = align256(sizeof(int32_t) * (3 + (size_t)p.sub_batch));
+  p.acc_off = p.ml_off + align256(sizeof(float) * 2 * rows * Hq);
+  p.bytes = p.acc_off + align256(sizeof(float) * (size_t)D * rows * Hq);
   return p;
 }
 
@@ -124,73 +128,77 @@ bool decode_uses_valu(int variant, int G) { return variant == 1 || (variant == 0
 
 bool decode_valu_supported(int ct, int qt, int D, int bs, int G) { return valu_supports(ct, qt, D, bs, G); }
 
+static int elem_size(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
+
 pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
-  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx);
   const bool valu = decode_uses_valu(decode_variant_override(), r.G);
   if (valu && !valu_supports(r.cache_dtype, r.q_dtype, r.D, r.bs, r.G)) {
     set_error("pa_decode: the VALU kernel is not built for group %d, head_dim %d, block size %d",
               r.G, r.D, r.bs);
     return PA_ERR_UNSUPPORTED;
   }
-
-  {
-    const int64_t items = (int64_t)r.B * plan.nparts * r.Hkv * (valu ? 1 : (r.G + 15) / 16);
-    if (items >= ((int64_t)1 << 31)) {
-      set_error("pa_decode: %lld work items exceed the 32-bit item index", (long long)items);
-      return PA_ERR_UNSUPPORTED;
-    }
+  const int tiles = valu ? 1 : (r.G + 15) / 16;
+  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count());
+  if (r.workspace_bytes < plan.bytes) {
+    set_error("pa_decode: workspace of %zu bytes needed, %zu given", plan.bytes, r.workspace_bytes);
+    return PA_ERR_WORKSPACE;
   }
+  const int64_t grid_waves = (int64_t)plan.nslices * r.Hkv * tiles;
+  if (grid_waves >= ((int64_t)1 << 31)) {
+    set_error("pa_decode: %lld waves exceed the grid limit", (long long)grid_waves);
+    return PA_ERR_UNSUPPORTED;
+  }
+  const int Hq = r.Hkv * r.G;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(r.workspace);
   DecodeArgs a{};
-  a.out = r.out;
-  a.q = r.q;
   a.k_cache = reinterpret_cast<const uint8_t*>(r.k_cache);
   a.v_cache = reinterpret_cast<const uint8_t*>(r.v_cache);
-  a.block_tables = r.block_tables;
-  a.context_lens = r.context_lens;
+  a.meta = reinterpret_cast<int32_t*>(ws + plan.meta_off);
+  a.part_ml = reinterpret_cast<float*>(ws + plan.ml_off);
+  a.part_acc = reinterpret_cast<float*>(ws + plan.acc_off);
   a.num_blocks = r.num_blocks;
-  a.B = r.B;
   a.Hkv = r.Hkv;
   a.G = r.G;
   a.M = r.M;
   a.max_ctx = r.max_ctx;
-  a.nparts = plan.nparts;
-  a.part_tokens = plan.part_tokens;
-  a.head_tiles = valu ? 1 : (r.G + 15) / 16;
-  a.dense = plan.nparts == 1;
+  a.nslices = plan.nslices;
+  a.min_slice = plan.min_slice;
+  a.head_tiles = tiles;
   a.out_dtype = r.out_dtype == PA_F32 ? 0 : (r.out_dtype == PA_F16 ? 1 : 2);
   const bool fp8 = r.cache_dtype == PA_FP8_E4M3;
   a.qk_scale_log2 = r.scale * (fp8 ? r.k_scale : 1.f) * 1.4426950408889634f;
   a.v_scale = fp8 ? r.v_scale : 1.f;
-  if (!a.dense) {
-    uint8_t* ws = reinterpret_cast<uint8_t*>(r.workspace);
-    a.work = reinterpret_cast<const int32_t*>(ws + plan.work_off);
-    a.part_ml = reinterpret_cast<float*>(ws + plan.ml_off);
-    a.part_acc = reinterpret_cast<float*>(ws + plan.acc_off);
-    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, r.context_lens, r.B,
-                       r.max_ctx, plan.part_tokens, reinterpret_cast<int32_t*>(ws + plan.work_off));
-  }
-  const int64_t upper = (int64_t)r.B * plan.nparts * r.Hkv * a.head_tiles;
-  const int64_t cap = 16384;
-  const dim3 grid((unsigned)(upper < cap ? upper : cap));
   const int ct = r.cache_dtype, qt = r.q_dtype;
-  const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream)
-                       : launch_decode_mfma(a, ct, qt, r.D, r.bs, grid, stream);
-  if (!ok) {
-    set_error("pa_decode: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d, group %d (%s)",
-              ct, qt, r.D, r.bs, r.G, valu ? "valu" : "mfma");
-    return PA_ERR_UNSUPPORTED;
-  }
-  if (!a.dense) {
-    const dim3 rgrid(r.Hkv, r.B);
-    if (r.D == 64)
-      hipLaunchKernelGGL(decode_reduce_kernel<64>, rgrid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL(decode_reduce_kernel<128>, rgrid, dim3(256), 0, stream, a);
-  }
-  const hipError_t err = hipGetLastError();
-  if (err != hipSuccess) {
-    set_error("pa_decode: launch failed: %s", hipGetErrorString(err));
-    return PA_ERR_HIP;
+  const size_t out_row = (size_t)Hq * r.D * elem_size(r.out_dtype);
+  const size_t q_row = (size_t)Hq * r.D * 2;
+  // batches beyond one launch's scan capacity run as consecutive launches;
+  // they share the workspace, which stream order makes safe
+  for (int s0 = 0; s0 < r.B; s0 += plan.sub_batch) {
+    a.B = std::min(plan.sub_batch, r.B - s0);
+    a.out = reinterpret_cast<uint8_t*>(r.out) + (size_t)s0 * out_row;
+    a.q = reinterpret_cast<const uint8_t*>(r.q) + (size_t)s0 * q_row;
+    a.block_tables = r.block_tables + (int64_t)s0 * r.M;
+    a.context_lens = r.context_lens + s0;
+    const dim3 grid((unsigned)grid_waves);
+    const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream)
+                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, grid, stream);
+    if (!ok) {
+      set_error("pa_decode: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d, group %d (%s)",
+                ct, qt, r.D, r.bs, r.G, valu ? "valu" : "mfma");
+      return PA_ERR_UNSUPPORTED;
+    }
+    if (plan.nslices > 1) {
+      const dim3 mgrid(r.Hkv, a.B);
+      if (r.D == 64)
+        hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, dim3(64), 0, stream, a);
+      else
+        hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(64), 0, stream, a);
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+      set_error("pa_decode: launch failed: %s", hipGetErrorString(err));
+      return PA_ERR_HIP;
+    }
   }
   return PA_OK;
 }

@@ -1,8 +1,8 @@
 // Paged decode attention on the matrix cores (v_mfma_f32_16x16x32_{f16,bf16}).
 //
-// One wavefront handles one (sequence, partition, KV head, tile of up to 16
-// query heads) item and walks the partition 32 positions at a time.  Per
-// 32-position chunk:
+// One wavefront walks one slice of the batch (decode_common.h) for one KV
+// head and one tile of up to 16 of its query heads, 32 positions (a chunk)
+// at a time.  Per chunk:
 //   QK:  S^T[tok, head] = K[tok, :] . Q[head, :]  as two 16x16 output tiles,
 //        K rows are the A operand (one position per lane row), the group's
 //        query heads are the B operand (padded to 16 columns).
@@ -13,7 +13,10 @@
 // lane fetch contiguous 16-byte pieces: K rows give 64 contiguous bytes per
 // row per load instruction, and V is fetched as whole rows (16 lanes x 16 B)
 // and transposed inside each lane's registers (8 positions x head_dim/16
-// values) with byte permutes, so nothing is staged through LDS.
+// values) with byte permutes.  The next chunk's K/V is in flight in
+// registers while the current one is computed; loads are nontemporal, and
+// none of them sits under a branch (positions past the end of a segment
+// re-read its last row and get a score of -inf).
 //
 // Softmax runs online in fp32 in the log2 domain.  The running maximum of a
 // head only moves when some score exceeds it by more than kRescaleThreshold
@@ -64,6 +67,16 @@ __device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t* o) {
   }
 }
 
+// two fp32 -> packed 16-bit pair, round to nearest even (hardware converts)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <class CT, class QT, int D, int BS>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int e = CT::bytes;
@@ -75,68 +88,89 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   using Raw = ChunkRaw<CT, D>;
   constexpr int VD = Raw::VD;
   constexpr int64_t kChunkBytes = (int64_t)BS * D * e;  // one (block, head) chunk
+  constexpr int NB = kChunk / BS;
+
+  __shared__ int cum[kScanMax + 1];
 
   const int lane = threadIdx.x;
   const int r = lane & 15;   // A-operand row / B-operand column / C column
   const int gq = lane >> 4;  // k-slot group
   const int Hq = a.Hkv * a.G;
   const int64_t blk_stride = (int64_t)a.Hkv * kChunkBytes;
-  const int total = item_count(a) * a.Hkv * a.head_tiles;
 
-  for (int flat = blockIdx.x; flat < total; flat += gridDim.x) {
-    const Item t = item_at(a, flat);
-    const int col_head = 16 * t.ht + r;  // head within the group this lane's column carries
-    const bool col_ok = col_head < a.G;
-    const int head = t.h * a.G + col_head;
+  // wave -> (slice, head tile, KV head); the KV head varies fastest, so the
+  // workgroups of one KV head land on the same XCD
+  const int h = blockIdx.x % a.Hkv;
+  const int rest = blockIdx.x / a.Hkv;
+  const int ht = rest % a.head_tiles;
+  const int k = rest / a.head_tiles;
 
-    if (t.L == 0) {  // empty context: zeros
+  Slice sl;
+  if (!slice_setup(a, cum, k, sl)) return;
+
+  const int col_head = 16 * ht + r;  // head within the group this lane's column carries
+  const bool col_ok = col_head < a.G;
+  const int head = h * a.G + col_head;
+  const uint8_t* kbase = a.k_cache + (int64_t)h * kChunkBytes;
+  const uint8_t* vbase = a.v_cache + (int64_t)h * kChunkBytes;
+
+  for (int s = sl.s_first; s < a.B; ++s) {
+    const int cs = cum[s], ce = cum[s + 1];
+    if (past_slice(sl, cs, ce)) break;
+    const int L = context_len(a, s);
+    if (L == 0) {  // empty context: zeros, written by the slice that owns it
       if (col_ok) {
         float z[4 * W];
 #pragma unroll
         for (int i = 0; i < 4 * W; ++i) z[i] = 0.f;
-        store_out(a, t.s, head, D, 4 * W * gq, z, 4 * W);
+        store_out(a, s, head, D, 4 * W * gq, z, 4 * W);
       }
       continue;
     }
+    // this slice's segment of sequence s: positions [tok0, tok_end)
+    const int tok0 = (max(sl.c0, cs) - cs) * kChunk;
+    const int tok_end = min((min(sl.c1, ce) - cs) * kChunk, L);
+    const int nchunks = (tok_end - tok0 + kChunk - 1) / kChunk;
 
     // ---- Q as the B operand of QK, in the k-slot order the K loads use
     i32x4 qop[KK];
     {
-      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)t.s * Hq + head) * D * 2;
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
+                            ((int64_t)s * Hq + (col_ok ? head : h * a.G)) * D * 2;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int d = kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
-        qop[kk] = col_ok ? ld16(qrow + d * 2) : i32x4{0, 0, 0, 0};
+        const i32x4 x = ld16(qrow + d * 2);
+        qop[kk] = col_ok ? x : i32x4{0, 0, 0, 0};
       }
     }
 
-    const int ids = load_block_ids(a, t, BS);
-    const uint8_t* kbase = a.k_cache + (int64_t)t.h * kChunkBytes;
-    const uint8_t* vbase = a.v_cache + (int64_t)t.h * kChunkBytes;
-    const int nchunks = (t.tok_end - t.tok0 + 31) / 32;
-    const int64_t last_off = last_row_offset(t, ids, BS, blk_stride, D * e);
+    const int32_t* trow = a.block_tables + (int64_t)s * a.M;
+    const int blk0 = tok0 / BS;
+    IdRing<BS> ring;
+    ring.start(trow + blk0, (tok_end + BS - 1) / BS - blk0);
+    // the segment's last row, read by lanes whose position lies past the end
+    int64_t last_off;
+    {
+      int id = uniform(trow[(tok_end - 1) / BS]);
+      if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
+      last_off = (int64_t)id * blk_stride + (int64_t)((tok_end - 1) % BS) * D * e;
+    }
 
     auto load_chunk = [&](int c, Raw& raw) {
-      const int ctok = t.tok0 + 32 * c;  // first position of the chunk
-      // its first block, relative to the partition (clamped so that the
-      // chunk just past the end still names lanes of `ids`)
-      const int cb = min(32 * c / BS, 64 - (32 + BS - 1) / BS);
-      int id[4];
-      if constexpr (BS == 32) {
-        id[0] = __builtin_amdgcn_readlane(ids, cb);
-      } else if constexpr (BS == 16) {
-        id[0] = __builtin_amdgcn_readlane(ids, cb);
-        id[1] = __builtin_amdgcn_readlane(ids, cb + 1);
-      } else {
+      const int ctok = tok0 + kChunk * c;  // first position of the chunk
+      int id[NB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) id[i] = __builtin_amdgcn_readlane(ids, cb + i);
+      for (int i = 0; i < NB; ++i) {
+        const int x = ring.id(c, i);
+        id[i] = (x < 0 || (int64_t)x >= a.num_blocks) ? 0 : x;
       }
       // K: rows 16*tt + r
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int tc = 16 * tt + r;
         const int bsel = BS == 32 ? 0 : (BS == 16 ? tt : 2 * tt + (r >> 3));
-        const bool ok = ctok + tc < t.tok_end;
+        const bool ok = ctok + tc < tok_end;
         const int64_t roff = ok ? (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : last_off;
         const uint8_t* row = kbase + roff;
 #pragma unroll
@@ -150,7 +184,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       for (int j = 0; j < 8; ++j) {
         const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
         const int bsel = BS == 32 ? 0 : (BS == 16 ? (j >> 2) : 2 * (j >> 2) + (gq >> 1));
-        const bool ok = ctok + tc < t.tok_end;
+        const bool ok = ctok + tc < tok_end;
         const int64_t roff = ok ? (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : last_off;
         load_dwords<VD>(vbase + roff + W * r * e, raw.v[j]);
       }
@@ -162,7 +196,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     for (int i = 0; i < W; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute_chunk = [&](int c, const Raw& raw) {
-      const int ctok = t.tok0 + 32 * c;
+      const int ctok = tok0 + kChunk * c;
       // ---- QK
       i32x4 kop[2][KK];
 #pragma unroll
@@ -195,7 +229,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       for (int j = 0; j < 8; ++j) {
         const float raw_s = (j < 4 ? s0[j & 3] : s1[j & 3]) * a.qk_scale_log2;
         const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
-        sc[j] = ctok + tc < t.tok_end ? raw_s : -INFINITY;
+        sc[j] = ctok + tc < tok_end ? raw_s : -INFINITY;
         mx = fmaxf(mx, sc[j]);
       }
       if (wave_any(mx > m + kRescaleThreshold)) {
@@ -219,13 +253,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int jp = 0; jp < 4; ++jp) {
         if constexpr (kBf16V) {
-          const uint16_t h0 = f32_to_bf16_rne(p[2 * jp]), h1 = f32_to_bf16_rne(p[2 * jp + 1]);
-          const uint16_t l0 = f32_to_bf16_rne(p[2 * jp] - bf16_bits_to_f32(h0));
-          const uint16_t l1 = f32_to_bf16_rne(p[2 * jp + 1] - bf16_bits_to_f32(h1));
-          pop[jp] = (int)(h0 | ((uint32_t)h1 << 16));
-          plo[jp] = (int)(l0 | ((uint32_t)l1 << 16));
+          const uint32_t hi = pack_bf16(p[2 * jp], p[2 * jp + 1]);
+          const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
+          pop[jp] = (int)hi;
+          plo[jp] = (int)pack_bf16(p[2 * jp] - h0, p[2 * jp + 1] - h1);
         } else {
-          pop[jp] = (int)(f32_to_f16_rne(p[2 * jp]) | ((uint32_t)f32_to_f16_rne(p[2 * jp + 1]) << 16));
+          pop[jp] = (int)pack_f16(p[2 * jp], p[2 * jp + 1]);
         }
       }
       // ---- V^T as the A operand: 16-bit values per position, then transpose
@@ -250,22 +283,25 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int jp = 0; jp < 4; ++jp) {
           const uint32_t a0 = vt[2 * jp][dt >> 1], a1 = vt[2 * jp + 1][dt >> 1];
-          vop[jp] = (dt & 1) ? (int)((a0 >> 16) | (a1 & 0xFFFF0000u)) : (int)((a0 & 0xFFFFu) | (a1 << 16));
+          vop[jp] = (dt & 1) ? (int)__builtin_amdgcn_perm(a1, a0, 0x07060302u)
+                             : (int)__builtin_amdgcn_perm(a1, a0, 0x05040100u);
         }
         acc[dt] = mfma32<PT>(vop, pop, acc[dt]);
         if constexpr (kBf16V) acc[dt] = mfma32<PT>(vop, plo, acc[dt]);
       }
     };
 
-    // Double-buffered walk over the partition's chunks.  The next chunk is
+    // Double-buffered walk over the segment's chunks.  The next chunk is
     // always requested (past the end every lane reads the last row), so no
     // load sits under a branch and each wait covers only the chunk it needs.
     Raw buf0, buf1;
     load_chunk(0, buf0);
     for (int c = 0; c < nchunks; c += 2) {
+      ring.advance();
       load_chunk(c + 1, buf1);
       compute_chunk(c, buf0);
       if (c + 1 >= nchunks) break;
+      ring.advance();
       load_chunk(c + 2, buf0);
       compute_chunk(c + 1, buf1);
     }
@@ -275,17 +311,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     l += shfl_xor(l, 32);
     if (col_ok) {
       float v[4 * W];
-      const bool final = t.nparts == 1;
-      const float f = final ? a.v_scale / l : 1.f;
+      const bool whole = whole_sequence(sl, cs, ce);
+      const float f = whole ? a.v_scale / l : 1.f;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
         for (int dt = 0; dt < W; ++dt) v[W * jj + dt] = acc[dt][jj] * f;
-      if (final) {
-        store_out(a, t.s, head, D, 4 * W * gq, v, 4 * W);
+      if (whole) {
+        store_out(a, s, head, D, 4 * W * gq, v, 4 * W);
       } else {
-        store_partial(a, t.s, head, t.p, D, 4 * W * gq, v, 4 * W);
-        if (gq == 0) store_ml(a, t.s, head, t.p, m, l);
+        const int64_t row = part_row(a, sl.k, s, head);
+        store_partial(a, row, D, 4 * W * gq, v, 4 * W);
+        if (gq == 0) store_ml(a, row, m, l);
       }
     }
   }

@@ -1,10 +1,13 @@
 // Paged decode attention on the vector ALUs, for small query groups.
 //
-// One wavefront handles one (sequence, partition, KV head) item.  A tile is
-// 64 / R positions with R = head_dim / 32 lanes per position: each lane holds
-// 32 elements of one key row and of one value row.  The element set of a lane
-// is chosen so that the R lanes of a row read R adjacent 16-byte pieces per
-// load instruction (each K and V row is read in full, once, by one wave).
+// One wavefront walks one slice of the batch (decode_common.h) for one KV
+// head and all query heads of its group.  A tile is 64 / R positions with
+// R = head_dim / 32 lanes per position: each lane holds 32 elements of one
+// key row and of one value row.  The element set of a lane is chosen so that
+// the R lanes of a row read R adjacent 16-byte pieces per load instruction
+// (each K and V row is read in full, once, by one wave).  A step covers one
+// 32-position chunk (two tiles at head_dim 128, one at head_dim 64); the
+// next chunk's rows are in flight while the current one is computed.
 //
 //   QK:  each lane forms the partial dot product of its 32 elements for each
 //        query head of the group (fp32 FMAs against the pre-scaled query),
@@ -14,19 +17,12 @@
 //        a head moves only when a score exceeds it by more than
 //        kRescaleThreshold.
 //   PV:  each lane accumulates p * v for its own position and elements; at
-//        the end of the partition the 64 / R lanes that hold the same
+//        the end of the segment the 64 / R lanes that hold the same
 //        elements are summed (DPP row rotations, then two cross-row
 //        exchanges).
 #include "decode_common.h"
 
 namespace pa {
-
-template <class CT, int D>
-struct TileRaw {
-  static constexpr int U = 32 * CT::bytes / 16;  // 16-byte loads per lane per row
-  i32x4 k[U];
-  i32x4 v[U];
-};
 
 // the 32 elements a lane holds, converted to fp32; element order: unit u,
 // then position within the 16-byte unit
@@ -54,28 +50,53 @@ __device__ __forceinline__ void widen32<FP8>(const i32x4* raw, float* o) {
     for (int w = 0; w < 4; ++w) fp8x4_to_f32((uint32_t)raw[u][w], o + 16 * u + 4 * w);
 }
 
+// id[i] for a lane-dependent i < N (a select chain, no memory)
+template <int N>
+__device__ __forceinline__ int pick(const int* id, int i) {
+  int x = id[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) x = i == j ? id[j] : x;
+  return x;
+}
+
 template <class CT, class QT, int D, int BS, int G>
 __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   constexpr int e = CT::bytes;
   constexpr int R = D / 32;         // lanes per position
   constexpr int TT = 64 / R;        // positions per tile
+  constexpr int NT = kChunk / TT;   // tiles per chunk
   constexpr int EPU = 16 / e;       // elements per 16-byte unit
-  using Raw = TileRaw<CT, D>;
-  constexpr int U = Raw::U;
+  constexpr int U = 32 * e / 16;    // 16-byte loads per lane per row
   constexpr int64_t kChunkBytes = (int64_t)BS * D * e;
+  constexpr int NB = kChunk / BS;
+  struct Raw {
+    i32x4 k[NT][U];
+    i32x4 v[NT][U];
+  };
+
+  __shared__ int cum[kScanMax + 1];
 
   const int lane = threadIdx.x;
   const int row = lane / R;  // position within the tile
   const int c = lane % R;    // element set
   const int Hq = a.Hkv * a.G;
   const int64_t blk_stride = (int64_t)a.Hkv * kChunkBytes;
-  const int total = item_count(a) * a.Hkv;
 
-  for (int flat = blockIdx.x; flat < total; flat += gridDim.x) {
-    const Item t = item_at(a, flat);
-    const int head0 = t.h * G;
+  const int h = blockIdx.x % a.Hkv;
+  const int k = blockIdx.x / a.Hkv;
+  const int head0 = h * G;
 
-    if (t.L == 0) {
+  Slice sl;
+  if (!slice_setup(a, cum, k, sl)) return;
+
+  const uint8_t* kbase = a.k_cache + (int64_t)h * kChunkBytes;
+  const uint8_t* vbase = a.v_cache + (int64_t)h * kChunkBytes;
+
+  for (int s = sl.s_first; s < a.B; ++s) {
+    const int cs = cum[s], ce = cum[s + 1];
+    if (past_slice(sl, cs, ce)) break;
+    const int L = context_len(a, s);
+    if (L == 0) {
       if (row == 0) {
         float z[EPU];
 #pragma unroll
@@ -83,16 +104,19 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < G; ++i)
 #pragma unroll
-          for (int u = 0; u < U; ++u) store_out(a, t.s, head0 + i, D, EPU * (c + R * u), z, EPU);
+          for (int u = 0; u < U; ++u) store_out(a, s, head0 + i, D, EPU * (c + R * u), z, EPU);
       }
       continue;
     }
+    const int tok0 = (max(sl.c0, cs) - cs) * kChunk;
+    const int tok_end = min((min(sl.c1, ce) - cs) * kChunk, L);
+    const int nchunks = (tok_end - tok0 + kChunk - 1) / kChunk;
 
     // query, pre-scaled into the log2 domain
     float qf[G][32];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)t.s * Hq + head0 + i) * D * 2;
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)s * Hq + head0 + i) * D * 2;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -109,22 +133,35 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
       }
     }
 
-    const int ids = load_block_ids(a, t, BS);
-    const uint8_t* kbase = a.k_cache + (int64_t)t.h * kChunkBytes;
-    const uint8_t* vbase = a.v_cache + (int64_t)t.h * kChunkBytes;
-    const int ntiles = (t.tok_end - t.tok0 + TT - 1) / TT;
-    const int64_t last_off = last_row_offset(t, ids, BS, blk_stride, D * e);
+    const int32_t* trow = a.block_tables + (int64_t)s * a.M;
+    const int blk0 = tok0 / BS;
+    IdRing<BS> ring;
+    ring.start(trow + blk0, (tok_end + BS - 1) / BS - blk0);
+    int64_t last_off;
+    {
+      int id = uniform(trow[(tok_end - 1) / BS]);
+      if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
+      last_off = (int64_t)id * blk_stride + (int64_t)((tok_end - 1) % BS) * D * e;
+    }
 
-    auto load_tile = [&](int tile, Raw& raw) {
-      const int tc = TT * tile + row;  // position relative to the partition
-      const int id = __shfl(ids, tc / BS);
-      const bool ok = t.tok0 + tc < t.tok_end;
-      const int64_t off = ok ? (int64_t)id * blk_stride + (tc % BS) * D * e : last_off;
+    auto load_chunk = [&](int ch, Raw& raw) {
+      int id[NB];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int col = 16 * (c + R * u);
-        raw.k[u] = ld16_stream(kbase + off + col);
-        raw.v[u] = ld16_stream(vbase + off + col);
+      for (int i = 0; i < NB; ++i) {
+        const int x = ring.id(ch, i);
+        id[i] = (x < 0 || (int64_t)x >= a.num_blocks) ? 0 : x;
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int tc = TT * t + row;  // position within the chunk
+        const bool ok = tok0 + kChunk * ch + tc < tok_end;
+        const int64_t off = ok ? (int64_t)pick<NB>(id, tc / BS) * blk_stride + (tc % BS) * D * e : last_off;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int col = 16 * (c + R * u);
+          raw.k[t][u] = ld16_stream(kbase + off + col);
+          raw.v[t][u] = ld16_stream(vbase + off + col);
+        }
       }
     };
 
@@ -137,49 +174,54 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
       for (int j = 0; j < 32; ++j) acc[i][j] = 0.f;
     }
 
-    auto compute_tile = [&](int tile, const Raw& raw) {
-      const bool ok = t.tok0 + TT * tile + row < t.tok_end;
-      float kf[32];
-      widen32<CT>(raw.k, kf);
-      float s[G];
+    auto compute_chunk = [&](int ch, const Raw& raw) {
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        float x = 0.f;
+      for (int t = 0; t < NT; ++t) {
+        const bool ok = tok0 + kChunk * ch + TT * t + row < tok_end;
+        float kf[32];
+        widen32<CT>(raw.k[t], kf);
+        float sv[G];
 #pragma unroll
-        for (int j = 0; j < 32; ++j) x = fmaf(qf[i][j], kf[j], x);
-        x += dpp<kQuadXor1>(x);
-        if constexpr (R == 4) x += dpp<kQuadXor2>(x);
-        s[i] = ok ? x : -INFINITY;
-      }
-      float vf[32];
-      widen32<CT>(raw.v, vf);
+        for (int i = 0; i < G; ++i) {
+          float x = 0.f;
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        if (wave_any(s[i] > m[i] + kRescaleThreshold)) {
-          const float mn = fmaxf(m[i], wave_max(s[i]));
-          const float alpha = fast_exp2(m[i] - mn);
-#pragma unroll
-          for (int j = 0; j < 32; ++j) acc[i][j] *= alpha;
-          l[i] *= alpha;
-          m[i] = mn;
+          for (int j = 0; j < 32; ++j) x = fmaf(qf[i][j], kf[j], x);
+          x += dpp<kQuadXor1>(x);
+          if constexpr (R == 4) x += dpp<kQuadXor2>(x);
+          sv[i] = ok ? x : -INFINITY;
         }
-        const float p = fast_exp2(s[i] - m[i]);
-        l[i] += p;
+        float vf[32];
+        widen32<CT>(raw.v[t], vf);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) acc[i][j] = fmaf(p, vf[j], acc[i][j]);
+        for (int i = 0; i < G; ++i) {
+          if (wave_any(sv[i] > m[i] + kRescaleThreshold)) {
+            const float mn = fmaxf(m[i], wave_max(sv[i]));
+            const float alpha = fast_exp2(m[i] - mn);
+#pragma unroll
+            for (int j = 0; j < 32; ++j) acc[i][j] *= alpha;
+            l[i] *= alpha;
+            m[i] = mn;
+          }
+          const float p = fast_exp2(sv[i] - m[i]);
+          l[i] += p;
+#pragma unroll
+          for (int j = 0; j < 32; ++j) acc[i][j] = fmaf(p, vf[j], acc[i][j]);
+        }
       }
     };
 
-    // Double-buffered; the next tile is always requested (past the end every
+    // Double-buffered; the next chunk is always requested (past the end every
     // lane reads the last row), so no load sits under a branch.
     Raw buf0, buf1;
-    load_tile(0, buf0);
-    for (int tile = 0; tile < ntiles; tile += 2) {
-      load_tile(tile + 1, buf1);
-      compute_tile(tile, buf0);
-      if (tile + 1 >= ntiles) break;
-      load_tile(tile + 2, buf0);
-      compute_tile(tile + 1, buf1);
+    load_chunk(0, buf0);
+    for (int ch = 0; ch < nchunks; ch += 2) {
+      ring.advance();
+      load_chunk(ch + 1, buf1);
+      compute_chunk(ch, buf0);
+      if (ch + 1 >= nchunks) break;
+      ring.advance();
+      load_chunk(ch + 2, buf0);
+      compute_chunk(ch + 1, buf1);
     }
 
     // sum over the positions (lanes with the same element set)
@@ -191,25 +233,26 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
       x += shfl_xor(x, 32);
       return x;
     };
-    const bool final = t.nparts == 1;
+    const bool whole = whole_sequence(sl, cs, ce);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const float lt = row_sum(l[i]);
 #pragma unroll
       for (int j = 0; j < 32; ++j) acc[i][j] = row_sum(acc[i][j]);
       if (row == 0) {
-        const float f = final ? a.v_scale / lt : 1.f;
+        const float f = whole ? a.v_scale / lt : 1.f;
+        const int64_t prow = part_row(a, sl.k, s, head0 + i);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float v[EPU];
 #pragma unroll
           for (int j = 0; j < EPU; ++j) v[j] = acc[i][EPU * u + j] * f;
-          if (final)
-            store_out(a, t.s, head0 + i, D, EPU * (c + R * u), v, EPU);
+          if (whole)
+            store_out(a, s, head0 + i, D, EPU * (c + R * u), v, EPU);
           else
-            store_partial(a, t.s, head0 + i, t.p, D, EPU * (c + R * u), v, EPU);
+            store_partial(a, prow, D, EPU * (c + R * u), v, EPU);
         }
-        if (!final && c == 0) store_ml(a, t.s, head0 + i, t.p, m[i], lt);
+        if (!whole && c == 0) store_ml(a, prow, m[i], lt);
       }
     }
   }

@@ -89,7 +89,8 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_gro
                                 int32_t block_size, int32_t max_context_len) {
   if (B <= 0 || num_kv_heads <= 0 || gqa_group <= 0 || max_context_len <= 0) return 0;
   if ((head_dim != 64 && head_dim != 128) || (block_size != 8 && block_size != 16 && block_size != 32)) return 0;
-  return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len).bytes;
+  // one query-head tile per KV head gives the most slices of any kernel choice
+  return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, 1, device_cu_count()).bytes;
 }
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -125,13 +126,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer argument", fn);
   const int full = max_blocks_per_seq * block_size;
   const int plan_ctx = max_context_len > 0 ? max_context_len : full;
-  const DecodePlan plan = plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx);
-  if (plan.bytes > 0) {
-    if (!workspace || workspace_bytes < plan.bytes)
-      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
-  }
+  const DecodePlan plan = plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx, 1, device_cu_count());
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   DecodeRequest r{};
   r.out = out;
   r.q = q;

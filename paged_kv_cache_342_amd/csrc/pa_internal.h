@@ -13,12 +13,16 @@ namespace pa {
 void set_error(const char* fmt, ...);
 
 struct DecodePlan {
-  int part_tokens;    // positions per split-K partition
-  int nparts;         // partitions per sequence the workspace holds
-  size_t work_off, ml_off, acc_off, bytes;  // workspace layout
+  int nslices;    // slices per (KV head, head tile): one wave each
+  int min_slice;  // fewest chunks per slice
+  int sub_batch;  // sequences per launch
+  size_t meta_off, ml_off, acc_off, bytes;  // workspace layout
 };
 
-DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx);
+// compute units of the current device (cached per device)
+int device_cu_count();
+
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu);
 
 struct DecodeRequest {
   void* out;

@@ -73,8 +73,14 @@ def test_decode_workspace_checks():
     assert _decode(B=64, Hkv=8, G=4, mcl=4096, M=256, ws=FAKE, wsb=need - 1) == pa.ERR_WORKSPACE
     assert _decode(B=64, Hkv=8, G=4, mcl=4096, M=256, ws=None, wsb=need) == pa.ERR_WORKSPACE
     assert _decode(B=64, Hkv=8, G=4, mcl=4096, M=256, ws=FAKE + 16, wsb=need) == pa.ERR_INVALID_ARG
-    # contexts that fit one partition need no workspace at all
-    assert pa.decode_workspace_size(2, 4, 1, 64, 16, 64) == 0
+    # every call needs the workspace (it carries the chunk prefix sum), and its
+    # size grows with the batch and with the query heads
+    small = pa.decode_workspace_size(2, 4, 1, 64, 16, 64)
+    assert small > 0
+    assert _decode(B=2, Hkv=4, G=1, D=64, mcl=64, M=4, ws=None, wsb=0) == pa.ERR_WORKSPACE
+    assert pa.decode_workspace_size(4, 4, 1, 64, 16, 64) > small
+    assert pa.decode_workspace_size(2, 4, 2, 64, 16, 64) > small
+    # sizes that describe no work give 0
     assert pa.decode_workspace_size(0, 4, 1, 64, 16, 100) == 0
 
 

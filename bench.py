@@ -27,6 +27,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "pa_decode KV GB/s (fraction of HBM peak) + seq·heads/s on 1 MI355X"
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "paged_kv_cache_342_amd", "csrc")
+# sources of the kernels a pa_decode call runs; profiler traffic recorded for
+# other sources is stale and is not reported
+DECODE_SOURCES = ("pa_device.h", "decode_common.h", "decode_core.hip", "decode_mfma.hip", "decode_valu.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 
 def log(msg):
@@ -74,6 +79,31 @@ def cpu_baseline(w, budget_s: float):
         "sample": f"{done_seqs} whole sequences of the same batch ({kv} KV bytes) in {t_total:.1f} s of "
                   f"fp64 NumPy gather + attention; seq*heads/s = {done_seqs * w.Hq / t_total:.1f}; cpu: {cpu}",
     }
+
+
+def decode_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per pa_decode call (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy
+    of known size) from the committed rocprofv3 record, if it was taken on the
+    current kernel sources; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    r = rec.get("workloads", {}).get(workload)
+    if not r or rec.get("decode_source_sha256_16") != decode_source_hash():
+        return None
+    return r.get("hbm_bytes_per_call")
 
 
 def _identity_layout(w, batch, slots_new):
@@ -228,8 +258,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "kernel": "pa_decode (work-list + partition + reduce kernels, one call)",
+            "traffic": None if args.identity_tables else recorded_traffic(w.name),
+            "kernel": "pa_decode call: decode kernel (balanced slices) + merge kernel",
         },
         "cpu_baseline": cpu,
     }

@@ -73,7 +73,7 @@ def test_decode_workspace_checks():
     assert _decode(B=64, Hkv=8, G=4, mcl=4096, M=256, ws=FAKE, wsb=need - 1) == pa.ERR_WORKSPACE
     assert _decode(B=64, Hkv=8, G=4, mcl=4096, M=256, ws=None, wsb=need) == pa.ERR_WORKSPACE
     assert _decode(B=64, Hkv=8, G=4, mcl=4096, M=256, ws=FAKE + 16, wsb=need) == pa.ERR_INVALID_ARG
-    # every call needs the workspace (it carries the chunk prefix sum), and its
+    # every call needs the workspace (chunk prefix sum + partials), and its
     # size grows with the batch and with the query heads
     small = pa.decode_workspace_size(2, 4, 1, 64, 16, 64)
     assert small > 0

@@ -16,16 +16,18 @@ bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int b
                         dim3 grid, hipStream_t stream);
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
 
-// One wave per (KV head, sequence): merge the slices' partials of each query
-// head of the group, in slice order, with an online rescale:
+// One workgroup per (KV head, sequence): merge the slices' partials of every
+// query head of the group, in slice order, with an online rescale:
 //   M = max_k m_k;  out = v_scale * sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
-// Lane j handles four consecutive outputs of one query head; 64 / (D / 4)
-// heads are merged side by side.  Sequences that are whole in one slice were
-// written by the decode kernel and are skipped here.
+// Thread j handles four consecutive outputs of one query head, so all heads
+// of the group are merged at once, and the loads of up to kMergeUnroll
+// pieces are issued before any of them is used.  Sequences that are whole in
+// one slice were written by the decode kernel and are skipped here.
+constexpr int kMergeUnroll = 8;
+
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int LPH = D / 4;    // lanes per head
-  constexpr int HPP = 64 / LPH; // heads per pass
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int LPH = D / 4;  // threads per head
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int S = a.meta[0];
@@ -36,28 +38,24 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int kl = min((ce - 1) / S, neff - 1);
   if (kl <= kf) return;
   const int np = kl - kf + 1;
-  const int lane = threadIdx.x;
-  const int sub = lane / LPH;
-  const int d = 4 * (lane % LPH);
-  for (int i0 = 0; i0 < a.G; i0 += HPP) {
-    const int i = i0 + sub;
-    const bool act = i < a.G;
-    const int head = h * a.G + (act ? i : 0);
+  for (int idx = threadIdx.x; idx < a.G * LPH; idx += blockDim.x) {
+    const int i = idx / LPH;
+    const int d = 4 * (idx - i * LPH);
+    const int head = h * a.G + i;
     float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    constexpr int UNR = 4;
-    for (int p0 = 0; p0 < np; p0 += UNR) {
-      f32x2 ml[UNR];
-      f32x4 x[UNR];
+    for (int p0 = 0; p0 < np; p0 += kMergeUnroll) {
+      f32x2 ml[kMergeUnroll];
+      f32x4 x[kMergeUnroll];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
+      for (int u = 0; u < kMergeUnroll; ++u) {
         const int p = min(p0 + u, np - 1);
         const int64_t row = part_row(a, kf + p, s, head);
         ml[u] = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * row);
         x[u] = *reinterpret_cast<const f32x4*>(a.part_acc + row * D + d);
       }
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
+      for (int u = 0; u < kMergeUnroll; ++u) {
         if (p0 + u < np) {
           const float Mn = fmaxf(M, ml[u][0]);
           const float ca = fast_exp2(M - Mn);
@@ -68,11 +66,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
         }
       }
     }
-    if (act) {
-      const float f = a.v_scale / den;
-      const float v[4] = {num[0] * f, num[1] * f, num[2] * f, num[3] * f};
-      store_out(a, s, head, D, d, v, 4);
-    }
+    const float f = a.v_scale / den;
+    const float v[4] = {num[0] * f, num[1] * f, num[2] * f, num[3] * f};
+    store_out(a, s, head, D, d, v, 4);
   }
 }
 
@@ -189,10 +185,12 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     }
     if (plan.nslices > 1) {
       const dim3 mgrid(r.Hkv, a.B);
+      const int threads = r.G * (r.D / 4);
+      const dim3 mblock(threads >= 256 ? 256 : ((threads + 63) / 64) * 64);
       if (r.D == 64)
-        hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, mblock, 0, stream, a);
       else
-        hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, mblock, 0, stream, a);
     }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {

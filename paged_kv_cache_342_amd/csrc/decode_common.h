@@ -146,17 +146,19 @@ __device__ __forceinline__ bool whole_sequence(const Slice& sl, int cs, int ce) 
 // j of the segment (counted from its first block) sits in lane j % 64.  The
 // ring holds the blocks of the next kIdAhead + 1 chunks; each step requests
 // one more chunk's ids (an unconditional load whose lanes that do not take
-// part re-read a valid entry), and that load is merged one step later, so no
-// wait ever falls on a table read that was just issued.
+// part re-read a valid entry), and a request is merged two steps after it
+// was issued, so a merge never waits on a table read newer than the chunk
+// loads it is followed by.
 template <int BS>
 struct IdRing {
   static constexpr int NB = kChunk / BS;  // blocks per chunk
-  static_assert((kIdAhead + 2) * NB <= 64, "ring too small for the lookahead");
+  static_assert((kIdAhead + 3) * NB <= 64, "ring too small for the lookahead");
   const int32_t* row;  // block table row of the sequence, from the segment's first block
   int nblk;            // blocks in the segment
   int ids;             // the ring
-  int pending;         // ids of chunk `next`, not merged yet
-  int next;            // chunk whose ids are pending
+  int pending0;        // ids of chunk `next`, not merged yet
+  int pending1;        // ids of chunk `next + 1`
+  int next;
 
   __device__ __forceinline__ int fetch(int chunk) const {
     const int lane = __lane_id();
@@ -170,15 +172,17 @@ struct IdRing {
     const int lane = __lane_id();
     ids = row[lane < nblk ? lane : nblk - 1];  // chunks 0 .. 64/NB - 1
     next = kIdAhead + 1;
-    pending = fetch(next);
+    pending0 = fetch(next);
+    pending1 = fetch(next + 1);
   }
-  // merge the pending chunk's ids, then request the one after it
+  // merge the oldest pending chunk's ids, then request one more
   __device__ __forceinline__ void advance() {
     const int lane = __lane_id();
     const int slot0 = (next * NB) & 63;
-    if (((lane - slot0) & 63) < NB) ids = pending;
+    if (((lane - slot0) & 63) < NB) ids = pending0;
+    pending0 = pending1;
+    pending1 = fetch(next + 2);
     ++next;
-    pending = fetch(next);
   }
   // id of block i (< NB) of chunk c; valid for chunks within the lookahead
   __device__ __forceinline__ int id(int c, int i) const {

@@ -291,19 +291,41 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       }
     };
 
-    // Double-buffered walk over the segment's chunks.  The next chunk is
-    // always requested (past the end every lane reads the last row), so no
-    // load sits under a branch and each wait covers only the chunk it needs.
-    Raw buf0, buf1;
-    load_chunk(0, buf0);
-    for (int c = 0; c < nchunks; c += 2) {
+    // Walk over the segment's chunks with the next chunk (two chunks for fp8
+    // caches, whose chunk is half the bytes) in flight while one is computed,
+    // so a wave keeps ~16 KiB requested.  Later chunks are always requested
+    // (past the end every lane reads the last row), so no load sits under a
+    // branch and each wait covers only the chunk it needs.
+    if constexpr (!kFp8) {
+      Raw buf0, buf1;
+      load_chunk(0, buf0);
+      for (int c = 0; c < nchunks; c += 2) {
+        ring.advance();
+        load_chunk(c + 1, buf1);
+        compute_chunk(c, buf0);
+        if (c + 1 >= nchunks) break;
+        ring.advance();
+        load_chunk(c + 2, buf0);
+        compute_chunk(c + 1, buf1);
+      }
+    } else {
+      Raw buf0, buf1, buf2;
+      load_chunk(0, buf0);
       ring.advance();
-      load_chunk(c + 1, buf1);
-      compute_chunk(c, buf0);
-      if (c + 1 >= nchunks) break;
-      ring.advance();
-      load_chunk(c + 2, buf0);
-      compute_chunk(c + 1, buf1);
+      load_chunk(1, buf1);
+      for (int c = 0; c < nchunks; c += 3) {
+        ring.advance();
+        load_chunk(c + 2, buf2);
+        compute_chunk(c, buf0);
+        if (c + 1 >= nchunks) break;
+        ring.advance();
+        load_chunk(c + 3, buf0);
+        compute_chunk(c + 1, buf1);
+        if (c + 2 >= nchunks) break;
+        ring.advance();
+        load_chunk(c + 4, buf1);
+        compute_chunk(c + 2, buf2);
+      }
     }
 
     // ---- epilogue: the lane holds head col_head, d = 4W*gq + W*jj + dt

@@ -6,6 +6,7 @@ and within max-abs 3e-2 for fp8 caches.  Every pool is poisoned with NaN
 before it is filled, so a read of an unwritten slot fails the comparison.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -356,3 +357,50 @@ def test_workspace_needs_no_initialisation_and_is_reusable():
         for _ in range(3):
             out = g.decode(workspace=ws)
             assert torch.equal(out, fresh)
+
+
+# ------------------------------------------------------------------ how the batch is split
+
+@pytest.mark.parametrize("waves_per_cu", ["1", "2", "8", "32"])
+def test_decode_parity_for_other_slice_counts(waves_per_cu):
+    """The split of the chunk line over waves is free (one to 32 waves per CU):
+    every split must stay within tolerance of the oracle."""
+    os.environ["PA_DECODE_WAVES_PER_CU"] = waves_per_cu
+    try:
+        for make in (lambda: W.llama8b(B=6), lambda: W.heavy_tail(bs=8, B=24), lambda: W.tiny()):
+            _check_decode(make(), label=f"[waves/CU={waves_per_cu}]")
+    finally:
+        os.environ.pop("PA_DECODE_WAVES_PER_CU", None)
+
+
+def test_decode_batch_split_into_launches_by_a_large_length_bound():
+    """A huge host-side max_context_len bound shrinks the sequences one launch
+    scans (its chunk prefix sum must fit 32 bits), so 150 sequences run as
+    several consecutive launches sharing one workspace."""
+    lens = [int(x) for x in np.random.default_rng(11).integers(1, 700, size=150)]
+    w = W.custom("sub_batches", 12, lens, 8, 2, 128, 16, "bf16")
+    g = GpuBatch(w)
+    bound = 1 << 30
+    out = pa.decode(g.q, g.kc, g.vc, g.tables, g.lens, w.scale, max_context_len=bound,
+                    out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    kc, vc = OH.build_pools(w)
+    ref = OH.decode(w, kc, vc)
+    ma, rel = errors(out, ref)
+    log(f"[sub-batches] max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= 2e-3 and rel <= 1e-3
+
+
+def test_decode_more_sequences_than_one_launch_scans():
+    """4,100 sequences (more than the 4,096 one launch scans in LDS), checked on
+    a sample that includes both sides of the launch boundary."""
+    lens = [int(x) for x in np.random.default_rng(12).integers(0, 60, size=4100)]
+    w = W.custom("many_seqs", 13, lens, 2, 1, 64, 16, "f16")
+    g = GpuBatch(w)
+    out = g.decode().cpu().numpy().astype(np.float64)
+    seqs = [0, 1, 2, 4094, 4095, 4096, 4097, 4099] + [int(i) for i in np.nonzero(np.array(lens) == 0)[0][:3]]
+    kc, vc = OH.build_pools(w, seqs=seqs)
+    ref = OH.decode(w, kc, vc, seqs=seqs)
+    ma, rel = errors(out[seqs], ref)
+    log(f"[4100 sequences] max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert np.isfinite(out).all()
+    assert ma <= 2e-3 and rel <= 1e-3

@@ -20,6 +20,12 @@
 // unique: the slices that cut s and those that cut s + 1 overlap in at most
 // one slice.
 //
+// Each sequence also costs a wave a fixed amount beyond its chunks (the first
+// chunk's latency, which nothing overlaps, a partly filled last chunk, the
+// epilogue), so the line charges every non-empty sequence `seg_cost` virtual
+// chunks in front of its data: a slice that holds many short sequences holds
+// fewer chunks.
+//
 // Each wave computes the prefix sum of chunk counts itself (the lengths are
 // read once into LDS), so no separate planning kernel runs before it.
 #pragma once
@@ -47,6 +53,7 @@ struct DecodeArgs {
   int32_t max_ctx;             // lengths are clamped to [0, max_ctx]
   int32_t nslices;             // slices per (KV head, head tile) in the grid
   int32_t min_slice;           // fewest chunks per slice
+  int32_t seg_cost;            // virtual chunks charged per non-empty sequence
   int32_t head_tiles;          // query-head tiles of 16 per KV head (MFMA kernel), 1 otherwise
   int32_t out_dtype;           // 0 f32, 1 f16, 2 bf16
   float qk_scale_log2;         // scale * k_scale * log2(e)
@@ -72,7 +79,8 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 }
 
 // This wave's slice [c0, c1) of the chunk line, and the first sequence it
-// visits.  cum[s] (LDS) = first chunk of sequence s, cum[B] = C.
+// visits.  cum[s] (LDS) = where sequence s starts on the line (its charge,
+// then its chunks), cum[B] = C.
 struct Slice {
   int k;        // slice index
   int S;        // chunks per slice
@@ -82,9 +90,10 @@ struct Slice {
   int s_first;  // first sequence it visits
 };
 
-// Fills cum[] and sl; returns false when the slice holds nothing.  Wave 0
-// also publishes S, the slice count and cum[] for the merge kernel.
-__device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int k, Slice& sl) {
+// Fills cum[], lens[] (clamped context lengths) and sl; returns false when
+// the slice holds nothing.  Wave 0 also publishes S, the slice count and
+// cum[] for the merge kernel.
+__device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int* lens, int k, Slice& sl) {
   const int lane = __lane_id();
   int carry = 0;
   for (int base = 0; base < a.B; base += 64) {
@@ -93,7 +102,8 @@ __device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int k
     if (s < a.B) {
       int L = a.context_lens[s];
       L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
-      n = (L + kChunk - 1) / kChunk;
+      lens[s] = L;
+      n = L > 0 ? (L + kChunk - 1) / kChunk + a.seg_cost : 0;
     }
     const int inc = wave_inclusive_sum(n);
     if (s < a.B) cum[s + 1] = carry + inc;
@@ -135,6 +145,41 @@ __device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int k
 // sequence at c1 belongs to the next slice, except at the very end.
 __device__ __forceinline__ bool past_slice(const Slice& sl, int cs, int ce) {
   return cs > sl.c1 || (cs == sl.c1 && (ce > cs || !sl.last));
+}
+
+// The piece of one sequence a slice covers (wave-uniform values); s == -1
+// means none.
+struct Segment {
+  int s;
+  int cs, ce;        // the range of the sequence's chunks on the line (after its charge)
+  int tok0, tok_end; // positions of the piece
+  int nchunks;
+};
+
+// First sequence at or after s_from that is not empty and has chunks in the slice.
+__device__ __forceinline__ Segment next_segment(const Slice& sl, const int* cum, const int* lens, int B,
+                                                int s_from) {
+  Segment g;
+  g.s = -1;
+  g.cs = g.ce = g.tok0 = g.tok_end = g.nchunks = 0;
+  for (int s = s_from; s < B; ++s) {
+    const int L = lens[s];
+    const int ce = cum[s + 1];
+    if (L == 0) {
+      if (past_slice(sl, cum[s], ce)) break;
+      continue;
+    }
+    const int cs = ce - (L + kChunk - 1) / kChunk;  // the charge lies before cs
+    if (cs >= sl.c1) break;
+    g.s = uniform(s);
+    g.cs = uniform(cs);
+    g.ce = uniform(ce);
+    g.tok0 = (max(sl.c0, cs) - cs) * kChunk;
+    g.tok_end = min((min(sl.c1, ce) - cs) * kChunk, L);
+    g.nchunks = (g.tok_end - g.tok0 + kChunk - 1) / kChunk;
+    break;
+  }
+  return g;
 }
 
 // Pieces sequence s is cut into, and whether this slice's piece is the whole.

@@ -32,8 +32,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int s = blockIdx.y;
   const int S = a.meta[0];
   const int neff = a.meta[1];
-  const int cs = a.meta[2 + s], ce = a.meta[3 + s];
-  if (ce <= cs) return;
+  const int ce = a.meta[3 + s];
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+  if (L == 0) return;
+  const int cs = ce - (L + kChunk - 1) / kChunk;  // the sequence's chunks, after its charge
   const int kf = cs / S;
   const int kl = min((ce - 1) / S, neff - 1);
   if (kl <= kf) return;
@@ -87,6 +90,13 @@ int device_cu_count() {
   return n;
 }
 
+// virtual chunks a sequence is charged on the line for its fixed costs
+static int segment_cost() {
+  const char* v = std::getenv("PA_DECODE_SEGMENT_COST");
+  const int n = v ? std::atoi(v) : -1;
+  return n >= 0 && n <= 64 ? n : 2;
+}
+
 static int waves_per_cu() {
   const char* v = std::getenv("PA_DECODE_WAVES_PER_CU");
   const int n = v ? std::atoi(v) : 0;
@@ -100,7 +110,8 @@ DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int he
   const int64_t per = (int64_t)Hkv * head_tiles;
   p.nslices = (int)std::max<int64_t>(1, (waves + per - 1) / per);
   p.min_slice = 4;
-  const int64_t chunks = std::max<int64_t>(1, ((int64_t)std::max(max_ctx, 1) + kChunk - 1) / kChunk);
+  p.seg_cost = segment_cost();
+  const int64_t chunks = ((int64_t)std::max(max_ctx, 1) + kChunk - 1) / kChunk + p.seg_cost;
   int64_t sub = std::min<int64_t>(kScanMax, INT_MAX / chunks);
   p.sub_batch = (int)std::max<int64_t>(1, std::min<int64_t>(sub, std::max(B, 1)));
   const size_t Hq = (size_t)Hkv * G;
@@ -159,6 +170,7 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   a.max_ctx = r.max_ctx;
   a.nslices = plan.nslices;
   a.min_slice = plan.min_slice;
+  a.seg_cost = plan.seg_cost;
   a.head_tiles = tiles;
   a.out_dtype = r.out_dtype == PA_F32 ? 0 : (r.out_dtype == PA_F16 ? 1 : 2);
   const bool fp8 = r.cache_dtype == PA_FP8_E4M3;

@@ -91,6 +91,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NB = kChunk / BS;
 
   __shared__ int cum[kScanMax + 1];
+  __shared__ int lens[kScanMax];
 
   const int lane = threadIdx.x;
   const int r = lane & 15;   // A-operand row / B-operand column / C column
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const int k = rest / a.head_tiles;
 
   Slice sl;
-  if (!slice_setup(a, cum, k, sl)) return;
+  if (!slice_setup(a, cum, lens, k, sl)) return;
 
   const int col_head = 16 * ht + r;  // head within the group this lane's column carries
   const bool col_ok = col_head < a.G;
@@ -114,48 +115,61 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const uint8_t* kbase = a.k_cache + (int64_t)h * kChunkBytes;
   const uint8_t* vbase = a.v_cache + (int64_t)h * kChunkBytes;
 
+  // empty contexts in this slice: zero rows, written by the slice that owns them
   for (int s = sl.s_first; s < a.B; ++s) {
     const int cs = cum[s], ce = cum[s + 1];
     if (past_slice(sl, cs, ce)) break;
-    const int L = context_len(a, s);
-    if (L == 0) {  // empty context: zeros, written by the slice that owns it
-      if (col_ok) {
-        float z[4 * W];
+    if (lens[s] == 0 && col_ok) {
+      float z[4 * W];
 #pragma unroll
-        for (int i = 0; i < 4 * W; ++i) z[i] = 0.f;
-        store_out(a, s, head, D, 4 * W * gq, z, 4 * W);
-      }
-      continue;
+      for (int i = 0; i < 4 * W; ++i) z[i] = 0.f;
+      store_out(a, s, head, D, 4 * W * gq, z, 4 * W);
     }
-    // this slice's segment of sequence s: positions [tok0, tok_end)
-    const int tok0 = (max(sl.c0, cs) - cs) * kChunk;
-    const int tok_end = min((min(sl.c1, ce) - cs) * kChunk, L);
-    const int nchunks = (tok_end - tok0 + kChunk - 1) / kChunk;
+  }
 
-    // ---- Q as the B operand of QK, in the k-slot order the K loads use
+  // What a segment needs before its first chunk: the query (B operand of QK,
+  // in the k-slot order the K loads use), its block-id ring and the offset of
+  // its last row (read by lanes whose position lies past the end).  Each
+  // segment's header is requested one segment ahead, with loads that do not
+  // depend on whether there is a next segment (past the last one the current
+  // segment's header is read again), so segment changes cost no table or
+  // query round trips.
+  struct Header {
     i32x4 qop[KK];
-    {
-      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                            ((int64_t)s * Hq + (col_ok ? head : h * a.G)) * D * 2;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int d = kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
-        const i32x4 x = ld16(qrow + d * 2);
-        qop[kk] = col_ok ? x : i32x4{0, 0, 0, 0};
-      }
-    }
-
-    const int32_t* trow = a.block_tables + (int64_t)s * a.M;
-    const int blk0 = tok0 / BS;
     IdRing<BS> ring;
-    ring.start(trow + blk0, (tok_end + BS - 1) / BS - blk0);
-    // the segment's last row, read by lanes whose position lies past the end
     int64_t last_off;
-    {
-      int id = uniform(trow[(tok_end - 1) / BS]);
-      if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
-      last_off = (int64_t)id * blk_stride + (int64_t)((tok_end - 1) % BS) * D * e;
+  };
+  auto load_header = [&](const Segment& g, Header& hd) {
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
+                          ((int64_t)g.s * Hq + (col_ok ? head : h * a.G)) * D * 2;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int d = kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
+      const i32x4 x = ld16(qrow + d * 2);
+      hd.qop[kk] = col_ok ? x : i32x4{0, 0, 0, 0};
     }
+    const int32_t* trow = a.block_tables + (int64_t)g.s * a.M;
+    const int blk0 = g.tok0 / BS;
+    hd.ring.start(trow + blk0, (g.tok_end + BS - 1) / BS - blk0);
+    int id = uniform(trow[(g.tok_end - 1) / BS]);
+    if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
+    hd.last_off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * D * e;
+  };
+
+  Segment cur = next_segment(sl, cum, lens, a.B, sl.s_first);
+  if (cur.s < 0) return;
+  Header hc, hn;
+  load_header(cur, hc);
+  Segment nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
+  load_header(nxt.s >= 0 ? nxt : cur, hn);
+
+  while (true) {
+    const int s = cur.s;
+    const int cs = cur.cs, ce = cur.ce;
+    const int tok0 = cur.tok0, tok_end = cur.tok_end, nchunks = cur.nchunks;
+    const i32x4* qop = hc.qop;
+    IdRing<BS>& ring = hc.ring;
+    const int64_t last_off = hc.last_off;
 
     auto load_chunk = [&](int c, Raw& raw) {
       const int ctok = tok0 + kChunk * c;  // first position of the chunk
@@ -347,6 +361,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         if (gq == 0) store_ml(a, row, m, l);
       }
     }
+
+    if (nxt.s < 0) break;
+    cur = nxt;
+    hc = hn;
+    nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
+    load_header(nxt.s >= 0 ? nxt : cur, hn);
   }
 }
 

@@ -75,6 +75,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   };
 
   __shared__ int cum[kScanMax + 1];
+  __shared__ int lens[kScanMax];
 
   const int lane = threadIdx.x;
   const int row = lane / R;  // position within the tile
@@ -87,62 +88,82 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   const int head0 = h * G;
 
   Slice sl;
-  if (!slice_setup(a, cum, k, sl)) return;
+  if (!slice_setup(a, cum, lens, k, sl)) return;
 
   const uint8_t* kbase = a.k_cache + (int64_t)h * kChunkBytes;
   const uint8_t* vbase = a.v_cache + (int64_t)h * kChunkBytes;
 
+  // empty contexts in this slice: zero rows, written by the slice that owns them
   for (int s = sl.s_first; s < a.B; ++s) {
     const int cs = cum[s], ce = cum[s + 1];
     if (past_slice(sl, cs, ce)) break;
-    const int L = context_len(a, s);
-    if (L == 0) {
-      if (row == 0) {
-        float z[EPU];
+    if (lens[s] == 0 && row == 0) {
+      float z[EPU];
 #pragma unroll
-        for (int i = 0; i < EPU; ++i) z[i] = 0.f;
+      for (int i = 0; i < EPU; ++i) z[i] = 0.f;
 #pragma unroll
-        for (int i = 0; i < G; ++i)
+      for (int i = 0; i < G; ++i)
 #pragma unroll
-          for (int u = 0; u < U; ++u) store_out(a, s, head0 + i, D, EPU * (c + R * u), z, EPU);
-      }
-      continue;
+        for (int u = 0; u < U; ++u) store_out(a, s, head0 + i, D, EPU * (c + R * u), z, EPU);
     }
-    const int tok0 = (max(sl.c0, cs) - cs) * kChunk;
-    const int tok_end = min((min(sl.c1, ce) - cs) * kChunk, L);
-    const int nchunks = (tok_end - tok0 + kChunk - 1) / kChunk;
+  }
 
-    // query, pre-scaled into the log2 domain
-    float qf[G][32];
+  // What a segment needs before its first chunk: the group's query rows (as
+  // loaded), its block-id ring and the offset of its last row.  Each header
+  // is requested one segment ahead with loads that do not depend on whether
+  // there is a next segment (past the last one the current header is read
+  // again), so segment changes cost no table or query round trips.
+  struct Header {
+    i32x4 q[G][U][EPU / 8];
+    IdRing<BS> ring;
+    int64_t last_off;
+  };
+  auto load_header = [&](const Segment& g, Header& hd) {
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)s * Hq + head0 + i) * D * 2;
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + ((int64_t)g.s * Hq + head0 + i) * D * 2;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int half = 0; half < EPU / 8; ++half) {
-          const i32x4 x = ld16(qrow + (EPU * (c + R * u) + 8 * half) * 2);
+        for (int half = 0; half < EPU / 8; ++half) hd.q[i][u][half] = ld16(qrow + (EPU * (c + R * u) + 8 * half) * 2);
+    }
+    const int32_t* trow = a.block_tables + (int64_t)g.s * a.M;
+    const int blk0 = g.tok0 / BS;
+    hd.ring.start(trow + blk0, (g.tok_end + BS - 1) / BS - blk0);
+    int id = uniform(trow[(g.tok_end - 1) / BS]);
+    if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
+    hd.last_off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * D * e;
+  };
+
+  Segment cur = next_segment(sl, cum, lens, a.B, sl.s_first);
+  if (cur.s < 0) return;
+  Header hc, hn;
+  load_header(cur, hc);
+  Segment nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
+  load_header(nxt.s >= 0 ? nxt : cur, hn);
+
+  while (true) {
+    const int s = cur.s;
+    const int cs = cur.cs, ce = cur.ce;
+    const int tok0 = cur.tok0, tok_end = cur.tok_end, nchunks = cur.nchunks;
+    IdRing<BS>& ring = hc.ring;
+    const int64_t last_off = hc.last_off;
+
+    // query, widened and pre-scaled into the log2 domain
+    float qf[G][32];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int half = 0; half < EPU / 8; ++half)
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             float lo, hi;
-            unpack2<QT>((uint32_t)x[w], lo, hi);
+            unpack2<QT>((uint32_t)hc.q[i][u][half][w], lo, hi);
             qf[i][EPU * u + 8 * half + 2 * w] = lo * a.qk_scale_log2;
             qf[i][EPU * u + 8 * half + 2 * w + 1] = hi * a.qk_scale_log2;
           }
-        }
-      }
-    }
-
-    const int32_t* trow = a.block_tables + (int64_t)s * a.M;
-    const int blk0 = tok0 / BS;
-    IdRing<BS> ring;
-    ring.start(trow + blk0, (tok_end + BS - 1) / BS - blk0);
-    int64_t last_off;
-    {
-      int id = uniform(trow[(tok_end - 1) / BS]);
-      if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
-      last_off = (int64_t)id * blk_stride + (int64_t)((tok_end - 1) % BS) * D * e;
-    }
 
     auto load_chunk = [&](int ch, Raw& raw) {
       int id[NB];
@@ -276,6 +297,12 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
         if (!whole && c == 0) store_ml(a, prow, m[i], lt);
       }
     }
+
+    if (nxt.s < 0) break;
+    cur = nxt;
+    hc = hn;
+    nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
+    load_header(nxt.s >= 0 ? nxt : cur, hn);
   }
 }
 

@@ -15,6 +15,7 @@ void set_error(const char* fmt, ...);
 struct DecodePlan {
   int nslices;    // slices per (KV head, head tile): one wave each
   int min_slice;  // fewest chunks per slice
+  int seg_cost;   // virtual chunks charged per non-empty sequence
   int sub_batch;  // sequences per launch
   size_t meta_off, ml_off, acc_off, bytes;  // workspace layout
 };

@@ -79,7 +79,8 @@ typedef enum {
   PA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misaligned pointer */
   PA_ERR_UNSUPPORTED = -2, /* valid but not built: dtype combination, head_dim, block size */
   PA_ERR_WORKSPACE = -3,   /* workspace smaller than pa_decode_workspace_size() */
-  PA_ERR_HIP = -4          /* the HIP runtime refused a launch */
+  PA_ERR_HIP = -4,         /* the HIP runtime refused a launch */
+  PA_ERR_NO_BLOCKS = -5    /* block manager: the pool has too few free blocks */
 } pa_status;
 
 /*
@@ -155,6 +156,79 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapping, int32_t N,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                          int64_t num_blocks, pa_dtype cache_dtype, pa_stream_t stream);
+
+/*
+ * Host block manager: the memory-management side of the paged cache.
+ *   "Paged Attention and Memory Efficiency ...", section "How PagedAttention
+ *   borrows OS paging ..." (block tables resolved at run time, blocks
+ *   allocated on demand, waste only in the tail of the last block, shared
+ *   prefixes, copy-on-write); "PagedAttention in Production", section "Core
+ *   Principle" (blocks allocated on demand and returned to the pool when a
+ *   request finishes); "PagedAttention - The KV Cache Problem", sections "How
+ *   It Works" and "Why This Matters for Production" (copy-on-write for
+ *   parallel sampling and beam search).
+ * A fixed pool of num_blocks physical blocks of block_size tokens.  Each
+ * sequence (any int64 id) has a block table that grows as tokens are
+ * appended; forking shares all of a sequence's blocks (reference counts);
+ * appending into a shared, partially filled last block first moves the
+ * sequence onto a copy of it, reported as a (src, dst) pair that the caller
+ * copies with pa_copy_blocks before writing the new rows; freeing a sequence
+ * returns the blocks no other sequence references.  Free blocks are handed
+ * out last-freed-first (a fresh pool hands out 0, 1, 2, ...).  Every call is
+ * host-only, synchronous and not thread-safe; the manager owns its host
+ * memory.  A call that fails changes nothing.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+typedef struct {
+  int64_t blocks_in_use;  /* physical blocks referenced by some table */
+  int64_t blocks_free;
+  int64_t shared_blocks;  /* blocks referenced by more than one table */
+  int64_t slots_held;     /* sum over sequences of table length * block_size */
+  int64_t tokens;         /* sum over sequences of their length */
+  int64_t sequences;
+} pa_bm_stats;
+
+/* NULL on bad sizes (num_blocks outside [0, 2^31), block_size < 1) or no memory. */
+pa_block_manager* pa_bm_create(int64_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager* bm);
+/* new empty sequence; PA_ERR_INVALID_ARG if the id exists */
+pa_status pa_bm_add(pa_block_manager* bm, int64_t seq);
+/* child shares every block of parent (and its length) */
+pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+/*
+ * Reserve n >= 0 token slots at the end of seq: slots[0..n) receive the slot
+ * ids (block * block_size + row).  *copied is 1 when a copy-on-write was
+ * needed, with copy_pair[0..2) = (src, dst); else 0.  PA_ERR_NO_BLOCKS when
+ * the pool cannot supply every block the append needs.
+ */
+pa_status pa_bm_append(pa_block_manager* bm, int64_t seq, int32_t n, int64_t* slots, int64_t* copy_pair,
+                       int32_t* copied);
+/*
+ * Append n_tokens[i] tokens to seqs[i] for i < count, in order (each id at
+ * most once): slots get the sum of n_tokens slot ids, sequence after
+ * sequence; copy_pairs[0 .. 2 * *n_pairs) the copy-on-write pairs (at most one
+ * per sequence, so room for 2 * count).  All or nothing: the blocks needed,
+ * counted before any of the batch is applied, must be free, or the call
+ * returns PA_ERR_NO_BLOCKS and changes nothing.
+ */
+pa_status pa_bm_append_batch(pa_block_manager* bm, const int64_t* seqs, int32_t count, const int32_t* n_tokens,
+                             int64_t* slots, int64_t* copy_pairs, int32_t* n_pairs);
+/* return seq's blocks to the pool (those no other sequence references) */
+pa_status pa_bm_free(pa_block_manager* bm, int64_t seq);
+/* number of blocks of seq (-1 if unknown); writes min(that, capacity) ids to table if non-NULL */
+int32_t pa_bm_table(const pa_block_manager* bm, int64_t seq, int32_t* table, int32_t capacity);
+/*
+ * Block tables of seqs[0..count) as rows of a [count, width] int32 matrix
+ * padded with -1 (the layout pa_decode reads), and their lengths into
+ * context_lens[count] if non-NULL.  PA_ERR_INVALID_ARG for an unknown id or a
+ * table longer than width (then nothing is written).
+ */
+pa_status pa_bm_tables(const pa_block_manager* bm, const int64_t* seqs, int32_t count, int32_t* tables,
+                       int32_t width, int32_t* context_lens);
+/* length of seq in tokens, -1 if unknown */
+int64_t pa_bm_length(const pa_block_manager* bm, int64_t seq);
+pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* out);
 
 /* Static description of a status code. */
 const char* pa_status_string(pa_status s);

@@ -14,13 +14,13 @@ from typing import Optional
 
 import torch
 
-from .blocks import slot_mapping  # noqa: F401
+from .blocks import BlockManager, slot_mapping  # noqa: F401
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 
 F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NO_BLOCKS = 0, -1, -2, -3, -4, -5
 
 _TORCH_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
 
@@ -57,6 +57,28 @@ def library() -> ctypes.CDLL:
     lib.pa_last_error_message.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
     lib.pa_version.restype = ctypes.c_char_p
+    lib.pa_bm_create.argtypes = [i64, i32]
+    lib.pa_bm_create.restype = p
+    lib.pa_bm_destroy.argtypes = [p]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_add.argtypes = [p, i64]
+    lib.pa_bm_add.restype = ctypes.c_int
+    lib.pa_bm_fork.argtypes = [p, i64, i64]
+    lib.pa_bm_fork.restype = ctypes.c_int
+    lib.pa_bm_append.argtypes = [p, i64, i32, p, p, p]
+    lib.pa_bm_append.restype = ctypes.c_int
+    lib.pa_bm_append_batch.argtypes = [p, p, i32, p, p, p, p]
+    lib.pa_bm_append_batch.restype = ctypes.c_int
+    lib.pa_bm_free.argtypes = [p, i64]
+    lib.pa_bm_free.restype = ctypes.c_int
+    lib.pa_bm_table.argtypes = [p, i64, p, i32]
+    lib.pa_bm_table.restype = ctypes.c_int32
+    lib.pa_bm_tables.argtypes = [p, p, i32, p, i32, p]
+    lib.pa_bm_tables.restype = ctypes.c_int
+    lib.pa_bm_length.argtypes = [p, i64]
+    lib.pa_bm_length.restype = ctypes.c_int64
+    lib.pa_bm_get_stats.argtypes = [p, p]
+    lib.pa_bm_get_stats.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -21,6 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["pa_api.hip", "decode_core.hip", "decode_mfma.hip", "decode_valu.hip", "cache_ops.hip"]
+HOST_SOURCES = ["block_manager.cpp"]  # host-only C++, built with the host compiler
 
 ARCH = "gfx950"
 FLAGS = [
@@ -44,9 +45,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpa.so)")
 
 
+def cxx() -> str:
+    for c in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if c and (os.path.exists(c) or shutil.which(c)):
+            return c
+    raise RuntimeError("no host C++ compiler found")
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src in HOST_SOURCES:
+        cmd = [cxx(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
+               "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -55,9 +67,10 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    srcs = SOURCES + HOST_SOURCES
+    jobs = min(len(srcs), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

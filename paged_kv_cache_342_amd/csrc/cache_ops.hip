@@ -51,14 +51,17 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict_
   if (row >= (int64_t)T * Hkv) return;
   const int64_t n = row / Hkv;
   const int h = (int)(row - n * Hkv);
+  // the rows do not depend on the slot: request all three at once (the empty
+  // asm keeps the compiler from sinking the row loads below the slot test)
+  const int64_t src = (row * D + chunk * 8) * 2;
   const int64_t slot = slots[n];
+  const i32x4 kx = ld16(key + src);
+  const i32x4 vx = ld16(value + src);
+  asm volatile("" : : "v"(kx), "v"(vx));
   if (slot < 0 || slot >= num_blocks * bs) return;
   const int64_t b = slot / bs;
   const int o = (int)(slot - b * bs);
-  const int64_t src = (row * D + chunk * 8) * 2;
   const int64_t dst_elem = ((b * Hkv + h) * bs + o) * D + chunk * 8;
-  const i32x4 kx = ld16(key + src);
-  const i32x4 vx = ld16(value + src);
   if constexpr (!kFp8) {
     *reinterpret_cast<i32x4*>(k_cache + dst_elem * 2) = kx;
     *reinterpret_cast<i32x4*>(v_cache + dst_elem * 2) = vx;

@@ -55,6 +55,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED: return "unsupported configuration";
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_NO_BLOCKS: return "not enough free blocks";
   }
   return "unknown status";
 }

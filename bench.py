@@ -106,6 +106,53 @@ def recorded_traffic(workload: str):
     return r.get("hbm_bytes_per_call")
 
 
+def block_manager_bench(w, steps: int = 200):
+    """The batch's host bookkeeping through the library's block manager.
+
+    The manager is brought to the workload's state (for shared prefixes, each
+    prompt is stored once and forked into its samples, whose first appends
+    copy the partially filled shared block), then each of `steps` decode steps
+    appends one token to every sequence and builds the block tables and
+    lengths a pa_decode call takes.  Host time per step through the Python
+    binding, and the tail waste of the workload's own lengths."""
+    import numpy as np
+
+    import paged_kv_cache_342_amd as pa
+
+    bs, B = w.bs, w.B
+    lens = w.context_lens.astype(np.int64)
+    bm = pa.BlockManager(w.num_blocks + B * ((steps + bs - 1) // bs + 1), bs)
+    seqs = np.arange(B, dtype=np.int64)
+    if w.name == "shared_prefix":
+        samples, plen = w.meta["samples"], w.meta["shared_len"].astype(np.int64)
+        for k in range(len(plen)):
+            bm.add(-1 - k)
+            bm.append(-1 - k, int(plen[k]))
+            for j in range(samples):
+                bm.fork(-1 - k, k * samples + j)
+            bm.free(-1 - k)
+        _, pairs = bm.append_batch(seqs, lens - np.repeat(plen, samples))
+    else:
+        for s in range(B):
+            bm.add(s)
+        _, pairs = bm.append_batch(seqs, lens)
+    st = bm.stats()
+    ones = np.ones(B, np.int32)
+    width = int((lens.max() + steps + bs - 1) // bs)
+    # one table matrix kept across steps, as a serving loop would: padded once,
+    # then only block ids are written
+    tables, clens = np.full((B, width), -1, np.int32), np.empty(B, np.int32)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bm.append_batch(seqs, ones)
+        bm.tables(seqs, width, out=tables, lens_out=clens, pad=False)
+    per_step = (time.perf_counter() - t0) / steps
+    return {"host_us_per_step": round(per_step * 1e6, 2), "steps": steps,
+            "ops": "append_batch(B seqs, 1 token each) + tables(B seqs) into a kept matrix",
+            "tail_waste": round(st["tail_waste"], 5), "blocks_in_use": st["blocks_in_use"],
+            "shared_blocks": st["shared_blocks"], "cow_pairs": int(len(pairs))}
+
+
 def _identity_layout(w, batch, slots_new):
     """Renumber physical blocks so each sequence's blocks are consecutive and in
     logical order (block tables become ranges); returns the new token slots."""
@@ -226,6 +273,9 @@ def main():
     log(f"step {ms_step * 1e3:.1f} us (median {np.median(step_ms) * 1e3:.1f}), decode {ms_dec * 1e3:.1f} us "
         f"(median {np.median(dec_ms) * 1e3:.1f}), wall/step incl. flush {wall / args.steps * 1e3:.3f} ms")
 
+    bm = block_manager_bench(w)
+    log(f"block manager: {bm['host_us_per_step']} us per step on the host, tail waste {bm['tail_waste']:.4f}")
+
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(w, args.cpu_budget)
@@ -262,6 +312,7 @@ def main():
             "kernel": "pa_decode call: decode kernel (balanced slices) + merge kernel",
         },
         "cpu_baseline": cpu,
+        "block_manager": bm,
     }
     print(json.dumps(res))
 

@@ -220,12 +220,16 @@ pa_status pa_bm_free(pa_block_manager* bm, int64_t seq);
 int32_t pa_bm_table(const pa_block_manager* bm, int64_t seq, int32_t* table, int32_t capacity);
 /*
  * Block tables of seqs[0..count) as rows of a [count, width] int32 matrix
- * padded with -1 (the layout pa_decode reads), and their lengths into
- * context_lens[count] if non-NULL.  PA_ERR_INVALID_ARG for an unknown id or a
- * table longer than width (then nothing is written).
+ * (the layout pa_decode reads), and their lengths into context_lens[count] if
+ * non-NULL.  pad != 0 writes -1 into every entry past a sequence's blocks;
+ * pad == 0 leaves those entries as they were, so a caller that keeps one
+ * matrix across decode steps writes only the block ids (pa_decode never reads
+ * an entry past a sequence's ceil(length / block_size) blocks).
+ * PA_ERR_INVALID_ARG for an unknown id or a table longer than width (then
+ * nothing is written).
  */
 pa_status pa_bm_tables(const pa_block_manager* bm, const int64_t* seqs, int32_t count, int32_t* tables,
-                       int32_t width, int32_t* context_lens);
+                       int32_t width, int32_t* context_lens, int32_t pad);
 /* length of seq in tokens, -1 if unknown */
 int64_t pa_bm_length(const pa_block_manager* bm, int64_t seq);
 pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* out);

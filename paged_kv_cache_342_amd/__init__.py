@@ -73,7 +73,7 @@ def library() -> ctypes.CDLL:
     lib.pa_bm_free.restype = ctypes.c_int
     lib.pa_bm_table.argtypes = [p, i64, p, i32]
     lib.pa_bm_table.restype = ctypes.c_int32
-    lib.pa_bm_tables.argtypes = [p, p, i32, p, i32, p]
+    lib.pa_bm_tables.argtypes = [p, p, i32, p, i32, p, i32]
     lib.pa_bm_tables.restype = ctypes.c_int
     lib.pa_bm_length.argtypes = [p, i64]
     lib.pa_bm_length.restype = ctypes.c_int64

@@ -90,14 +90,23 @@ class BlockManager:
         self._lib.pa_bm_table(self._h, int(seq), out.ctypes.data, n)
         return out[:n]
 
-    def tables(self, seqs, width: int):
-        """Block tables [len(seqs), width] int32 padded with -1, and lengths [len(seqs)] int32."""
+    def tables(self, seqs, width: int, out=None, lens_out=None, pad: bool = True):
+        """Block tables [len(seqs), width] int32 padded with -1, and lengths [len(seqs)] int32.
+        out / lens_out: C-contiguous int32 arrays of those shapes to write into (a caller that
+        builds tables every step reuses them instead of faulting in new pages each time).
+        pad=False leaves the entries past each sequence's blocks as they were in `out`."""
         seqs = np.ascontiguousarray(seqs, np.int64)
-        tables = np.zeros((max(len(seqs), 1), width), np.int32)
-        lens = np.zeros(max(len(seqs), 1), np.int32)
-        self._check(self._lib.pa_bm_tables(self._h, seqs.ctypes.data, len(seqs), tables.ctypes.data, int(width),
-                                           lens.ctypes.data))
-        return tables[:len(seqs)], lens[:len(seqs)]
+        n = len(seqs)
+        if not pad and out is None:
+            raise ValueError("pad=False writes only block ids: pass the table matrix to update as out")
+        tables = np.empty((max(n, 1), width), np.int32) if out is None else out
+        lens = np.empty(max(n, 1), np.int32) if lens_out is None else lens_out
+        for arr, shape, name in ((out, (n, width), "out"), (lens_out, (n,), "lens_out")):
+            if arr is not None and (arr.dtype != np.int32 or not arr.flags.c_contiguous or arr.shape != shape):
+                raise ValueError(f"{name} must be a C-contiguous int32 array of shape {shape}")
+        self._check(self._lib.pa_bm_tables(self._h, seqs.ctypes.data, n, tables.ctypes.data, int(width),
+                                           lens.ctypes.data, 1 if pad else 0))
+        return tables[:n], lens[:n]
 
     def length(self, seq: int) -> int:
         n = self._lib.pa_bm_length(self._h, int(seq))

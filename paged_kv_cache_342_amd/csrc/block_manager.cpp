@@ -194,7 +194,7 @@ int32_t pa_bm_table(const pa_block_manager* bm, int64_t seq, int32_t* table, int
 }
 
 pa_status pa_bm_tables(const pa_block_manager* bm, const int64_t* seqs, int32_t count, int32_t* tables,
-                       int32_t width, int32_t* context_lens) {
+                       int32_t width, int32_t* context_lens, int32_t pad) {
   if (!bm || count < 0 || width < 1 || (count > 0 && (!seqs || !tables)))
     return set_error("pa_bm_tables: null pointer or bad size"), PA_ERR_INVALID_ARG;
   for (int32_t i = 0; i < count; ++i) {
@@ -210,7 +210,7 @@ pa_status pa_bm_tables(const pa_block_manager* bm, const int64_t* seqs, int32_t 
     int32_t* row = tables + (int64_t)i * width;
     const size_t n = s.table.size();
     if (n) std::memcpy(row, s.table.data(), n * sizeof(int32_t));
-    for (int32_t j = (int32_t)n; j < width; ++j) row[j] = -1;
+    if (pad) std::fill_n(row + n, (size_t)width - n, -1);
     if (context_lens) context_lens[i] = (int32_t)s.length;
   }
   return PA_OK;

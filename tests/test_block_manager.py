@@ -281,3 +281,26 @@ def test_library_manager_rejects_bad_calls():
     assert e.value.status == pa.ERR_INVALID_ARG
     with pytest.raises(KeyError):
         lib.table(9)
+
+
+def test_tables_into_a_kept_matrix():
+    """pad=False writes each sequence's ids and length and nothing past its
+    blocks; pad=True pads with -1.  Bad output buffers are rejected."""
+    lib = pa.BlockManager(64, 4)
+    for s, n in ((0, 9), (1, 1), (2, 16)):
+        lib.add(s)
+        lib.append(s, n)
+    kept = np.full((3, 6), 77, np.int32)
+    lens = np.zeros(3, np.int32)
+    lib.tables([2, 0, 1], 6, out=kept, lens_out=lens, pad=False)
+    for i, s in enumerate((2, 0, 1)):
+        t = [int(x) for x in lib.table(s)]
+        assert list(kept[i, :len(t)]) == t and (kept[i, len(t):] == 77).all()
+    assert list(lens) == [16, 9, 1]
+    lib.tables([2, 0, 1], 6, out=kept, lens_out=lens)
+    assert (kept[0, 4:] == -1).all() and (kept[1, 3:] == -1).all() and (kept[2, 1:] == -1).all()
+    for bad in (np.zeros((3, 6), np.int64), np.zeros((2, 6), np.int32), np.zeros((3, 12), np.int32)[:, ::2]):
+        with pytest.raises(ValueError):
+            lib.tables([2, 0, 1], 6, out=bad)
+    with pytest.raises(ValueError):
+        lib.tables([2, 0, 1], 6, pad=False)

@@ -146,6 +146,35 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * One decode step in one call: each sequence's new token row is appended
+ * and the sequence then attends over all of its positions, the new one
+ * included (the cache grows by one row per generated token: "Paged Attention
+ * and Memory Efficiency ...", section "Why KV cache memory was the
+ * bottleneck ...").  The result, out and both caches, equals
+ *   pa_reshape_and_cache(key, value, slots) followed by pa_decode(...)
+ * with slots[s] = block_tables[s][(L - 1) / bs] * bs + (L - 1) % bs for the
+ * clamped length L = min(context_lens[s], max_context_len, M * bs) of each
+ * sequence; a sequence with L == 0, or whose last block id lies outside the
+ * pool, appends nothing.  The block of position L - 1 must be private to the
+ * sequence (copy it first with pa_copy_blocks if it is shared).
+ *   key, value     [B, num_kv_heads, head_dim] rows of position L - 1, src_dtype:
+ *                  == cache_dtype for 16-bit caches, PA_F16 or PA_BF16 for
+ *                  an FP8 cache (encoded as pa_reshape_and_cache does)
+ *   every other argument as for pa_decode; the caches are written.
+ * For 16-bit caches the decode kernel stores the rows itself and reads them
+ * from key/value, so the call launches no scatter; for FP8 caches a scatter
+ * runs first.  Errors are those of pa_decode and pa_reshape_and_cache; a
+ * call that fails has no effect.
+ */
+pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, const void* key,
+                           const void* value, pa_dtype src_dtype, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t num_kv_heads, int32_t gqa_group,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale, float k_scale,
+                           float v_scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                           void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * Copy-on-write: for each n < N with (src, dst) = block_mapping[n],
  *   k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src]
  * byte for byte (whole [num_kv_heads, block_size, head_dim] chunks).

@@ -49,6 +49,9 @@ def library() -> ctypes.CDLL:
     lib.pa_decode.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32, f32, f32,
                               i32, i32, i32, p, sz, p]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_append.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32,
+                                     f32, f32, i32, i32, i32, p, sz, p]
+    lib.pa_decode_append.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, p]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -158,6 +161,43 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
     _check(library().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
+        _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
+        _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def decode_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, key: torch.Tensor,
+                  value: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                  max_context_len: Optional[int] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                  out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step: append key/value [B, Hkv, D] (the row of position context_lens[s] - 1 of
+    each sequence) into the caches, then attend as decode() does.  Returns out [B, Hq, D]."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (key, "key"), (value, "value")):
+        _require(t, n)
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or Hq % Hkv:
+        raise ValueError("q, k_cache and v_cache shapes do not agree")
+    if key.shape != (B, Hkv, D) or value.shape != key.shape:
+        raise ValueError("key and value must be [B, num_kv_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, M] and context_lens [B]")
+    M = block_tables.shape[1]
+    mcl = M * bs if max_context_len is None else int(max_context_len)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _require(out, "out")
+    need = decode_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl) if B else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_decode_append(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _TORCH_CODE.get(key.dtype, -9),
+        _ptr(block_tables), _ptr(context_lens), B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
         _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
         _ptr(workspace), ws_bytes, _stream(q)))
     return out

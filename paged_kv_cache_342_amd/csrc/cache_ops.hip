@@ -35,6 +35,26 @@ __device__ __forceinline__ i32x2 encode8_fp8(const float* x, float scale) {
   return i32x2{(int)keep_nan_sign((uint32_t)w0, x), (int)keep_nan_sign((uint32_t)w1, x + 4)};
 }
 
+// 8 elements of a K and a V row into the caches at element offset dst_elem.
+template <class ST, bool kFp8>
+__device__ __forceinline__ void store_row8(i32x4 kx, i32x4 vx, uint8_t* __restrict__ k_cache,
+                                           uint8_t* __restrict__ v_cache, int64_t dst_elem, float k_scale,
+                                           float v_scale) {
+  if constexpr (!kFp8) {
+    *reinterpret_cast<i32x4*>(k_cache + dst_elem * 2) = kx;
+    *reinterpret_cast<i32x4*>(v_cache + dst_elem * 2) = vx;
+  } else {
+    float kf[8], vf[8];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      unpack2<ST>((uint32_t)kx[w], kf[2 * w], kf[2 * w + 1]);
+      unpack2<ST>((uint32_t)vx[w], vf[2 * w], vf[2 * w + 1]);
+    }
+    *reinterpret_cast<i32x2*>(k_cache + dst_elem) = encode8_fp8(kf, k_scale);
+    *reinterpret_cast<i32x2*>(v_cache + dst_elem) = encode8_fp8(vf, v_scale);
+  }
+}
+
 // One thread per 8 elements of one (token, kv head) row.
 template <class ST, bool kFp8>
 __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict__ key,
@@ -62,19 +82,67 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict_
   const int64_t b = slot / bs;
   const int o = (int)(slot - b * bs);
   const int64_t dst_elem = ((b * Hkv + h) * bs + o) * D + chunk * 8;
-  if constexpr (!kFp8) {
-    *reinterpret_cast<i32x4*>(k_cache + dst_elem * 2) = kx;
-    *reinterpret_cast<i32x4*>(v_cache + dst_elem * 2) = vx;
-  } else {
-    float kf[8], vf[8];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      unpack2<ST>((uint32_t)kx[w], kf[2 * w], kf[2 * w + 1]);
-      unpack2<ST>((uint32_t)vx[w], vf[2 * w], vf[2 * w + 1]);
-    }
-    *reinterpret_cast<i32x2*>(k_cache + dst_elem) = encode8_fp8(kf, k_scale);
-    *reinterpret_cast<i32x2*>(v_cache + dst_elem) = encode8_fp8(vf, v_scale);
+  store_row8<ST, kFp8>(kx, vx, k_cache, v_cache, dst_elem, k_scale, v_scale);
+}
+
+// The row of position L - 1 of every sequence ([B, Hkv, D]) into the slot
+// the sequence's block table gives that position (L = context_lens[s]
+// clamped to [0, max_ctx]); nothing for L = 0 or a block id outside the
+// pool.  One thread per 8 elements of one (sequence, kv head) row.
+template <class ST, bool kFp8>
+__global__ __launch_bounds__(256) void append_last_kernel(const uint8_t* __restrict__ key,
+                                                          const uint8_t* __restrict__ value,
+                                                          uint8_t* __restrict__ k_cache,
+                                                          uint8_t* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ block_tables,
+                                                          const int32_t* __restrict__ context_lens, int B,
+                                                          int M, int max_ctx, int Hkv, int D, int bs,
+                                                          int64_t num_blocks, float k_scale, float v_scale) {
+  const int per_row = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / per_row;  // sequence * Hkv + head
+  const int chunk = (int)(gid - row * per_row);
+  if (row >= (int64_t)B * Hkv) return;
+  const int64_t n = row / Hkv;
+  const int h = (int)(row - n * Hkv);
+  const int64_t src = (row * D + chunk * 8) * 2;
+  const i32x4 kx = ld16(key + src);
+  const i32x4 vx = ld16(value + src);
+  int L = context_lens[n];
+  L = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+  if (L == 0) return;
+  const int64_t b = block_tables[n * M + (L - 1) / bs];
+  if (b < 0 || b >= num_blocks) return;
+  const int64_t dst_elem = ((b * Hkv + h) * bs + (L - 1) % bs) * D + chunk * 8;
+  store_row8<ST, kFp8>(kx, vx, k_cache, v_cache, dst_elem, k_scale, v_scale);
+}
+
+pa_status append_last_launch(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens, int B, int M,
+                             int max_ctx, int Hkv, int D, int bs, int64_t num_blocks, int src_dtype,
+                             int cache_dtype, float k_scale, float v_scale, hipStream_t stream) {
+  if (B == 0) return PA_OK;
+  const int64_t threads = (int64_t)B * Hkv * (D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  auto K = reinterpret_cast<const uint8_t*>(key);
+  auto V = reinterpret_cast<const uint8_t*>(value);
+  auto KC = reinterpret_cast<uint8_t*>(k_cache);
+  auto VC = reinterpret_cast<uint8_t*>(v_cache);
+  if (cache_dtype != PA_FP8_E4M3)
+    hipLaunchKernelGGL((append_last_kernel<F16, false>), grid, block, 0, stream, K, V, KC, VC, block_tables,
+                       context_lens, B, M, max_ctx, Hkv, D, bs, num_blocks, k_scale, v_scale);
+  else if (src_dtype == PA_F16)
+    hipLaunchKernelGGL((append_last_kernel<F16, true>), grid, block, 0, stream, K, V, KC, VC, block_tables,
+                       context_lens, B, M, max_ctx, Hkv, D, bs, num_blocks, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL((append_last_kernel<BF16, true>), grid, block, 0, stream, K, V, KC, VC, block_tables,
+                       context_lens, B, M, max_ctx, Hkv, D, bs, num_blocks, k_scale, v_scale);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    set_error("pa_decode_append: launch failed: %s", hipGetErrorString(err));
+    return PA_ERR_HIP;
   }
+  return PA_OK;
 }
 
 pa_status scatter_launch(const void* key, const void* value, void* k_cache, void* v_cache,

@@ -58,6 +58,13 @@ struct DecodeArgs {
   int32_t out_dtype;           // 0 f32, 1 f16, 2 bf16
   float qk_scale_log2;         // scale * k_scale * log2(e)
   float v_scale;
+  // Appending in the same launch (16-bit caches): the row of position L - 1
+  // of every sequence, [B, Hkv, D] in the cache dtype; null = no append.
+  // Loads of that position read these rows, never the cache, and the wave
+  // that owns a sequence's last chunk (query-head tile 0) stores them into
+  // the cache, so nothing in the launch reads a slot written by it.
+  const uint8_t* new_k;
+  const uint8_t* new_v;
 };
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

@@ -156,6 +156,17 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     return PA_ERR_UNSUPPORTED;
   }
   const int Hq = r.Hkv * r.G;
+  // Appending: 16-bit rows are stored by the decode kernel itself; fp8 rows
+  // are encoded into the cache by a scatter first.
+  const bool fused_append = r.new_k != nullptr && r.cache_dtype != PA_FP8_E4M3;
+  if (r.new_k != nullptr && !fused_append) {
+    const pa_status st = append_last_launch(r.new_k, r.new_v, const_cast<void*>(r.k_cache),
+                                            const_cast<void*>(r.v_cache), r.block_tables, r.context_lens, r.B,
+                                            r.M, r.max_ctx, r.Hkv, r.D, r.bs, r.num_blocks, r.src_dtype,
+                                            r.cache_dtype, r.k_scale, r.v_scale, stream);
+    if (st != PA_OK) return st;
+  }
+  const size_t new_row = (size_t)r.Hkv * r.D * 2;
   uint8_t* ws = reinterpret_cast<uint8_t*>(r.workspace);
   DecodeArgs a{};
   a.k_cache = reinterpret_cast<const uint8_t*>(r.k_cache);
@@ -187,6 +198,8 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     a.q = reinterpret_cast<const uint8_t*>(r.q) + (size_t)s0 * q_row;
     a.block_tables = r.block_tables + (int64_t)s0 * r.M;
     a.context_lens = r.context_lens + s0;
+    a.new_k = fused_append ? reinterpret_cast<const uint8_t*>(r.new_k) + (size_t)s0 * new_row : nullptr;
+    a.new_v = fused_append ? reinterpret_cast<const uint8_t*>(r.new_v) + (size_t)s0 * new_row : nullptr;
     const dim3 grid((unsigned)grid_waves);
     const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream)
                          : launch_decode_mfma(a, ct, qt, r.D, r.bs, grid, stream);

@@ -18,6 +18,11 @@
 // none of them sits under a branch (positions past the end of a segment
 // re-read its last row and get a score of -inf).
 //
+// When the launch also appends each sequence's new row (16-bit caches), the
+// loads of position L - 1 read the caller's row instead of the cache, and
+// the wave that owns the sequence's last chunk stores that row into its slot
+// at the end of the segment.
+//
 // Softmax runs online in fp32 in the log2 domain.  The running maximum of a
 // head only moves when some score exceeds it by more than kRescaleThreshold
 // (a wave-uniform branch); otherwise probabilities are 2^(s - m) <= 2^8,
@@ -89,6 +94,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int VD = Raw::VD;
   constexpr int64_t kChunkBytes = (int64_t)BS * D * e;  // one (block, head) chunk
   constexpr int NB = kChunk / BS;
+  constexpr bool kCanAppend = !kFp8;   // new rows are stored as given
+  constexpr int kRowLanes = D * e / 16;  // lanes that hold one row, 16 bytes each
 
   __shared__ int cum[kScanMax + 1];
   __shared__ int lens[kScanMax];
@@ -128,16 +135,19 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 
   // What a segment needs before its first chunk: the query (B operand of QK,
-  // in the k-slot order the K loads use), its block-id ring and the offset of
-  // its last row (read by lanes whose position lies past the end).  Each
-  // segment's header is requested one segment ahead, with loads that do not
-  // depend on whether there is a next segment (past the last one the current
-  // segment's header is read again), so segment changes cost no table or
-  // query round trips.
+  // in the k-slot order the K loads use), its block-id ring and where its
+  // last row is read from (by lanes whose position lies past the end, and,
+  // when appending, by the last position itself).  Each segment's header is
+  // requested one segment ahead, with loads that do not depend on whether
+  // there is a next segment (past the last one the current segment's header
+  // is read again), so segment changes cost no table or query round trips.
   struct Header {
     i32x4 qop[KK];
     IdRing<BS> ring;
-    int64_t last_off;
+    const uint8_t* last_k;  // row of the last position
+    const uint8_t* last_v;
+    int lim;                // positions from lim on read last_k / last_v
+    int64_t tail_off;       // cache offset the appended row goes to; -1 = none
   };
   auto load_header = [&](const Segment& g, Header& hd) {
     const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
@@ -152,8 +162,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const int blk0 = g.tok0 / BS;
     hd.ring.start(trow + blk0, (g.tok_end + BS - 1) / BS - blk0);
     int id = uniform(trow[(g.tok_end - 1) / BS]);
-    if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
-    hd.last_off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * D * e;
+    const bool id_ok = id >= 0 && (int64_t)id < a.num_blocks;
+    if (!id_ok) id = 0;
+    const int64_t off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * D * e;
+    const bool app = kCanAppend && a.new_k != nullptr && g.tok_end == lens[g.s];
+    const int64_t nrow = ((int64_t)g.s * a.Hkv + h) * D * e;
+    hd.last_k = app ? a.new_k + nrow : kbase + off;
+    hd.last_v = app ? a.new_v + nrow : vbase + off;
+    hd.lim = g.tok_end - (app ? 1 : 0);
+    hd.tail_off = app && id_ok && ht == 0 ? off : -1;
   };
 
   Segment cur = next_segment(sl, cum, lens, a.B, sl.s_first);
@@ -169,7 +186,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const int tok0 = cur.tok0, tok_end = cur.tok_end, nchunks = cur.nchunks;
     const i32x4* qop = hc.qop;
     IdRing<BS>& ring = hc.ring;
-    const int64_t last_off = hc.last_off;
+    const int lim = hc.lim;
+    // the appended row, stored at the end of the segment: lane i < kRowLanes
+    // holds 16 bytes of K, the next kRowLanes lanes 16 bytes of V
+    i32x4 app_row = {0, 0, 0, 0};
+    if (kCanAppend && a.new_k != nullptr)
+      app_row = ld16((lane < kRowLanes ? hc.last_k : hc.last_v) + 16 * (lane % kRowLanes));
 
     auto load_chunk = [&](int c, Raw& raw) {
       const int ctok = tok0 + kChunk * c;  // first position of the chunk
@@ -184,9 +206,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       for (int tt = 0; tt < 2; ++tt) {
         const int tc = 16 * tt + r;
         const int bsel = BS == 32 ? 0 : (BS == 16 ? tt : 2 * tt + (r >> 3));
-        const bool ok = ctok + tc < tok_end;
-        const int64_t roff = ok ? (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : last_off;
-        const uint8_t* row = kbase + roff;
+        const bool ok = ctok + tc < lim;
+        const uint8_t* row = ok ? kbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : hc.last_k;
 #pragma unroll
         for (int u = 0; u < Raw::KR; ++u) {
           const int off = kFp8 ? 64 * u + 16 * gq : (32 * u + 8 * gq) * 2;
@@ -198,9 +219,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       for (int j = 0; j < 8; ++j) {
         const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
         const int bsel = BS == 32 ? 0 : (BS == 16 ? (j >> 2) : 2 * (j >> 2) + (gq >> 1));
-        const bool ok = ctok + tc < tok_end;
-        const int64_t roff = ok ? (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : last_off;
-        load_dwords<VD>(vbase + roff + W * r * e, raw.v[j]);
+        const bool ok = ctok + tc < lim;
+        const uint8_t* row = ok ? vbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : hc.last_v;
+        load_dwords<VD>(row + W * r * e, raw.v[j]);
       }
     };
 
@@ -360,6 +381,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         store_partial(a, row, D, 4 * W * gq, v, 4 * W);
         if (gq == 0) store_ml(a, row, m, l);
       }
+    }
+    if (hc.tail_off >= 0 && lane < 2 * kRowLanes) {
+      uint8_t* dst = const_cast<uint8_t*>(lane < kRowLanes ? kbase : vbase) + hc.tail_off;
+      *reinterpret_cast<i32x4*>(dst + 16 * (lane % kRowLanes)) = app_row;
     }
 
     if (nxt.s < 0) break;

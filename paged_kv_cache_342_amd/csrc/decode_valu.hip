@@ -20,6 +20,10 @@
 //        the end of the segment the 64 / R lanes that hold the same
 //        elements are summed (DPP row rotations, then two cross-row
 //        exchanges).
+// When the launch also appends each sequence's new row (16-bit caches), the
+// loads of position L - 1 read the caller's row instead of the cache, and
+// the wave that owns the sequence's last chunk stores that row into its slot
+// at the end of the segment.
 #include "decode_common.h"
 
 namespace pa {
@@ -69,6 +73,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   constexpr int U = 32 * e / 16;    // 16-byte loads per lane per row
   constexpr int64_t kChunkBytes = (int64_t)BS * D * e;
   constexpr int NB = kChunk / BS;
+  constexpr bool kCanAppend = e == 2;    // new rows are stored as given
+  constexpr int kRowLanes = D * e / 16;  // lanes that hold one row, 16 bytes each
   struct Raw {
     i32x4 k[NT][U];
     i32x4 v[NT][U];
@@ -109,14 +115,19 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   }
 
   // What a segment needs before its first chunk: the group's query rows (as
-  // loaded), its block-id ring and the offset of its last row.  Each header
-  // is requested one segment ahead with loads that do not depend on whether
-  // there is a next segment (past the last one the current header is read
-  // again), so segment changes cost no table or query round trips.
+  // loaded), its block-id ring and where its last row is read from (by lanes
+  // whose position lies past the end, and, when appending, by the last
+  // position itself).  Each header is requested one segment ahead with loads
+  // that do not depend on whether there is a next segment (past the last one
+  // the current header is read again), so segment changes cost no table or
+  // query round trips.
   struct Header {
     i32x4 q[G][U][EPU / 8];
     IdRing<BS> ring;
-    int64_t last_off;
+    const uint8_t* last_k;  // row of the last position
+    const uint8_t* last_v;
+    int lim;                // positions from lim on read last_k / last_v
+    int64_t tail_off;       // cache offset the appended row goes to; -1 = none
   };
   auto load_header = [&](const Segment& g, Header& hd) {
 #pragma unroll
@@ -131,8 +142,15 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     const int blk0 = g.tok0 / BS;
     hd.ring.start(trow + blk0, (g.tok_end + BS - 1) / BS - blk0);
     int id = uniform(trow[(g.tok_end - 1) / BS]);
-    if (id < 0 || (int64_t)id >= a.num_blocks) id = 0;
-    hd.last_off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * D * e;
+    const bool id_ok = id >= 0 && (int64_t)id < a.num_blocks;
+    if (!id_ok) id = 0;
+    const int64_t off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * D * e;
+    const bool app = kCanAppend && a.new_k != nullptr && g.tok_end == lens[g.s];
+    const int64_t nrow = ((int64_t)g.s * a.Hkv + h) * D * e;
+    hd.last_k = app ? a.new_k + nrow : kbase + off;
+    hd.last_v = app ? a.new_v + nrow : vbase + off;
+    hd.lim = g.tok_end - (app ? 1 : 0);
+    hd.tail_off = app && id_ok ? off : -1;
   };
 
   Segment cur = next_segment(sl, cum, lens, a.B, sl.s_first);
@@ -147,7 +165,12 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     const int cs = cur.cs, ce = cur.ce;
     const int tok0 = cur.tok0, tok_end = cur.tok_end, nchunks = cur.nchunks;
     IdRing<BS>& ring = hc.ring;
-    const int64_t last_off = hc.last_off;
+    const int lim = hc.lim;
+    // the appended row, stored at the end of the segment: lane i < kRowLanes
+    // holds 16 bytes of K, the next kRowLanes lanes 16 bytes of V
+    i32x4 app_row = {0, 0, 0, 0};
+    if (kCanAppend && a.new_k != nullptr)
+      app_row = ld16((lane < kRowLanes ? hc.last_k : hc.last_v) + 16 * (lane % kRowLanes));
 
     // query, widened and pre-scaled into the log2 domain
     float qf[G][32];
@@ -175,13 +198,15 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int tc = TT * t + row;  // position within the chunk
-        const bool ok = tok0 + kChunk * ch + tc < tok_end;
-        const int64_t off = ok ? (int64_t)pick<NB>(id, tc / BS) * blk_stride + (tc % BS) * D * e : last_off;
+        const bool ok = tok0 + kChunk * ch + tc < lim;
+        const int64_t off = (int64_t)pick<NB>(id, tc / BS) * blk_stride + (tc % BS) * D * e;
+        const uint8_t* krow = ok ? kbase + off : hc.last_k;
+        const uint8_t* vrow = ok ? vbase + off : hc.last_v;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int col = 16 * (c + R * u);
-          raw.k[t][u] = ld16_stream(kbase + off + col);
-          raw.v[t][u] = ld16_stream(vbase + off + col);
+          raw.k[t][u] = ld16_stream(krow + col);
+          raw.v[t][u] = ld16_stream(vrow + col);
         }
       }
     };
@@ -296,6 +321,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
         }
         if (!whole && c == 0) store_ml(a, prow, m[i], lt);
       }
+    }
+    if (hc.tail_off >= 0 && lane < 2 * kRowLanes) {
+      uint8_t* dst = const_cast<uint8_t*>(lane < kRowLanes ? kbase : vbase) + hc.tail_off;
+      *reinterpret_cast<i32x4*>(dst + 16 * (lane % kRowLanes)) = app_row;
     }
 
     if (nxt.s < 0) break;

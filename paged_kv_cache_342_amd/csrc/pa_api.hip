@@ -94,18 +94,26 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_gro
   return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, 1, device_cu_count()).bytes;
 }
 
-pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
-                    int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim, int32_t block_size,
-                    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
-                    float scale, float k_scale, float v_scale, pa_dtype q_dtype,
-                    pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
-                    size_t workspace_bytes, pa_stream_t stream) {
-  g_error[0] = 0;
-  const char* fn = "pa_decode";
+}  // extern "C"
+
+namespace pa {
+
+// Checks shared by pa_decode and pa_decode_append; fills r on success.
+static pa_status decode_request(const char* fn, void* out, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, float scale, float k_scale, float v_scale,
+                                pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
+                                size_t workspace_bytes, DecodeRequest& r) {
   if (B < 0) return fail(PA_ERR_INVALID_ARG, "%s: B must be >= 0", fn);
   if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: at most 65535 sequences per call", fn);
-  PA_CHECK_SHAPE("pa_decode", num_kv_heads, head_dim, block_size, num_blocks);
+  if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "%s: num_kv_heads must be >= 1 (got %d)", fn, num_kv_heads);
+  if (num_blocks < 1) return fail(PA_ERR_INVALID_ARG, "%s: num_blocks must be >= 1", fn);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128 (got %d)", fn, head_dim);
+  if (block_size != 8 && block_size != 16 && block_size != 32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size must be 8, 16 or 32 (got %d)", fn, block_size);
   if (gqa_group < 1) return fail(PA_ERR_INVALID_ARG, "%s: gqa_group must be >= 1", fn);
   if ((int64_t)num_kv_heads * gqa_group > 65536) return fail(PA_ERR_UNSUPPORTED, "%s: too many query heads", fn);
   if (max_blocks_per_seq < 1) return fail(PA_ERR_INVALID_ARG, "%s: max_blocks_per_seq must be >= 1", fn);
@@ -119,6 +127,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
   if (cache_dtype == PA_FP8_E4M3 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return fail(PA_ERR_INVALID_ARG, "%s: fp8 scales must be finite and > 0", fn);
+  r = DecodeRequest{};
+  r.B = B;
   if (B == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PA_ERR_INVALID_ARG, "%s: null pointer argument", fn);
@@ -132,14 +142,12 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
-  DecodeRequest r{};
   r.out = out;
   r.q = q;
   r.k_cache = k_cache;
   r.v_cache = v_cache;
   r.block_tables = block_tables;
   r.context_lens = context_lens;
-  r.B = B;
   r.Hkv = num_kv_heads;
   r.G = gqa_group;
   r.D = head_dim;
@@ -156,6 +164,54 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   r.out_dtype = out_dtype;
   r.workspace = workspace;
   r.workspace_bytes = workspace_bytes;
+  return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                    int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, float k_scale, float v_scale, pa_dtype q_dtype,
+                    pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
+                    size_t workspace_bytes, pa_stream_t stream) {
+  g_error[0] = 0;
+  DecodeRequest r;
+  const pa_status st = decode_request("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, B,
+                                      num_kv_heads, gqa_group, head_dim, block_size, num_blocks,
+                                      max_blocks_per_seq, max_context_len, scale, k_scale, v_scale, q_dtype,
+                                      cache_dtype, out_dtype, workspace, workspace_bytes, r);
+  if (st != PA_OK || B == 0) return st;
+  return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
+}
+
+pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, const void* key,
+                           const void* value, pa_dtype src_dtype, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t num_kv_heads, int32_t gqa_group,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len, float scale, float k_scale,
+                           float v_scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                           void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_decode_append";
+  DecodeRequest r;
+  const pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads,
+                                      gqa_group, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                      max_context_len, scale, k_scale, v_scale, q_dtype, cache_dtype, out_dtype,
+                                      workspace, workspace_bytes, r);
+  if (st != PA_OK) return st;
+  if (!known_dtype(src_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (cache_dtype == PA_FP8_E4M3 ? (src_dtype != PA_F16 && src_dtype != PA_BF16) : src_dtype != cache_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "%s: new rows must have the cache dtype (f16 or bf16 for an fp8 cache)", fn);
+  if (B == 0) return PA_OK;
+  if (!key || !value) return fail(PA_ERR_INVALID_ARG, "%s: null key/value", fn);
+  if (!aligned(key, 16) || !aligned(value, 16)) return fail(PA_ERR_INVALID_ARG, "%s: misaligned key/value", fn);
+  r.new_k = key;
+  r.new_v = value;
+  r.src_dtype = src_dtype;
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -40,6 +40,11 @@ struct DecodeRequest {
   int q_dtype, cache_dtype, out_dtype;
   void* workspace;
   size_t workspace_bytes;
+  // appending the row of position L - 1 of every sequence in the same call
+  // ([B, Hkv, D], src_dtype); null = plain decode
+  const void* new_k;
+  const void* new_v;
+  int src_dtype;
 };
 
 // 0 = default choice, 1 = VALU/DPP kernel, 2 = MFMA kernel
@@ -53,6 +58,11 @@ pa_status scatter_launch(const void* key, const void* value, void* k_cache, void
                          const int64_t* slots, int T, int Hkv, int D, int bs, int64_t num_blocks,
                          int src_dtype, int cache_dtype, float k_scale, float v_scale,
                          hipStream_t stream);
+
+pa_status append_last_launch(const void* key, const void* value, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens, int B, int M,
+                             int max_ctx, int Hkv, int D, int bs, int64_t num_blocks, int src_dtype,
+                             int cache_dtype, float k_scale, float v_scale, hipStream_t stream);
 
 pa_status copy_blocks_launch(void* k_cache, void* v_cache, const int64_t* pairs, int N,
                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);

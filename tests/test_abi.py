@@ -67,6 +67,36 @@ def test_decode_rejects_bad_arguments(kw, status):
     assert pa.library().pa_last_error_message()
 
 
+def _decode_append(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, key=FAKE, value=FAKE, sd=pa.BF16, bt=FAKE, cl=FAKE, B=2, Hkv=2, G=2,
+             D=128, bs=16, nb=10, M=4, mcl=64, scale=0.1, ks=1.0, vs=1.0, qd=pa.BF16, cd=pa.BF16, od=pa.F32, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return pa.library().pa_decode_append(a["out"], a["q"], a["k"], a["v"], a["key"], a["value"], a["sd"], a["bt"],
+                                         a["cl"], a["B"], a["Hkv"], a["G"], a["D"], a["bs"], a["nb"], a["M"], a["mcl"],
+                                         a["scale"], a["ks"], a["vs"], a["qd"], a["cd"], a["od"], a["ws"], a["wsb"],
+                                         None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sd=pa.F16), pa.ERR_UNSUPPORTED),          # 16-bit cache: rows must have its dtype
+    (dict(cd=pa.FP8_E4M3, sd=pa.F32), pa.ERR_UNSUPPORTED),
+    (dict(sd=9), pa.ERR_INVALID_ARG),
+    (dict(key=None), pa.ERR_INVALID_ARG),
+    (dict(value=FAKE + 8), pa.ERR_INVALID_ARG),
+    (dict(D=96), pa.ERR_UNSUPPORTED),                # the checks of pa_decode apply as well
+    (dict(ws=None, wsb=0), pa.ERR_WORKSPACE),
+    (dict(qd=pa.F16, cd=pa.BF16), pa.ERR_UNSUPPORTED),
+])
+def test_decode_append_rejects_bad_arguments(kw, status):
+    assert _decode_append(**kw) == status
+    assert pa.library().pa_last_error_message()
+
+
+def test_decode_append_empty_batch_is_a_no_op():
+    assert _decode_append(B=0, out=None, q=None, bt=None, cl=None, key=None, value=None) == pa.OK
+
+
 def test_decode_workspace_checks():
     need = pa.decode_workspace_size(64, 8, 4, 128, 16, 4096)
     assert need > 0

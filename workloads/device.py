@@ -95,10 +95,29 @@ class DeviceBatch:
             pa.reshape_and_cache(k[i:i + step], v[i:i + step], self.kc, self.vc, slots[i:i + step],
                                  w.k_scale, w.v_scale)
 
+    def last_rows(self):
+        """The row of position L - 1 of every sequence, [B, Hkv, D] each for K and V in the
+        source dtype (zeros where L = 0): what one decode step appends."""
+        w = self.w
+        k = np.zeros((w.B, w.Hkv, w.D), np.float16 if w.src_dtype == "f16" else np.uint16)
+        v = np.zeros_like(k)
+        for s in range(w.B):
+            L = int(w.context_lens[s])
+            if L > 0:
+                ks, vs = w.seq_kv(s)
+                k[s], v[s] = ks[L - 1], vs[L - 1]
+        return (storage_to_torch(k, w.src_dtype).to(self.device), storage_to_torch(v, w.src_dtype).to(self.device))
+
+    def decode_append(self, k_new, v_new, out_dtype=torch.float32, **kw):
+        w = self.w
+        kw.setdefault("max_context_len", w.max_context_len if w.B else 1)
+        return pa.decode_append(self.q, self.kc, self.vc, k_new, v_new, self.tables, self.lens, w.scale,
+                                k_scale=w.k_scale, v_scale=w.v_scale, out_dtype=out_dtype, **kw)
+
     def decode(self, out_dtype=torch.float32, **kw):
         w = self.w
-        return pa.decode(self.q, self.kc, self.vc, self.tables, self.lens, w.scale,
-                         max_context_len=w.max_context_len if w.B else 1, k_scale=w.k_scale,
+        kw.setdefault("max_context_len", w.max_context_len if w.B else 1)
+        return pa.decode(self.q, self.kc, self.vc, self.tables, self.lens, w.scale, k_scale=w.k_scale,
                          v_scale=w.v_scale, out_dtype=out_dtype, **kw)
 
 

@@ -20,6 +20,10 @@
  *       Batching" (flow figure: the attention kernel reads blocks by block
  *       table);
  *       "PagedAttention - The KV Cache Problem", section "How It Works".
+ *   - pa_decode_append: one decode step in one call (append, then attend).
+ *   - pa_bm_*: the host block manager that hands out the slots, tables and
+ *     copy pairs the calls above take (pool, on-demand growth, sharing,
+ *     copy-on-write, sink + window eviction).
  *   - pa_copy_blocks: copy-on-write duplication of a shared block once a
  *     sequence diverges from a shared prefix:
  *       "Paged Attention and Memory Efficiency ...", section "How
@@ -243,6 +247,26 @@ pa_status pa_bm_append(pa_block_manager* bm, int64_t seq, int32_t n, int64_t* sl
  */
 pa_status pa_bm_append_batch(pa_block_manager* bm, const int64_t* seqs, int32_t count, const int32_t* n_tokens,
                              int64_t* slots, int64_t* copy_pairs, int32_t* n_pairs);
+/*
+ * Block-wise sliding-window eviction with attention sinks: keep the blocks
+ * that hold the first sink_tokens positions and those that hold the last
+ * window_tokens positions of seq, release the whole blocks in between (a
+ * shared block loses one reference) and close the gap in the table.  The
+ * sequence then holds its kept positions in order, renumbered from 0, so a
+ * plain pa_decode over the new table attends exactly to the sink and the
+ * recent window; its length shrinks by *dropped (a multiple of block_size,
+ * 0 when nothing lies between).  Whole blocks only: at least sink_tokens
+ * and window_tokens positions stay, at most block_size - 1 more of each,
+ * and the block holding the newest position always stays (window 0 keeps
+ * the block the next token goes into).
+ * ("Paged Attention and Memory Efficiency ...", section "Eviction,
+ * compression, and the challenge of fitting more KV cache into less
+ * memory": initial sink tokens plus a window of recent ones, and eviction
+ * of whole blocks of the paged layout without changing the kernel.)
+ * PA_ERR_INVALID_ARG for an unknown id or a negative count.
+ */
+pa_status pa_bm_evict(pa_block_manager* bm, int64_t seq, int64_t sink_tokens, int64_t window_tokens,
+                      int64_t* dropped);
 /* return seq's blocks to the pool (those no other sequence references) */
 pa_status pa_bm_free(pa_block_manager* bm, int64_t seq);
 /* number of blocks of seq (-1 if unknown); writes min(that, capacity) ids to table if non-NULL */

@@ -153,6 +153,36 @@ class BlockManager:
         for b in s.table:
             self._release(b)
 
+    def evict(self, seq: int, sink_tokens: int, window_tokens: int) -> int:
+        """Sliding window with attention sinks, whole blocks at a time ("Paged
+        Attention and Memory Efficiency in Production LLM Serving", section
+        "Eviction, compression, and the challenge of fitting more KV cache
+        into less memory": the first few tokens are kept as attention sinks
+        next to a window of recent tokens, and eviction works on whole blocks
+        of the paged layout).  A block may go only if none of its positions is
+        among the first sink_tokens or the last window_tokens, and the block
+        holding the newest position (the one the next token goes into) always
+        stays; the blocks that go leave the table, which keeps its order.
+        Returns the number of positions dropped."""
+        s = self.seqs[seq]
+        if sink_tokens < 0 or window_tokens < 0:
+            raise ValueError("negative sink or window")
+        bs, L = self.block_size, s.length
+        keep = []
+        for j, b in enumerate(s.table):
+            first, last = j * bs, min(L, (j + 1) * bs) - 1  # positions block j holds
+            in_sink = first < sink_tokens
+            in_window = last >= L - window_tokens
+            newest = j == len(s.table) - 1
+            keep.append(in_sink or in_window or newest)
+        gone = [j for j, k in enumerate(keep) if not k]
+        assert all((j + 1) * bs <= L for j in gone)  # only full blocks can go
+        for j in gone:
+            self._release(s.table[j])
+        s.table = [b for b, k in zip(s.table, keep) if k]
+        s.length -= len(gone) * bs
+        return len(gone) * bs
+
     def table(self, seq: int) -> List[int]:
         return list(self.seqs[seq].table)
 

@@ -74,6 +74,8 @@ def library() -> ctypes.CDLL:
     lib.pa_bm_append_batch.restype = ctypes.c_int
     lib.pa_bm_free.argtypes = [p, i64]
     lib.pa_bm_free.restype = ctypes.c_int
+    lib.pa_bm_evict.argtypes = [p, i64, i64, i64, p]
+    lib.pa_bm_evict.restype = ctypes.c_int
     lib.pa_bm_table.argtypes = [p, i64, p, i32]
     lib.pa_bm_table.restype = ctypes.c_int32
     lib.pa_bm_tables.argtypes = [p, p, i32, p, i32, p, i32]

@@ -82,6 +82,14 @@ class BlockManager:
     def free(self, seq: int):
         self._check(self._lib.pa_bm_free(self._h, int(seq)))
 
+    def evict(self, seq: int, sink_tokens: int, window_tokens: int) -> int:
+        """Keep the blocks of the first sink_tokens and the last window_tokens positions of seq,
+        release the whole blocks in between and close the gap; returns the positions dropped."""
+        dropped = self._ct.c_int64(0)
+        self._check(self._lib.pa_bm_evict(self._h, int(seq), int(sink_tokens), int(window_tokens),
+                                          self._ct.byref(dropped)))
+        return int(dropped.value)
+
     def table(self, seq: int) -> np.ndarray:
         n = self._lib.pa_bm_table(self._h, int(seq), None, 0)
         if n < 0:

@@ -173,6 +173,29 @@ pa_status pa_bm_append_batch(pa_block_manager* bm, const int64_t* seqs, int32_t 
   return PA_OK;
 }
 
+pa_status pa_bm_evict(pa_block_manager* bm, int64_t seq, int64_t sink_tokens, int64_t window_tokens,
+                      int64_t* dropped) {
+  if (!bm || sink_tokens < 0 || window_tokens < 0)
+    return set_error("pa_bm_evict: null manager or negative sink/window"), PA_ERR_INVALID_ARG;
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return set_error("pa_bm_evict: no sequence %lld", (long long)seq), PA_ERR_INVALID_ARG;
+  pa_block_manager::Seq& s = it->second;
+  const int64_t bs = bm->block_size;
+  const int64_t nblk = (int64_t)s.table.size();
+  const int64_t head = (sink_tokens + bs - 1) / bs;  // blocks kept in front
+  // first block kept behind: the window's first, never past the newest block
+  const int64_t tail = std::min(s.length > window_tokens ? (s.length - window_tokens) / bs : 0, nblk - 1);
+  int64_t n = 0;
+  if (tail > head) {
+    for (int64_t j = head; j < tail; ++j) bm->release(s.table[(size_t)j]);
+    s.table.erase(s.table.begin() + head, s.table.begin() + tail);
+    n = (tail - head) * bs;
+    s.length -= n;
+  }
+  if (dropped) *dropped = n;
+  return PA_OK;
+}
+
 pa_status pa_bm_free(pa_block_manager* bm, int64_t seq) {
   if (!bm) return set_error("pa_bm_free: null manager"), PA_ERR_INVALID_ARG;
   auto it = bm->seqs.find(seq);

@@ -108,11 +108,37 @@ def test_exhausted_pool_changes_nothing():
     assert before == (list(m._free), list(m.refcount), m.table(0), m.table(1))
 
 
+def _evict_ok(old_rows, new_rows, bs, sink, window):
+    """What sink + window eviction must leave, stated on positions: the kept
+    rows are original rows in their order, the first `sink` and the last
+    `window` positions are among them, whole blocks went, and no block that
+    stayed could have gone (each holds a sink position, a window position or
+    the newest one)."""
+    L = len(old_rows)
+    where = {r.tobytes(): t for t, r in enumerate(old_rows)}
+    kept = [where.get(r.tobytes(), -1) for r in new_rows]
+    if -1 in kept or kept != sorted(kept) or len(set(kept)) != len(kept):
+        return False
+    ks = set(kept)
+    if not set(range(min(sink, L))) <= ks or not set(range(max(0, L - window), L)) <= ks:
+        return False
+    if (L - len(kept)) % bs:
+        return False
+    for j in range(0, len(kept), bs):  # blocks of the new table
+        block = kept[j:j + bs]
+        if block != list(range(block[0], block[0] + len(block))):
+            return False
+        if not (block[0] < sink or block[-1] >= L - window or j + bs >= len(kept)):
+            return False
+    return True
+
+
 def _run_stream(manager_cls, seed, steps=400, num_blocks=96, bs=4, H=2, D=8):
-    """Random add / fork / append / free stream.  Token rows are written
-    through the manager's slots into an oracle pool (copying blocks first for
-    every copy pair); returns whether every live sequence gathers back exactly
-    the rows it was given."""
+    """Random add / fork / append / free / evict stream.  Token rows are
+    written through the manager's slots into an oracle pool (copying blocks
+    first for every copy pair); returns whether every eviction kept what it
+    must and every live sequence gathers back exactly the rows it was given
+    (less the evicted ones)."""
     rng = np.random.default_rng(seed)
     m = manager_cls(num_blocks, bs)
     kc = O.new_pool(num_blocks, H, bs, D, "f16")
@@ -120,10 +146,19 @@ def _run_stream(manager_cls, seed, steps=400, num_blocks=96, bs=4, H=2, D=8):
     rows = {}
     next_id = 0
     for _ in range(steps):
-        op = rng.integers(0, 10)
+        op = rng.integers(0, 11)
         live = sorted(rows)
         try:
-            if op == 0 or not live:
+            if op == 10 and live:
+                s = int(rng.choice(live))
+                sink, window = int(rng.integers(0, 7)), int(rng.integers(0, 21))
+                dropped = m.evict(s, sink, window)
+                new_len = len(rows[s]) - dropped
+                new_rows = O.gather_kv(kc, m.table(s), new_len)
+                if m.length(s) != new_len or not _evict_ok(rows[s], new_rows, bs, sink, window):
+                    return False
+                rows[s] = new_rows
+            elif op == 0 or not live:
                 m.add(next_id)
                 rows[next_id] = np.zeros((0, H, D), np.float16)
                 next_id += 1
@@ -180,6 +215,13 @@ class _NoCopy(RefManager):
         return slots, []
 
 
+class _EvictOneTooMany(RefManager):
+    """planted mistake: the window loses its oldest block"""
+
+    def evict(self, seq, sink_tokens, window_tokens):
+        return super().evict(seq, sink_tokens, max(0, window_tokens - self.block_size))
+
+
 class _NoForkRef(RefManager):
     """planted mistake: forking does not count the child's references"""
 
@@ -192,6 +234,23 @@ class _NoForkRef(RefManager):
 def test_pins_catch_planted_mistakes():
     assert not all(_run_stream(_NoCopy, seed) for seed in range(6))
     assert not all(_run_stream(_NoForkRef, seed) for seed in range(6))
+    assert not all(_run_stream(_EvictOneTooMany, seed) for seed in range(6))
+
+
+def test_worked_sink_window_eviction():
+    """Four tokens per block, 30 tokens, a 4-token sink and a 10-token window:
+    block 0 (the sink) and blocks 5-7 (positions 20-29) stay, blocks 1-4 go."""
+    for make in (lambda: RefManager(16, 4), lambda: pa.BlockManager(16, 4)):
+        m = make()
+        m.add(0)
+        m.append(0, 30)
+        before = [int(b) for b in m.table(0)]
+        assert m.evict(0, 4, 10) == 16
+        assert [int(b) for b in m.table(0)] == [before[0]] + before[5:]
+        assert m.length(0) == 14 and m.stats()["blocks_free"] == 16 - 4
+        assert m.evict(0, 4, 10) == 0  # nothing left between sink and window
+        slots, _ = m.append(0, 3)  # appends continue in the newest block
+        assert [int(x) for x in slots] == [before[7] * 4 + 2, before[7] * 4 + 3, int(m.table(0)[-1]) * 4]
 
 
 # ------------------------------------------------------------------ the library against the oracle
@@ -229,6 +288,10 @@ def test_library_manager_matches_oracle(seed):
             ref.free(s)
             lib.free(s)
             live.remove(s)
+        elif op == 9:
+            s = int(rng.choice(live))
+            sink, window = int(rng.integers(0, 3 * bs)), int(rng.integers(0, 5 * bs))
+            assert lib.evict(s, sink, window) == ref.evict(s, sink, window)
         elif op == 3:
             s, n = int(rng.choice(live)), int(rng.integers(0, 3 * bs))
             try:
@@ -270,6 +333,7 @@ def test_library_manager_rejects_bad_calls():
         pa.BlockManager(4, 0)
     lib.add(1)
     for call in (lambda: lib.add(1), lambda: lib.fork(9, 2), lambda: lib.fork(1, 1), lambda: lib.free(9),
+                 lambda: lib.evict(9, 4, 4), lambda: lib.evict(1, -1, 4), lambda: lib.evict(1, 4, -1),
                  lambda: lib.append(9, 1), lambda: lib.append_batch([1, 1], [1, 1]),
                  lambda: lib.append_batch([1], [-1]), lambda: lib.tables([9], 4)):
         with pytest.raises(pa.PagedAttentionError) as e:

@@ -97,3 +97,67 @@ def test_parallel_sampling_stream_through_the_block_manager():
     live = [b for b in range(nb) if ref.refcount[b] > 0]
     assert np.array_equal(torch_to_bytes(kc).reshape(nb, -1)[live], okc.reshape(nb, -1).view(np.uint8)[live])
     assert np.array_equal(torch_to_bytes(vc).reshape(nb, -1)[live], ovc.reshape(nb, -1).view(np.uint8)[live])
+
+
+def test_sink_window_eviction_stream_decodes_over_the_kept_positions():
+    """Decode steps through pa_decode_append on tables kept by the library's
+    manager, which evicts everything between a 4-token sink and a 40-token
+    window every few steps.  Each step's output matches oracle attention over
+    exactly the rows the oracle manager keeps, and the freed blocks are reused
+    by later appends."""
+    Hkv, G, D, bs, dt = 2, 4, 128, 16, "bf16"
+    nb = 48
+    rng = np.random.default_rng(33)
+    bm, ref = pa.BlockManager(nb, bs), RefManager(nb, bs)
+    kc = torch.full((nb, Hkv, bs, D), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    vc = kc.clone()
+    seqs = [0, 1, 2]
+    rows = {}
+    for s, n in zip(seqs, (70, 130, 21)):
+        bm.add(s)
+        ref.add(s)
+        k = W.to_storage(rng.standard_normal((n, Hkv, D), dtype=np.float32), dt)
+        v = W.to_storage(rng.standard_normal((n, Hkv, D), dtype=np.float32), dt)
+        slots, _ = bm.append(s, n)
+        assert [int(x) for x in slots] == ref.append(s, n)[0]
+        pa.reshape_and_cache(storage_to_torch(k, dt).cuda(), storage_to_torch(v, dt).cuda(), kc, vc,
+                             torch.from_numpy(np.ascontiguousarray(slots)).cuda())
+        rows[s] = (k, v)
+    ws = None
+    for step in range(40):
+        if step % 5 == 0:
+            for s in seqs:
+                d = bm.evict(s, 4, 40)
+                assert d == ref.evict(s, 4, 40)
+                # the oracle manager's kept rows: drop the whole blocks it released
+                keep = np.ones(len(rows[s][0]), bool)
+                if d:
+                    first = (4 + bs - 1) // bs * bs
+                    keep[first:first + d] = False
+                rows[s] = (rows[s][0][keep], rows[s][1][keep])
+                assert bm.length(s) == ref.length(s) == len(rows[s][0])
+        slots, pairs = bm.append_batch(seqs, [1] * len(seqs))
+        assert len(pairs) == 0
+        new_k = W.to_storage(rng.standard_normal((len(seqs), Hkv, D), dtype=np.float32), dt)
+        new_v = W.to_storage(rng.standard_normal((len(seqs), Hkv, D), dtype=np.float32), dt)
+        ref.append_batch(seqs, [1] * len(seqs))
+        for i, s in enumerate(seqs):
+            rows[s] = (np.concatenate([rows[s][0], new_k[i:i + 1]]), np.concatenate([rows[s][1], new_v[i:i + 1]]))
+        width = max(len(bm.table(s)) for s in seqs)
+        tables, lens = bm.tables(seqs, width)
+        q = W.to_storage(rng.standard_normal((len(seqs), Hkv * G, D), dtype=np.float32), dt)
+        out = pa.decode_append(storage_to_torch(q, dt).cuda(), kc, vc, storage_to_torch(new_k, dt).cuda(),
+                               storage_to_torch(new_v, dt).cuda(), torch.from_numpy(tables).cuda(),
+                               torch.from_numpy(lens).cuda(), 1.0 / np.sqrt(D), out_dtype=torch.float32,
+                               workspace=ws).cpu().numpy()
+        ref_out = np.stack([O.attend(O.widen(q[i], dt), O.widen(rows[s][0], dt), O.widen(rows[s][1], dt),
+                                     1.0 / np.sqrt(D), G) for i, s in enumerate(seqs)])
+        ma, rel = errors(out, ref_out)
+        if step % 10 == 0:
+            log(f"[sink+window step {step}] lens={list(lens)} max_abs={ma:.2e} rel_l2={rel:.2e}")
+        assert ma <= 2e-3 and rel <= 1e-3
+    # right after an eviction a table holds the sink block and the window's
+    # blocks: ceil(40 / 16) of them, one more when the window starts mid-block
+    for s in seqs:
+        bm.evict(s, 4, 40)
+        assert len(bm.table(s)) <= 1 + (40 + bs - 1) // bs + 1

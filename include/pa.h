@@ -170,6 +170,40 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * runs first.  Errors are those of pa_decode and pa_reshape_and_cache; a
  * call that fails has no effect.
  */
+/*
+ * Several query tokens per sequence over the same paged cache: the tokens of
+ * a chunked prefill, or the draft tokens a speculative decoder verifies
+ * ("Paged Attention and Memory Efficiency ...", section "How vLLM turned
+ * PagedAttention into a production serving engine": batched speculative
+ * decoding and prefill next to decode; "PagedAttention in Production",
+ * section "Deployment Architecture", "Inference Service Layer": a scheduling
+ * strategy for the prefill and decode phases).  The n = query_start[s + 1] - query_start[s] queries of sequence s
+ * are its last n positions (their K/V rows are in the cache already, with
+ * context_lens[s] = L counting them), and query j of them sees positions
+ * 0 .. L - n + j (causal within the chunk):
+ *   out[query_start[s] + j, i, :] = sum_{t <= L-n+j} softmax_t(scale * q.K[t]) V[t]
+ * with the head mapping, dtypes and scales of pa_decode.
+ *   q, out         [total_queries, num_kv_heads*gqa_group, head_dim]
+ *   query_start    [B + 1] int32 device array, non-decreasing, query_start[0] = 0,
+ *                  query_start[B] = total_queries; 0 <= n <= min(max_queries, L)
+ *                  (n larger than that is cut to it; a range outside the rows
+ *                  is dropped: device-side contract)
+ *   max_queries    host-side bound of n, 1 .. 1024; n = 1 everywhere is pa_decode
+ *   workspace      at least pa_decode_multi_workspace_size(B, num_kv_heads,
+ *                  gqa_group, head_dim, block_size, max_context_len, max_queries) bytes
+ * The kernel is the MFMA one, its 16 columns being (query, head) pairs, for
+ * every group size.
+ */
+size_t pa_decode_multi_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                                      int32_t block_size, int32_t max_context_len, int32_t max_queries);
+pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                          int32_t B, int32_t total_queries, int32_t max_queries, int32_t num_kv_heads,
+                          int32_t gqa_group, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t max_context_len, float scale, float k_scale,
+                          float v_scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                          void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
 pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, const void* key,
                            const void* value, pa_dtype src_dtype, const int32_t* block_tables,
                            const int32_t* context_lens, int32_t B, int32_t num_kv_heads, int32_t gqa_group,

@@ -59,3 +59,9 @@ def decode(w, kc, vc, seqs=None, q=None):
     q = w.query() if q is None else q
     return O.decode(q, kc, vc, w.block_tables, w.context_lens, w.scale, w.group, w.cache_dtype,
                     w.q_dtype, w.k_scale, w.v_scale, seqs=seqs)
+
+
+def decode_multi(w, kc, vc, seqs=None):
+    """Oracle output [T, Hq, D] of a workload with several queries per sequence."""
+    return O.decode_multi(w.query(), kc, vc, w.block_tables, w.context_lens, w.query_start, w.scale, w.group,
+                          w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale, seqs=seqs)

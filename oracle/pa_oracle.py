@@ -271,6 +271,34 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, group:
     return np.stack(out) if out else np.zeros((0,) + q.shape[1:])
 
 
+def decode_multi(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float, group: int,
+                 cache_dtype: str, q_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0,
+                 seqs=None) -> np.ndarray:
+    """Several query tokens per sequence, each seeing what a decode step at its
+    own position would see ("Paged Attention and Memory Efficiency in
+    Production LLM Serving", section "How vLLM turned PagedAttention into a
+    production serving engine": speculative decoding and prefill run over the
+    same paged cache).  Sequence s owns q rows query_start[s] .. query_start[s+1]-1,
+    its last n positions; query j of them attends over positions
+    0 .. L - n + j, i.e. the sequence cut just after its own position.
+    Returns fp64 [T, Hq, D] (rows of sequences not in ``seqs`` stay zero)."""
+    q = np.asarray(q)
+    qs = np.asarray(query_start, np.int64)
+    out = np.zeros(q.shape, np.float64)
+    for s in (range(len(context_lens)) if seqs is None else seqs):
+        L = int(context_lens[s])
+        a, b = int(qs[s]), int(qs[s + 1])
+        n = b - a
+        if n == 0:
+            continue
+        k = widen(gather_kv(k_cache, block_tables[s], L), cache_dtype, k_scale)
+        v = widen(gather_kv(v_cache, block_tables[s], L), cache_dtype, v_scale)
+        for j in range(n):
+            seen = L - n + j + 1  # positions 0 .. L - n + j
+            out[a + j] = attend(widen(q[a + j], q_dtype), k[:seen], v[:seen], scale, group)
+    return out
+
+
 def decode_contiguous(q, keys, values, scale: float, group: int, cache_dtype: str, q_dtype: str,
                       k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
     """The same attention over per-sequence contiguous arrays (no paging):

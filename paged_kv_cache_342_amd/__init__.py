@@ -52,6 +52,11 @@ def library() -> ctypes.CDLL:
     lib.pa_decode_append.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32,
                                      f32, f32, i32, i32, i32, p, sz, p]
     lib.pa_decode_append.restype = ctypes.c_int
+    lib.pa_decode_multi_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_multi_workspace_size.restype = sz
+    lib.pa_decode_multi.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32, f32, f32,
+                                    f32, i32, i32, i32, p, sz, p]
+    lib.pa_decode_multi.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, p]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
@@ -200,6 +205,51 @@ def decode_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _check(library().pa_decode_append(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _TORCH_CODE.get(key.dtype, -9),
         _ptr(block_tables), _ptr(context_lens), B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
+        _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
+        _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def decode_multi_workspace_size(B: int, num_kv_heads: int, group: int, head_dim: int, block_size: int,
+                                max_context_len: int, max_queries: int) -> int:
+    return int(library().pa_decode_multi_workspace_size(B, num_kv_heads, group, head_dim, block_size,
+                                                        max_context_len, max_queries))
+
+
+def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, query_start: torch.Tensor, max_queries: int, scale: float,
+                 max_context_len: Optional[int] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                 out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Several queries per sequence: q [T, Hq, D], sequence s owning rows query_start[s] ..
+    query_start[s+1]-1 (int32 [B+1] on the device), its last positions, causal within them.
+    max_queries: host-side bound of queries per sequence.  Returns out [T, Hq, D]."""
+    _require(q, "q")
+    _require(k_cache, "k_cache")
+    _require(v_cache, "v_cache")
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    _require(query_start, "query_start", torch.int32)
+    T, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or Hq % Hkv:
+        raise ValueError("q, k_cache and v_cache shapes do not agree")
+    B = context_lens.shape[0]
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start.shape != (B + 1,):
+        raise ValueError("block_tables must be [B, M], context_lens [B] and query_start [B + 1]")
+    M = block_tables.shape[1]
+    mcl = M * bs if max_context_len is None else int(max_context_len)
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _require(out, "out")
+    need = decode_multi_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl, max_queries) if B else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_decode_multi(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(query_start),
+        B, T, int(max_queries), Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
         _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
         _ptr(workspace), ws_bytes, _stream(q)))
     return out

@@ -65,7 +65,22 @@ struct DecodeArgs {
   // the cache, so nothing in the launch reads a slot written by it.
   const uint8_t* new_k;
   const uint8_t* new_v;
+  // Several queries per sequence (multi-query kernels only): the queries of
+  // sequence s are rows q_start[s] .. q_start[s + 1] - 1 of q and out, at
+  // most nq of them; query j of n sees positions 0 .. L - n + j.  Decode
+  // kernels have nq == 1 and row s.
+  const int32_t* q_start;
+  int32_t nq;
+  int32_t q_rows;  // rows of q and out (a query range outside them is dropped)
 };
+
+// Queries of sequence s under MQ: first row and count, clamped to at most nq,
+// at most the sequence's length and to rows that exist.
+__device__ __forceinline__ void query_range(const DecodeArgs& a, int s, int L, int& row0, int& n) {
+  row0 = a.q_start[s];
+  n = max(0, min(a.q_start[s + 1] - row0, min(a.nq, L)));
+  if (row0 < 0 || row0 > a.q_rows - n) n = 0, row0 = 0;
+}
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -242,10 +257,11 @@ struct IdRing {
   }
 };
 
-// Store n consecutive outputs of (s, head) starting at d0.
-__device__ __forceinline__ void store_out(const DecodeArgs& a, int s, int head, int D, int d0,
+// Store n consecutive outputs of output row `orow` (the sequence for decode,
+// the query token otherwise), query head `head`, starting at d0.
+__device__ __forceinline__ void store_out(const DecodeArgs& a, int orow, int head, int D, int d0,
                                           const float* v, int n) {
-  const int64_t base = ((int64_t)s * a.Hkv * a.G + head) * D + d0;
+  const int64_t base = ((int64_t)orow * a.Hkv * a.G + head) * D + d0;
   if (a.out_dtype == 0) {
     float* o = reinterpret_cast<float*>(a.out) + base;
     for (int i = 0; i < n; i += 4) *reinterpret_cast<f32x4*>(o + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
@@ -265,9 +281,10 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int s, int head, 
   }
 }
 
-// workspace row of the partial of sequence s from slice k, query head `head`
-__device__ __forceinline__ int64_t part_row(const DecodeArgs& a, int k, int s, int head) {
-  return (int64_t)(k + s) * a.Hkv * a.G + head;
+// workspace row of the partial of sequence s from slice k, for its query j
+// and query head `head`
+__device__ __forceinline__ int64_t part_row(const DecodeArgs& a, int k, int s, int j, int head) {
+  return ((int64_t)(k + s) * a.nq + j) * a.Hkv * a.G + head;
 }
 
 __device__ __forceinline__ void store_partial(const DecodeArgs& a, int64_t row, int D, int d0,

@@ -10,7 +10,7 @@
 
 namespace pa {
 
-bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, dim3 grid,
+bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query, dim3 grid,
                         hipStream_t stream);
 bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, int group,
                         dim3 grid, hipStream_t stream);
@@ -20,12 +20,14 @@ bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
 // query head of the group, in slice order, with an online rescale:
 //   M = max_k m_k;  out = v_scale * sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
 // Thread j handles four consecutive outputs of one query head, so all heads
-// of the group are merged at once, and the loads of up to kMergeUnroll
-// pieces are issued before any of them is used.  Sequences that are whole in
-// one slice were written by the decode kernel and are skipped here.
+// of the group (and, with several queries per sequence, all its queries) are
+// merged at once, and the loads of up to kMergeUnroll pieces are issued
+// before any of them is used.  Sequences that are whole in one slice were
+// written by the decode kernel and are skipped here.  Under MQ a piece whose
+// positions all lie past what a query sees holds m = -inf and is skipped.
 constexpr int kMergeUnroll = 8;
 
-template <int D>
+template <int D, bool MQ>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   constexpr int LPH = D / 4;  // threads per head
   const int h = blockIdx.x;
@@ -41,9 +43,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   const int kl = min((ce - 1) / S, neff - 1);
   if (kl <= kf) return;
   const int np = kl - kf + 1;
-  for (int idx = threadIdx.x; idx < a.G * LPH; idx += blockDim.x) {
-    const int i = idx / LPH;
-    const int d = 4 * (idx - i * LPH);
+  int qrow0 = s, nqs = 1;
+  if constexpr (MQ) query_range(a, s, L, qrow0, nqs);
+  for (int idx = threadIdx.x; idx < nqs * a.G * LPH; idx += blockDim.x) {
+    const int jq = MQ ? idx / (a.G * LPH) : 0;
+    const int rem = idx - jq * a.G * LPH;
+    const int i = rem / LPH;
+    const int d = 4 * (rem - i * LPH);
     const int head = h * a.G + i;
     float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
@@ -53,13 +59,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
         const int p = min(p0 + u, np - 1);
-        const int64_t row = part_row(a, kf + p, s, head);
+        const int64_t row = part_row(a, kf + p, s, jq, head);
         ml[u] = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * row);
         x[u] = *reinterpret_cast<const f32x4*>(a.part_acc + row * D + d);
       }
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
-        if (p0 + u < np) {
+        if (p0 + u < np && (!MQ || ml[u][0] > -INFINITY)) {
           const float Mn = fmaxf(M, ml[u][0]);
           const float ca = fast_exp2(M - Mn);
           const float cb = fast_exp2(ml[u][0] - Mn);
@@ -71,7 +77,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     }
     const float f = a.v_scale / den;
     const float v[4] = {num[0] * f, num[1] * f, num[2] * f, num[3] * f};
-    store_out(a, s, head, D, d, v, 4);
+    store_out(a, qrow0 + jq, head, D, d, v, 4);
   }
 }
 
@@ -103,7 +109,7 @@ static int waves_per_cu() {
   return n >= 1 && n <= 32 ? n : 4;
 }
 
-DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu) {
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq) {
   (void)bs;
   DecodePlan p{};
   const int64_t waves = (int64_t)waves_per_cu() * num_cu;
@@ -114,7 +120,7 @@ DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int he
   const int64_t chunks = ((int64_t)std::max(max_ctx, 1) + kChunk - 1) / kChunk + p.seg_cost;
   int64_t sub = std::min<int64_t>(kScanMax, INT_MAX / chunks);
   p.sub_batch = (int)std::max<int64_t>(1, std::min<int64_t>(sub, std::max(B, 1)));
-  const size_t Hq = (size_t)Hkv * G;
+  const size_t Hq = (size_t)Hkv * G * std::max(nq, 1);  // partial rows per (slice, sequence)
   const size_t rows = (size_t)p.nslices + p.sub_batch;
   p.meta_off = 0;
   p.ml_off = align256(sizeof(int32_t) * (3 + (size_t)p.sub_batch));
@@ -138,14 +144,16 @@ bool decode_valu_supported(int ct, int qt, int D, int bs, int G) { return valu_s
 static int elem_size(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
 
 pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
-  const bool valu = decode_uses_valu(decode_variant_override(), r.G);
+  const bool mq = r.q_start != nullptr;  // several queries per sequence: MFMA kernel only
+  const int nq = mq ? r.nq : 1;
+  const bool valu = !mq && decode_uses_valu(decode_variant_override(), r.G);
   if (valu && !valu_supports(r.cache_dtype, r.q_dtype, r.D, r.bs, r.G)) {
     set_error("pa_decode: the VALU kernel is not built for group %d, head_dim %d, block size %d",
               r.G, r.D, r.bs);
     return PA_ERR_UNSUPPORTED;
   }
-  const int tiles = valu ? 1 : (r.G + 15) / 16;
-  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count());
+  const int tiles = valu ? 1 : (int)(((int64_t)nq * r.G + 15) / 16);
+  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq);
   if (r.workspace_bytes < plan.bytes) {
     set_error("pa_decode: workspace of %zu bytes needed, %zu given", plan.bytes, r.workspace_bytes);
     return PA_ERR_WORKSPACE;
@@ -187,6 +195,8 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const bool fp8 = r.cache_dtype == PA_FP8_E4M3;
   a.qk_scale_log2 = r.scale * (fp8 ? r.k_scale : 1.f) * 1.4426950408889634f;
   a.v_scale = fp8 ? r.v_scale : 1.f;
+  a.nq = nq;
+  a.q_rows = mq ? r.q_rows : r.B;
   const int ct = r.cache_dtype, qt = r.q_dtype;
   const size_t out_row = (size_t)Hq * r.D * elem_size(r.out_dtype);
   const size_t q_row = (size_t)Hq * r.D * 2;
@@ -194,15 +204,18 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   // they share the workspace, which stream order makes safe
   for (int s0 = 0; s0 < r.B; s0 += plan.sub_batch) {
     a.B = std::min(plan.sub_batch, r.B - s0);
-    a.out = reinterpret_cast<uint8_t*>(r.out) + (size_t)s0 * out_row;
-    a.q = reinterpret_cast<const uint8_t*>(r.q) + (size_t)s0 * q_row;
+    // decode rows follow the sequences; query rows are named by q_start
+    a.out = reinterpret_cast<uint8_t*>(r.out) + (mq ? 0 : (size_t)s0 * out_row);
+    a.q = reinterpret_cast<const uint8_t*>(r.q) + (mq ? 0 : (size_t)s0 * q_row);
+    a.q_start = mq ? r.q_start + s0 : nullptr;
+    if (!mq) a.q_rows = a.B;
     a.block_tables = r.block_tables + (int64_t)s0 * r.M;
     a.context_lens = r.context_lens + s0;
     a.new_k = fused_append ? reinterpret_cast<const uint8_t*>(r.new_k) + (size_t)s0 * new_row : nullptr;
     a.new_v = fused_append ? reinterpret_cast<const uint8_t*>(r.new_v) + (size_t)s0 * new_row : nullptr;
     const dim3 grid((unsigned)grid_waves);
     const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream)
-                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, grid, stream);
+                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, grid, stream);
     if (!ok) {
       set_error("pa_decode: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d, group %d (%s)",
                 ct, qt, r.D, r.bs, r.G, valu ? "valu" : "mfma");
@@ -210,12 +223,16 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     }
     if (plan.nslices > 1) {
       const dim3 mgrid(r.Hkv, a.B);
-      const int threads = r.G * (r.D / 4);
-      const dim3 mblock(threads >= 256 ? 256 : ((threads + 63) / 64) * 64);
-      if (r.D == 64)
-        hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, mblock, 0, stream, a);
+      const int64_t threads = (int64_t)nq * r.G * (r.D / 4);
+      const dim3 mblock(threads >= 256 ? 256 : (unsigned)(((threads + 63) / 64) * 64));
+      if (r.D == 64 && !mq)
+        hipLaunchKernelGGL((decode_merge_kernel<64, false>), mgrid, mblock, 0, stream, a);
+      else if (!mq)
+        hipLaunchKernelGGL((decode_merge_kernel<128, false>), mgrid, mblock, 0, stream, a);
+      else if (r.D == 64)
+        hipLaunchKernelGGL((decode_merge_kernel<64, true>), mgrid, mblock, 0, stream, a);
       else
-        hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, mblock, 0, stream, a);
+        hipLaunchKernelGGL((decode_merge_kernel<128, true>), mgrid, mblock, 0, stream, a);
     }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {

@@ -18,6 +18,12 @@
 // none of them sits under a branch (positions past the end of a segment
 // re-read its last row and get a score of -inf).
 //
+// Several queries per sequence (MQ): the columns of a tile are (query, head)
+// pairs instead of heads -- column c is query c / G of the sequence and head
+// c % G of the group -- and each column masks the positions its query may
+// not see (past L - n + j for query j of n).  A tile none of whose columns is
+// a query of the sequence skips the segment.
+//
 // When the launch also appends each sequence's new row (16-bit caches), the
 // loads of position L - 1 read the caller's row instead of the cache, and
 // the wave that owns the sequence's last chunk stores that row into its slot
@@ -82,7 +88,7 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <class CT, class QT, int D, int BS>
+template <class CT, class QT, int D, int BS, bool MQ>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int e = CT::bytes;
   constexpr int KK = D / 32;   // MFMAs per QK tile
@@ -116,14 +122,17 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   Slice sl;
   if (!slice_setup(a, cum, lens, k, sl)) return;
 
-  const int col_head = 16 * ht + r;  // head within the group this lane's column carries
-  const bool col_ok = col_head < a.G;
-  const int head = h * a.G + col_head;
+  const int col = 16 * ht + r;                 // this lane's column
+  const int cq = MQ ? col / a.G : 0;           // its query within the sequence
+  const int col_head = MQ ? col - cq * a.G : col;  // its head within the group
+  const bool col_ok = MQ ? cq < a.nq : col < a.G;
+  const int head = h * a.G + (col_ok ? col_head : 0);
   const uint8_t* kbase = a.k_cache + (int64_t)h * kChunkBytes;
   const uint8_t* vbase = a.v_cache + (int64_t)h * kChunkBytes;
 
-  // empty contexts in this slice: zero rows, written by the slice that owns them
-  for (int s = sl.s_first; s < a.B; ++s) {
+  // empty contexts in this slice: zero rows, written by the slice that owns
+  // them (a sequence with no positions has no queries under MQ)
+  for (int s = sl.s_first; s < a.B && !MQ; ++s) {
     const int cs = cum[s], ce = cum[s + 1];
     if (past_slice(sl, cs, ce)) break;
     if (lens[s] == 0 && col_ok) {
@@ -148,15 +157,28 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const uint8_t* last_v;
     int lim;                // positions from lim on read last_k / last_v
     int64_t tail_off;       // cache offset the appended row goes to; -1 = none
+    int qrow0;              // row of the sequence's first query
+    int nqs;                // its queries (1 for decode)
   };
   auto load_header = [&](const Segment& g, Header& hd) {
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) +
-                          ((int64_t)g.s * Hq + (col_ok ? head : h * a.G)) * D * 2;
+    hd.qrow0 = g.s;
+    hd.nqs = 1;
+    if constexpr (MQ) {
+      int row0, n;
+      query_range(a, g.s, lens[g.s], row0, n);
+      hd.qrow0 = uniform(row0);
+      hd.nqs = uniform(n);
+    }
+    // a column that is no query of the sequence reads a row that exists
+    // (row 0) and contributes zeros
+    const bool live = MQ ? cq < hd.nqs : col_ok;
+    const int64_t qr = MQ ? (live ? hd.qrow0 + cq : 0) : g.s;
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + (qr * Hq + (live ? head : h * a.G)) * D * 2;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       const int d = kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
       const i32x4 x = ld16(qrow + d * 2);
-      hd.qop[kk] = col_ok ? x : i32x4{0, 0, 0, 0};
+      hd.qop[kk] = live ? x : i32x4{0, 0, 0, 0};
     }
     const int32_t* trow = a.block_tables + (int64_t)g.s * a.M;
     const int blk0 = g.tok0 / BS;
@@ -187,6 +209,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const i32x4* qop = hc.qop;
     IdRing<BS>& ring = hc.ring;
     const int lim = hc.lim;
+    const bool live = MQ ? cq < hc.nqs : col_ok;
+    const int qlim = MQ ? lens[s] - hc.nqs + cq : 0;  // last position this column's query sees
     // the appended row, stored at the end of the segment: lane i < kRowLanes
     // holds 16 bytes of K, the next kRowLanes lanes 16 bytes of V
     i32x4 app_row = {0, 0, 0, 0};
@@ -264,14 +288,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       for (int j = 0; j < 8; ++j) {
         const float raw_s = (j < 4 ? s0[j & 3] : s1[j & 3]) * a.qk_scale_log2;
         const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
-        sc[j] = ctok + tc < tok_end ? raw_s : -INFINITY;
+        const bool seen = ctok + tc < tok_end && (!MQ || ctok + tc <= qlim);
+        sc[j] = seen ? raw_s : -INFINITY;
         mx = fmaxf(mx, sc[j]);
       }
       if (wave_any(mx > m + kRescaleThreshold)) {
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
         const float mn = fmaxf(m, mx);
-        const float alpha = fast_exp2(m - mn);
+        // under MQ a column may have seen no position yet (mn = -inf)
+        const float alpha = (MQ && mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
 #pragma unroll
         for (int i = 0; i < W; ++i) acc[i] *= alpha;
         l *= alpha;
@@ -280,7 +306,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = fast_exp2(sc[j] - m);
+        p[j] = (MQ && sc[j] == -INFINITY) ? 0.f : fast_exp2(sc[j] - m);
         l += p[j];
       }
       // ---- P as the B operand of PV
@@ -330,8 +356,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     // caches, whose chunk is half the bytes) in flight while one is computed,
     // so a wave keeps ~16 KiB requested.  Later chunks are always requested
     // (past the end every lane reads the last row), so no load sits under a
-    // branch and each wait covers only the chunk it needs.
-    if constexpr (!kFp8) {
+    // branch and each wait covers only the chunk it needs.  (Under MQ a tile
+    // with no query of this sequence among its columns skips the segment.)
+    if (MQ && 16 * ht >= hc.nqs * a.G) {
+    } else if constexpr (!kFp8) {
       Raw buf0, buf1;
       load_chunk(0, buf0);
       for (int c = 0; c < nchunks; c += 2) {
@@ -363,10 +391,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- epilogue: the lane holds head col_head, d = 4W*gq + W*jj + dt
+    // ---- epilogue: the lane holds head col_head (of query cq), d = 4W*gq + W*jj + dt
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
-    if (col_ok) {
+    if (live) {
       float v[4 * W];
       const bool whole = whole_sequence(sl, cs, ce);
       const float f = whole ? a.v_scale / l : 1.f;
@@ -375,9 +403,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int dt = 0; dt < W; ++dt) v[W * jj + dt] = acc[dt][jj] * f;
       if (whole) {
-        store_out(a, s, head, D, 4 * W * gq, v, 4 * W);
+        store_out(a, MQ ? hc.qrow0 + cq : s, head, D, 4 * W * gq, v, 4 * W);
       } else {
-        const int64_t row = part_row(a, sl.k, s, head);
+        const int64_t row = part_row(a, sl.k, s, cq, head);
         store_partial(a, row, D, 4 * W * gq, v, 4 * W);
         if (gq == 0) store_ml(a, row, m, l);
       }
@@ -395,10 +423,13 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-#define PA_MFMA_CASE(CT, QT, D, BS)                                                    \
-  if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS) {                 \
-    hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS>), grid, dim3(64), 0, stream, a); \
-    return true;                                                                       \
+#define PA_MFMA_CASE(CT, QT, D, BS)                                                            \
+  if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS) {                         \
+    if (multi_query)                                                                           \
+      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true>), grid, dim3(64), 0, stream, a); \
+    else                                                                                       \
+      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, false>), grid, dim3(64), 0, stream, a); \
+    return true;                                                                               \
   }
 
 #define PA_MFMA_BS(CT, QT, D) \
@@ -406,7 +437,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   PA_MFMA_CASE(CT, QT, D, 16) \
   PA_MFMA_CASE(CT, QT, D, 32)
 
-bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, dim3 grid,
+bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query, dim3 grid,
                         hipStream_t stream) {
   PA_MFMA_BS(F16, F16, 64)
   PA_MFMA_BS(F16, F16, 128)

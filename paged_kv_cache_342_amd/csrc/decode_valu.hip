@@ -308,7 +308,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
       for (int j = 0; j < 32; ++j) acc[i][j] = row_sum(acc[i][j]);
       if (row == 0) {
         const float f = whole ? a.v_scale / lt : 1.f;
-        const int64_t prow = part_row(a, sl.k, s, head0 + i);
+        const int64_t prow = part_row(a, sl.k, s, 0, head0 + i);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           float v[EPU];

@@ -20,10 +20,14 @@ struct DecodePlan {
   size_t meta_off, ml_off, acc_off, bytes;  // workspace layout
 };
 
+// most queries per sequence pa_decode_multi takes
+constexpr int kMaxQueries = 1024;
+
 // compute units of the current device (cached per device)
 int device_cu_count();
 
-DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu);
+// nq: queries per sequence at most (1 for decode); partial rows scale with it
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq);
 
 struct DecodeRequest {
   void* out;
@@ -45,6 +49,11 @@ struct DecodeRequest {
   const void* new_k;
   const void* new_v;
   int src_dtype;
+  // several queries per sequence: rows q_start[s] .. q_start[s+1]-1 of q and
+  // out ([q_rows, Hq, D]), at most nq per sequence; null = one per sequence
+  const int32_t* q_start;
+  int nq;
+  int q_rows;
 };
 
 // 0 = default choice, 1 = VALU/DPP kernel, 2 = MFMA kernel

@@ -409,3 +409,103 @@ def test_pins_catch_planted_mistakes(mistake):
         return out
 
     assert not _pins_pass(bad)
+
+
+# ---------------------------------------------------------------- several queries per sequence
+
+def _causal_sdpa(q, k, v, scale, group):
+    """torch float64 scaled_dot_product_attention with its own causal mask
+    (is_causal: query row i sees key rows 0..i) over L queries and L keys."""
+    qt = torch.from_numpy(q).permute(1, 0, 2)  # [Hq, L, D]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale, is_causal=True).permute(1, 0, 2).numpy()
+
+
+def _multi_case(seed, lens, nqs, group=4, Hkv=2, D=32, bs=8):
+    """Pools holding each sequence's rows, plus one query row per position of
+    every sequence (so the causal routine sees the whole sequence); the
+    multi-query call takes the query rows of each sequence's last n positions."""
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    nb = int(sum((L + bs - 1) // bs for L in lens)) + 3
+    perm = rng.permutation(nb)
+    M = max((L + bs - 1) // bs for L in lens)
+    tables = np.full((B, M), -1, np.int64)
+    kc = O.new_pool(nb, Hkv, bs, D, "f16")
+    vc = O.new_pool(nb, Hkv, bs, D, "f16")
+    full_q, ks, vs, off = [], [], [], 0
+    for s, L in enumerate(lens):
+        n = (L + bs - 1) // bs
+        tables[s, :n] = perm[off:off + n]
+        off += n
+        k = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        v = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        O.reshape_and_cache(k, v, kc, vc, O.slots_for(tables[s], 0, L, bs), bs, "f16")
+        full_q.append(rng.standard_normal((L, Hkv * group, D)).astype(np.float16))
+        ks.append(k)
+        vs.append(v)
+    qs = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int64)
+    q = np.concatenate([full_q[s][lens[s] - nqs[s]:] for s in range(B)])
+    return tables, kc, vc, np.array(lens), qs, q, full_q, ks, vs
+
+
+@pytest.mark.parametrize("group", [1, 4])
+def test_multi_query_matches_torch_causal_attention(group):
+    """The last n query rows of a sequence equal the last n rows of torch's
+    causal attention over the whole sequence, for n = L (a whole prefill) and
+    n < L (a chunk, or draft tokens)."""
+    lens, nqs = [1, 9, 40, 75], [1, 9, 17, 3]
+    tables, kc, vc, L, qs, q, full_q, ks, vs = _multi_case(5 + group, lens, nqs, group=group)
+    scale = 0.2
+    out = O.decode_multi(q, kc, vc, tables, L, qs, scale, group, "f16", "f16")
+    for s in range(len(lens)):
+        ref = _causal_sdpa(full_q[s].astype(np.float64), ks[s].astype(np.float64), vs[s].astype(np.float64),
+                           scale, group)[lens[s] - nqs[s]:]
+        assert np.max(np.abs(out[qs[s]:qs[s + 1]] - ref)) <= 1e-12
+
+
+def test_multi_query_with_one_query_is_decode():
+    lens, nqs = [5, 33, 64], [1, 1, 1]
+    tables, kc, vc, L, qs, q, *_ = _multi_case(9, lens, nqs)
+    out = O.decode_multi(q, kc, vc, tables, L, qs, 0.3, 4, "f16", "f16")
+    ref = O.decode(q, kc, vc, tables, L, 0.3, 4, "f16", "f16")
+    assert np.array_equal(out, ref)
+
+
+def test_multi_query_matches_brute_force():
+    """Scalar Python over the positions each query may see."""
+    lens, nqs = [6, 11], [3, 11]
+    tables, kc, vc, L, qs, q, full_q, ks, vs = _multi_case(13, lens, nqs, group=2, D=8)
+    out = O.decode_multi(q, kc, vc, tables, L, qs, 0.5, 2, "f16", "f16")
+    for s in range(len(lens)):
+        for j in range(nqs[s]):
+            seen = lens[s] - nqs[s] + j + 1
+            k = [[[float(x) for x in ks[s][t, h]] for h in range(2)] for t in range(seen)]
+            v = [[[float(x) for x in vs[s][t, h]] for h in range(2)] for t in range(seen)]
+            ref = np.array(_brute_force([[float(x) for x in row] for row in q[qs[s] + j]], k, v, 0.5, 2))
+            assert np.max(np.abs(out[qs[s] + j] - ref)) <= 1e-13
+
+
+@pytest.mark.parametrize("mistake", ["mask_off_by_one", "mask_from_chunk_start", "row_by_sequence"])
+def test_multi_query_pins_catch_planted_mistakes(mistake):
+    def bad(q, kc, vc, tables, L, qs, scale, group, cd, qd):
+        out = np.zeros(q.shape)
+        for s in range(len(L)):
+            a, b = int(qs[s]), int(qs[s + 1])
+            n = b - a
+            k = O.widen(O.gather_kv(kc, tables[s], int(L[s])), cd)
+            v = O.widen(O.gather_kv(vc, tables[s], int(L[s])), cd)
+            for j in range(n):
+                seen = {"mask_off_by_one": L[s] - n + j, "mask_from_chunk_start": j + 1}.get(mistake, L[s] - n + j + 1)
+                row = s + j if mistake == "row_by_sequence" else a + j
+                out[a + j] = O.attend(O.widen(q[row], qd), k[:max(int(seen), 1)], v[:max(int(seen), 1)], scale, group)
+        return out
+
+    lens, nqs = [1, 9, 40, 75], [1, 9, 17, 3]
+    tables, kc, vc, L, qs, q, full_q, ks, vs = _multi_case(5, lens, nqs)
+    got = bad(q, kc, vc, tables, L, qs, 0.2, 4, "f16", "f16")
+    ok = all(np.max(np.abs(got[qs[s]:qs[s + 1]] - _causal_sdpa(full_q[s].astype(np.float64), ks[s].astype(np.float64),
+                                                                 vs[s].astype(np.float64), 0.2, 4)[lens[s] - nqs[s]:]))
+             <= 1e-12 for s in range(len(lens)))
+    assert not ok

@@ -98,6 +98,9 @@ class Workload:
     _kv: Callable[[int], Tuple[np.ndarray, np.ndarray]] = field(repr=False, default=None)
     _q: Callable[[], np.ndarray] = field(repr=False, default=None)
     meta: dict = field(default_factory=dict)
+    # several queries per sequence: sequence s owns query rows
+    # query_start[s] .. query_start[s+1]-1, its last positions (None = one each)
+    query_start: Optional[np.ndarray] = None
 
     @property
     def group(self) -> int:
@@ -116,8 +119,12 @@ class Workload:
         return self._kv(s)
 
     def query(self) -> np.ndarray:
-        """Decode queries [B, Hq, D] in q_dtype storage."""
+        """Queries in q_dtype storage: [B, Hq, D], or [T, Hq, D] with several per sequence."""
         return self._q()
+
+    @property
+    def max_queries(self) -> int:
+        return int(np.diff(self.query_start).max()) if self.query_start is not None and self.B else 1
 
     def kv_bytes(self) -> int:
         """Bytes of K and V the decode batch attends over (each row once per KV head)."""
@@ -332,6 +339,37 @@ def custom(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, bs: int, cache
         w.k_scale = float(np.float32(kmax) / np.float32(448.0))
         w.v_scale = float(np.float32(vmax) / np.float32(448.0))
     return w
+
+
+def multi_query(name: str, seed: int, lens, nqs, Hq: int, Hkv: int, D: int, bs: int, cache_dtype: str,
+                q_dtype: Optional[str] = None) -> Workload:
+    """Sequences whose last nqs[s] positions are queries (a chunk of a chunked
+    prefill, or draft tokens to verify); the cache holds all of every
+    sequence's rows, the chunk's included.  Queries are N(0,1) rows of its own
+    stream, one per query token."""
+    w = custom(name, seed, lens, Hq, Hkv, D, bs, cache_dtype, q_dtype)
+    nqs = np.asarray(nqs, np.int64)
+    assert len(nqs) == w.B and (nqs >= 0).all() and (nqs <= w.context_lens).all()
+    w.query_start = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32)
+    T = int(w.query_start[-1])
+    qd = w.q_dtype
+    w._q = lambda: to_storage(_rng(seed, _Q, 7).standard_normal((T, Hq, D), dtype=np.float32), qd)
+    return w
+
+
+def spec_decode(seed: int = 3426, B: int = 64, draft: int = 4) -> Workload:
+    """Speculative verification on the 8B-shaped layer: the 8B-shaped lengths,
+    each sequence verifying `draft` tokens (its last positions)."""
+    base = llama8b(B=B)
+    w = multi_query("spec_decode", seed, base.context_lens, [draft] * B, 32, 8, 128, 16, "bf16")
+    return w
+
+
+def chunked_prefill(seed: int = 3427, B: int = 16, chunk: int = 64) -> Workload:
+    """Chunked prefill on the 8B-shaped layer: contexts U{512..4096} whose last
+    `chunk` positions are this step's queries."""
+    lens = _rng(seed, _LENS).integers(512, 4096, size=B, endpoint=True)
+    return multi_query("chunked_prefill", seed, lens, [chunk] * B, 32, 8, 128, 16, "bf16")
 
 
 CONFIGS = {

@@ -114,6 +114,14 @@ class DeviceBatch:
         return pa.decode_append(self.q, self.kc, self.vc, k_new, v_new, self.tables, self.lens, w.scale,
                                 k_scale=w.k_scale, v_scale=w.v_scale, out_dtype=out_dtype, **kw)
 
+    def decode_multi(self, out_dtype=torch.float32, **kw):
+        """pa.decode_multi over the workload's queries (several per sequence)."""
+        w = self.w
+        kw.setdefault("max_context_len", w.max_context_len if w.B else 1)
+        qs = torch.from_numpy(np.ascontiguousarray(w.query_start)).to(self.device)
+        return pa.decode_multi(self.q, self.kc, self.vc, self.tables, self.lens, qs, w.max_queries, w.scale,
+                               k_scale=w.k_scale, v_scale=w.v_scale, out_dtype=out_dtype, **kw)
+
     def decode(self, out_dtype=torch.float32, **kw):
         w = self.w
         kw.setdefault("max_context_len", w.max_context_len if w.B else 1)

@@ -36,6 +36,9 @@ namespace pa {
 
 constexpr int kChunk = 32;        // positions per chunk, the unit of the split
 constexpr int kScanMax = 4096;    // sequences one launch scans in LDS
+// with several queries per sequence the first query rows are kept in LDS as
+// well; three arrays of this many entries leave room for four waves per CU
+constexpr int kScanMaxMQ = 3072;
 constexpr int kIdAhead = 6;       // chunks of block ids held ahead of the loads
 
 struct DecodeArgs {
@@ -74,11 +77,12 @@ struct DecodeArgs {
   int32_t q_rows;  // rows of q and out (a query range outside them is dropped)
 };
 
-// Queries of sequence s under MQ: first row and count, clamped to at most nq,
-// at most the sequence's length and to rows that exist.
-__device__ __forceinline__ void query_range(const DecodeArgs& a, int s, int L, int& row0, int& n) {
-  row0 = a.q_start[s];
-  n = max(0, min(a.q_start[s + 1] - row0, min(a.nq, L)));
+// Queries of sequence s under MQ (qs = q_start, in memory or in LDS): first
+// row and count, clamped to at most nq, at most the sequence's length and to
+// rows that exist.
+__device__ __forceinline__ void query_range(const DecodeArgs& a, const int* qs, int s, int L, int& row0, int& n) {
+  row0 = qs[s];
+  n = max(0, min(qs[s + 1] - row0, min(a.nq, L)));
   if (row0 < 0 || row0 > a.q_rows - n) n = 0, row0 = 0;
 }
 
@@ -112,12 +116,14 @@ struct Slice {
   int s_first;  // first sequence it visits
 };
 
-// Fills cum[], lens[] (clamped context lengths) and sl; returns false when
+// Fills cum[], lens[] (clamped context lengths), qrow[] (q_start, when
+// several queries per sequence; null otherwise) and sl; returns false when
 // the slice holds nothing.  Wave 0 also publishes S, the slice count and
 // cum[] for the merge kernel.
-__device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int* lens, int k, Slice& sl) {
+__device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int* lens, int* qrow, int k, Slice& sl) {
   const int lane = __lane_id();
   int carry = 0;
+  if (qrow != nullptr && lane == 0) qrow[a.B] = a.q_start[a.B];
   for (int base = 0; base < a.B; base += 64) {
     const int s = base + lane;
     int n = 0;
@@ -125,6 +131,7 @@ __device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int* 
       int L = a.context_lens[s];
       L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
       lens[s] = L;
+      if (qrow != nullptr) qrow[s] = a.q_start[s];
       n = L > 0 ? (L + kChunk - 1) / kChunk + a.seg_cost : 0;
     }
     const int inc = wave_inclusive_sum(n);

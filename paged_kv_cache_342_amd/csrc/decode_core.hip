@@ -16,8 +16,10 @@ bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int b
                         dim3 grid, hipStream_t stream);
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
 
-// One workgroup per (KV head, sequence): merge the slices' partials of every
-// query head of the group, in slice order, with an online rescale:
+// Workgroups per (KV head, sequence) -- one for decode, more when its
+// queries hold more outputs than a workgroup has threads: merge the slices'
+// partials of every query head of the group, in slice order, with an online
+// rescale:
 //   M = max_k m_k;  out = v_scale * sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
 // Thread j handles four consecutive outputs of one query head, so all heads
 // of the group (and, with several queries per sequence, all its queries) are
@@ -44,8 +46,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   if (kl <= kf) return;
   const int np = kl - kf + 1;
   int qrow0 = s, nqs = 1;
-  if constexpr (MQ) query_range(a, s, L, qrow0, nqs);
-  for (int idx = threadIdx.x; idx < nqs * a.G * LPH; idx += blockDim.x) {
+  if constexpr (MQ) query_range(a, a.q_start, s, L, qrow0, nqs);
+  for (int idx = blockIdx.z * blockDim.x + threadIdx.x; idx < nqs * a.G * LPH; idx += gridDim.z * blockDim.x) {
     const int jq = MQ ? idx / (a.G * LPH) : 0;
     const int rem = idx - jq * a.G * LPH;
     const int i = rem / LPH;
@@ -109,7 +111,8 @@ static int waves_per_cu() {
   return n >= 1 && n <= 32 ? n : 4;
 }
 
-DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq) {
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq,
+                       bool multi_query) {
   (void)bs;
   DecodePlan p{};
   const int64_t waves = (int64_t)waves_per_cu() * num_cu;
@@ -118,7 +121,7 @@ DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int he
   p.min_slice = 4;
   p.seg_cost = segment_cost();
   const int64_t chunks = ((int64_t)std::max(max_ctx, 1) + kChunk - 1) / kChunk + p.seg_cost;
-  int64_t sub = std::min<int64_t>(kScanMax, INT_MAX / chunks);
+  int64_t sub = std::min<int64_t>(multi_query ? kScanMaxMQ : kScanMax, INT_MAX / chunks);
   p.sub_batch = (int)std::max<int64_t>(1, std::min<int64_t>(sub, std::max(B, 1)));
   const size_t Hq = (size_t)Hkv * G * std::max(nq, 1);  // partial rows per (slice, sequence)
   const size_t rows = (size_t)p.nslices + p.sub_batch;
@@ -153,7 +156,7 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     return PA_ERR_UNSUPPORTED;
   }
   const int tiles = valu ? 1 : (int)(((int64_t)nq * r.G + 15) / 16);
-  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq);
+  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq, mq);
   if (r.workspace_bytes < plan.bytes) {
     set_error("pa_decode: workspace of %zu bytes needed, %zu given", plan.bytes, r.workspace_bytes);
     return PA_ERR_WORKSPACE;
@@ -222,8 +225,8 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
       return PA_ERR_UNSUPPORTED;
     }
     if (plan.nslices > 1) {
-      const dim3 mgrid(r.Hkv, a.B);
       const int64_t threads = (int64_t)nq * r.G * (r.D / 4);
+      const dim3 mgrid(r.Hkv, a.B, (unsigned)std::min<int64_t>(65535, (threads + 255) / 256));
       const dim3 mblock(threads >= 256 ? 256 : (unsigned)(((threads + 63) / 64) * 64));
       if (r.D == 64 && !mq)
         hipLaunchKernelGGL((decode_merge_kernel<64, false>), mgrid, mblock, 0, stream, a);

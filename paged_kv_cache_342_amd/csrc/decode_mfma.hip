@@ -103,8 +103,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr bool kCanAppend = !kFp8;   // new rows are stored as given
   constexpr int kRowLanes = D * e / 16;  // lanes that hold one row, 16 bytes each
 
-  __shared__ int cum[kScanMax + 1];
-  __shared__ int lens[kScanMax];
+  constexpr int kScan = MQ ? kScanMaxMQ : kScanMax;
+  __shared__ int cum[kScan + 1];
+  __shared__ int lens[kScan];
+  __shared__ int qrow[MQ ? kScan + 1 : 1];
 
   const int lane = threadIdx.x;
   const int r = lane & 15;   // A-operand row / B-operand column / C column
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const int k = rest / a.head_tiles;
 
   Slice sl;
-  if (!slice_setup(a, cum, lens, k, sl)) return;
+  if (!slice_setup(a, cum, lens, MQ ? qrow : nullptr, k, sl)) return;
 
   const int col = 16 * ht + r;                 // this lane's column
   const int cq = MQ ? col / a.G : 0;           // its query within the sequence
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     hd.nqs = 1;
     if constexpr (MQ) {
       int row0, n;
-      query_range(a, g.s, lens[g.s], row0, n);
+      query_range(a, qrow, g.s, lens[g.s], row0, n);
       hd.qrow0 = uniform(row0);
       hd.nqs = uniform(n);
     }

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   const int head0 = h * G;
 
   Slice sl;
-  if (!slice_setup(a, cum, lens, k, sl)) return;
+  if (!slice_setup(a, cum, lens, nullptr, k, sl)) return;
 
   const uint8_t* kbase = a.k_cache + (int64_t)h * kChunkBytes;
   const uint8_t* vbase = a.v_cache + (int64_t)h * kChunkBytes;

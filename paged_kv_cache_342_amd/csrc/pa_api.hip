@@ -91,7 +91,8 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_gro
   if (B <= 0 || num_kv_heads <= 0 || gqa_group <= 0 || max_context_len <= 0) return 0;
   if ((head_dim != 64 && head_dim != 128) || (block_size != 8 && block_size != 16 && block_size != 32)) return 0;
   // one query-head tile per KV head gives the most slices of any kernel choice
-  return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, 1, device_cu_count(), 1).bytes;
+  return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, 1, device_cu_count(), 1,
+                     false).bytes;
 }
 
 }  // extern "C"
@@ -105,7 +106,7 @@ static pa_status decode_request(const char* fn, void* out, const void* q, const 
                                 int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
                                 int32_t max_context_len, float scale, float k_scale, float v_scale,
                                 pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
-                                size_t workspace_bytes, int nq, DecodeRequest& r) {
+                                size_t workspace_bytes, int nq, bool multi_query, DecodeRequest& r) {
   if (B < 0) return fail(PA_ERR_INVALID_ARG, "%s: B must be >= 0", fn);
   if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: at most 65535 sequences per call", fn);
   if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "%s: num_kv_heads must be >= 1 (got %d)", fn, num_kv_heads);
@@ -137,7 +138,8 @@ static pa_status decode_request(const char* fn, void* out, const void* q, const 
     return fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer argument", fn);
   const int full = max_blocks_per_seq * block_size;
   const int plan_ctx = max_context_len > 0 ? max_context_len : full;
-  const DecodePlan plan = plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx, 1, device_cu_count(), nq);
+  const DecodePlan plan = plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx, 1, device_cu_count(), nq,
+                                      multi_query);
   if (!workspace || workspace_bytes < plan.bytes)
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -183,7 +185,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const pa_status st = decode_request("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, B,
                                       num_kv_heads, gqa_group, head_dim, block_size, num_blocks,
                                       max_blocks_per_seq, max_context_len, scale, k_scale, v_scale, q_dtype,
-                                      cache_dtype, out_dtype, workspace, workspace_bytes, 1, r);
+                                      cache_dtype, out_dtype, workspace, workspace_bytes, 1, false, r);
   if (st != PA_OK || B == 0) return st;
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
@@ -201,7 +203,7 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
   const pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads,
                                       gqa_group, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                       max_context_len, scale, k_scale, v_scale, q_dtype, cache_dtype, out_dtype,
-                                      workspace, workspace_bytes, 1, r);
+                                      workspace, workspace_bytes, 1, false, r);
   if (st != PA_OK) return st;
   if (!known_dtype(src_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (cache_dtype == PA_FP8_E4M3 ? (src_dtype != PA_F16 && src_dtype != PA_BF16) : src_dtype != cache_dtype)
@@ -221,7 +223,7 @@ size_t pa_decode_multi_workspace_size(int32_t B, int32_t num_kv_heads, int32_t g
   if ((head_dim != 64 && head_dim != 128) || (block_size != 8 && block_size != 16 && block_size != 32)) return 0;
   if (max_queries > kMaxQueries) return 0;
   return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, 1, device_cu_count(),
-                     max_queries).bytes;
+                     max_queries, true).bytes;
 }
 
 pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -242,7 +244,7 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
   const pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads,
                                       gqa_group, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                       max_context_len, scale, k_scale, v_scale, q_dtype, cache_dtype, out_dtype,
-                                      workspace, workspace_bytes, max_queries, r);
+                                      workspace, workspace_bytes, max_queries, true, r);
   if (st != PA_OK) return st;
   if (B == 0 || total_queries == 0) return PA_OK;
   if (!query_start || !aligned(query_start, 4)) return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned query_start", fn);

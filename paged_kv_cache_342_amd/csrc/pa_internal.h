@@ -26,8 +26,10 @@ constexpr int kMaxQueries = 1024;
 // compute units of the current device (cached per device)
 int device_cu_count();
 
-// nq: queries per sequence at most (1 for decode); partial rows scale with it
-DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq);
+// nq: queries per sequence at most (1 for decode); partial rows scale with it.
+// multi_query: the launch uses the several-queries kernel (fewer sequences per launch).
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq,
+                       bool multi_query);
 
 struct DecodeRequest {
   void* out;

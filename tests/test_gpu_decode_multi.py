@@ -106,3 +106,14 @@ def test_multi_query_rejects_bad_arguments():
     assert e.value.status == pa.ERR_UNSUPPORTED
     with pytest.raises(ValueError):
         pa.decode_multi(g.q, g.kc, g.vc, g.tables, g.lens, qs[:2], 3, w.scale)
+
+
+def test_multi_query_more_sequences_than_one_launch_scans():
+    """3,100 sequences: more than the 3,072 a multi-query launch scans (its
+    query rows sit in LDS beside the lengths), so two launches share the call."""
+    rng = np.random.default_rng(48)
+    lens = [int(x) for x in rng.integers(0, 50, size=3100)]
+    nqs = [min(L, int(n)) for L, n in zip(lens, rng.integers(0, 4, size=3100))]
+    w = W.multi_query("mq_many_seqs", 49, lens, nqs, 4, 2, 64, 16, "f16")
+    seqs = [0, 1, 3070, 3071, 3072, 3073, 3099] + [int(i) for i in np.nonzero(np.array(nqs) > 0)[0][:5]]
+    _check_multi(w, seqs=sorted(set(seqs)))

@@ -378,6 +378,8 @@ CONFIGS = {
     "llama70b": llama70b,
     "shared_prefix": shared_prefix,
     "heavy_tail": heavy_tail,
+    "spec_decode": spec_decode,
+    "chunked_prefill": chunked_prefill,
 }
 
 

@@ -171,6 +171,36 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * call that fails has no effect.
  */
 /*
+ * FP8 cache with one scale per (slot, kv head) row ("PagedAttention - The KV
+ * Cache Problem", section "What's Still Unsolved": FP8/FP4 quantized KV
+ * caches).  pa_reshape_and_cache_scaled writes each (token, head) row as
+ * E4M3FN codes of fp32(x) / s with s = (largest |x| of the row, NaN left out)
+ * / 448 in fp32 -- 1 for a row of zeros or one holding an infinity -- and
+ * stores s at the row's place in the scale pools; the encoder is the one of
+ * pa_reshape_and_cache.  A row's scale is fixed when the row is written, so
+ * appending one token at a time never re-encodes earlier rows, and rows of
+ * very different magnitudes keep their own precision.
+ *   k_scales, v_scales [num_blocks, num_kv_heads, block_size] fp32 (device;
+ *                  4 bytes per 128-byte row at head_dim 128)
+ *   k_cache, v_cache  PA_FP8_E4M3; key, value f16 or bf16; slot_mapping as
+ *                  for pa_reshape_and_cache.
+ * pa_decode_scaled is pa_decode over such a cache: K[t, h, :] =
+ * k_scales[b, h, t % bs] * decode(k_cache[b, h, t % bs, :]) with
+ * b = block_tables[s][t / bs], V likewise; the workspace is pa_decode's.
+ * The kernel is the MFMA one for every group size.
+ */
+pa_status pa_reshape_and_cache_scaled(const void* key, const void* value, void* k_cache, void* v_cache,
+                                      float* k_scales, float* v_scales, const int64_t* slot_mapping, int32_t T,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      pa_dtype src_dtype, pa_stream_t stream);
+pa_status pa_decode_scaled(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
+                           const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, float scale, pa_dtype q_dtype, pa_dtype out_dtype,
+                           void* workspace, size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * Several query tokens per sequence over the same paged cache: the tokens of
  * a chunked prefill, or the draft tokens a speculative decoder verifies
  * ("Paged Attention and Memory Efficiency ...", section "How vLLM turned

@@ -212,6 +212,59 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, bs: int, cache
     v_cache[b, :, o, :] = v
 
 
+# ---------------------------------------------------------------------------
+# FP8 with one scale per (slot, kv head) row ("PagedAttention - The KV Cache
+# Problem", section "What's Still Unsolved" names FP8/FP4 KV caches; the
+# granularity is a reading: a row's scale is fixed when the row is written,
+# which suits a cache that grows one token at a time)
+# ---------------------------------------------------------------------------
+
+def row_scale(rows32: np.ndarray) -> np.ndarray:
+    """Scale of each row (last axis = the row's elements, fp32): its largest
+    magnitude, NaN elements left out, divided by 448 in fp32, so that element
+    lands on the largest finite E4M3FN value; 1 for a row of zeros or one
+    holding an infinity."""
+    x = np.abs(np.asarray(rows32, np.float32))
+    x = np.where(np.isnan(x), np.float32(0), x)
+    amax = x.max(axis=-1)
+    ok = (amax > 0) & np.isfinite(amax)
+    return np.where(ok, amax / np.float32(E4M3_MAX), np.float32(1)).astype(np.float32)
+
+
+def reshape_and_cache_scaled(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping, bs: int,
+                             src_dtype: str):
+    """Token n's rows into slot_mapping[n] of an FP8 cache, each (token, head)
+    row encoded against its own scale, which goes to the scale pools
+    [num_blocks, kv_heads, bs] (fp32); a negative slot writes nothing."""
+    slots = np.asarray(slot_mapping, np.int64)
+    keep = slots >= 0
+    b = slots[keep] // bs
+    o = slots[keep] % bs
+    for src, cache, scales in ((key, k_cache, k_scales), (value, v_cache, v_scales)):
+        x = widen(np.asarray(src)[keep], src_dtype).astype(np.float32)  # [n, kv_heads, D]
+        s = row_scale(x)  # [n, kv_heads]
+        cache[b, :, o, :] = e4m3_encode(x, s[..., None])
+        scales[b, :, o] = s
+
+
+def widen_rows(codes, scales) -> np.ndarray:
+    """fp64 values of E4M3FN codes [..., D] times their rows' scales [...]: exact."""
+    return _E4M3[np.asarray(codes, np.uint8)] * np.asarray(scales, np.float32).astype(np.float64)[..., None]
+
+
+def decode_scaled(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens, scale: float,
+                  group: int, q_dtype: str, seqs=None) -> np.ndarray:
+    """fp64 decode over an FP8 cache with a scale per row [B, Hq, D]."""
+    q = np.asarray(q)
+    out = []
+    for s in (range(q.shape[0]) if seqs is None else seqs):
+        L = int(context_lens[s])
+        k = widen_rows(gather_kv(k_cache, block_tables[s], L), gather_kv(k_scales[..., None], block_tables[s], L)[..., 0])
+        v = widen_rows(gather_kv(v_cache, block_tables[s], L), gather_kv(v_scales[..., None], block_tables[s], L)[..., 0])
+        out.append(attend(widen(q[s], q_dtype), k, v, scale, group))
+    return np.stack(out) if out else np.zeros((0,) + q.shape[1:])
+
+
 def copy_blocks(k_cache, v_cache, pairs):
     """Copy-on-write duplication: block dst becomes a byte copy of block src,
     for K and V (P1 copy-on-write)."""

@@ -52,6 +52,11 @@ def library() -> ctypes.CDLL:
     lib.pa_decode_append.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32,
                                      f32, f32, i32, i32, i32, p, sz, p]
     lib.pa_decode_append.restype = ctypes.c_int
+    lib.pa_reshape_and_cache_scaled.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i64, i32, p]
+    lib.pa_reshape_and_cache_scaled.restype = ctypes.c_int
+    lib.pa_decode_scaled.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32, i32, i32,
+                                     p, sz, p]
+    lib.pa_decode_scaled.restype = ctypes.c_int
     lib.pa_decode_multi_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.pa_decode_multi_workspace_size.restype = sz
     lib.pa_decode_multi.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32, f32, f32,
@@ -207,6 +212,65 @@ def decode_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _ptr(block_tables), _ptr(context_lens), B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
         _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
         _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def reshape_and_cache_scaled(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             k_scales: torch.Tensor, v_scales: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Write key/value rows [T, Hkv, D] (f16/bf16) into an FP8 cache [num_blocks, Hkv, bs, D], each
+    (token, head) row against its own scale (largest magnitude / 448), stored in k_scales / v_scales
+    [num_blocks, Hkv, bs] float32."""
+    for t, n in ((key, "key"), (value, "value"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(t, n)
+    _require(k_scales, "k_scales", torch.float32)
+    _require(v_scales, "v_scales", torch.float32)
+    _require(slot_mapping, "slot_mapping", torch.int64)
+    T, Hkv, D = key.shape
+    nb, Hkv2, bs, D2 = k_cache.shape
+    if (value.shape != key.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D)
+            or slot_mapping.shape != (T,) or k_scales.shape != (nb, Hkv, bs) or v_scales.shape != k_scales.shape):
+        raise ValueError("shape mismatch between key/value, caches, scale pools and slot_mapping")
+    if k_cache.dtype != torch.float8_e4m3fn or v_cache.dtype != torch.float8_e4m3fn:
+        raise ValueError("row scales are for FP8 (float8_e4m3fn) caches")
+    _check(library().pa_reshape_and_cache_scaled(
+        _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(slot_mapping),
+        T, Hkv, D, bs, nb, _TORCH_CODE.get(key.dtype, -9), _stream(k_cache)))
+
+
+def decode_scaled(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: torch.Tensor,
+                  v_scales: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                  max_context_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                  out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode() over an FP8 cache whose rows carry their own scales ([num_blocks, Hkv, bs] float32)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(t, n)
+    _require(k_scales, "k_scales", torch.float32)
+    _require(v_scales, "v_scales", torch.float32)
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or Hq % Hkv or k_scales.shape != (nb, Hkv, bs) \
+            or v_scales.shape != k_scales.shape:
+        raise ValueError("q, caches and scale pools do not agree")
+    if k_cache.dtype != torch.float8_e4m3fn or v_cache.dtype != torch.float8_e4m3fn:
+        raise ValueError("row scales are for FP8 (float8_e4m3fn) caches")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, M] and context_lens [B]")
+    M = block_tables.shape[1]
+    mcl = M * bs if max_context_len is None else int(max_context_len)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
+    else:
+        _require(out, "out")
+    need = decode_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl) if B else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_decode_scaled(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables),
+        _ptr(context_lens), B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, _TORCH_CODE.get(q.dtype, -9),
+        _TORCH_CODE.get(out.dtype, -9), _ptr(workspace), ws_bytes, _stream(q)))
     return out
 
 

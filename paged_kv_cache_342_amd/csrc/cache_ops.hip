@@ -85,6 +85,91 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict_
   store_row8<ST, kFp8>(kx, vx, k_cache, v_cache, dst_elem, k_scale, v_scale);
 }
 
+// Scale of one row for an FP8 cache with a scale per (slot, kv head) row:
+// the row's largest magnitude maps to 448, the largest finite E4M3FN value;
+// a row of zeros, or one holding an infinity, keeps scale 1.
+__device__ __forceinline__ float row_scale(float amax) {
+  return amax > 0.f && amax <= 3.402823466e38f ? amax / 448.0f : 1.0f;
+}
+
+// One thread per 8 elements of one (token, kv head) row, the D / 8 threads
+// of a row being adjacent lanes: they share the row's largest magnitude
+// (NaN elements do not count), then write their codes; the first writes the
+// row's K and V scales.
+template <class ST>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const uint8_t* __restrict__ key,
+                                                           const uint8_t* __restrict__ value,
+                                                           uint8_t* __restrict__ k_cache,
+                                                           uint8_t* __restrict__ v_cache,
+                                                           float* __restrict__ k_scales,
+                                                           float* __restrict__ v_scales,
+                                                           const int64_t* __restrict__ slots, int T, int Hkv,
+                                                           int D, int bs, int64_t num_blocks) {
+  const int per_row = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / per_row;  // token * Hkv + head
+  const int chunk = (int)(gid - row * per_row);
+  if (row >= (int64_t)T * Hkv) return;  // whole rows leave together
+  const int64_t n = row / Hkv;
+  const int h = (int)(row - n * Hkv);
+  const int64_t src = (row * D + chunk * 8) * 2;
+  const int64_t slot = slots[n];
+  const i32x4 kx = ld16(key + src);
+  const i32x4 vx = ld16(value + src);
+  float kf[8], vf[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    unpack2<ST>((uint32_t)kx[w], kf[2 * w], kf[2 * w + 1]);
+    unpack2<ST>((uint32_t)vx[w], vf[2 * w], vf[2 * w + 1]);
+  }
+  float ka = 0.f, va = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ka = fmaxf(ka, fabsf(kf[i]));
+    va = fmaxf(va, fabsf(vf[i]));
+  }
+  for (int m = 1; m < per_row; m <<= 1) {  // stays inside the row's lanes
+    ka = fmaxf(ka, shfl_xor(ka, m));
+    va = fmaxf(va, shfl_xor(va, m));
+  }
+  if (slot < 0 || slot >= num_blocks * bs) return;
+  const float ks = row_scale(ka), vs = row_scale(va);
+  const int64_t b = slot / bs;
+  const int o = (int)(slot - b * bs);
+  const int64_t srow = (b * Hkv + h) * bs + o;
+  const int64_t dst_elem = srow * D + chunk * 8;
+  *reinterpret_cast<i32x2*>(k_cache + dst_elem) = encode8_fp8(kf, ks);
+  *reinterpret_cast<i32x2*>(v_cache + dst_elem) = encode8_fp8(vf, vs);
+  if (chunk == 0) {
+    k_scales[srow] = ks;
+    v_scales[srow] = vs;
+  }
+}
+
+pa_status scatter_rows_launch(const void* key, const void* value, void* k_cache, void* v_cache, float* k_scales,
+                              float* v_scales, const int64_t* slots, int T, int Hkv, int D, int bs,
+                              int64_t num_blocks, int src_dtype, hipStream_t stream) {
+  if (T == 0) return PA_OK;
+  const int64_t threads = (int64_t)T * Hkv * (D / 8);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  auto K = reinterpret_cast<const uint8_t*>(key);
+  auto V = reinterpret_cast<const uint8_t*>(value);
+  auto KC = reinterpret_cast<uint8_t*>(k_cache);
+  auto VC = reinterpret_cast<uint8_t*>(v_cache);
+  if (src_dtype == PA_F16)
+    hipLaunchKernelGGL((scatter_rows_kernel<F16>), grid, block, 0, stream, K, V, KC, VC, k_scales, v_scales, slots,
+                       T, Hkv, D, bs, num_blocks);
+  else
+    hipLaunchKernelGGL((scatter_rows_kernel<BF16>), grid, block, 0, stream, K, V, KC, VC, k_scales, v_scales,
+                       slots, T, Hkv, D, bs, num_blocks);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    set_error("pa_reshape_and_cache_scaled: launch failed: %s", hipGetErrorString(err));
+    return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
 // The row of position L - 1 of every sequence ([B, Hkv, D]) into the slot
 // the sequence's block table gives that position (L = context_lens[s]
 // clamped to [0, max_ctx]); nothing for L = 0 or a block id outside the

@@ -75,6 +75,10 @@ struct DecodeArgs {
   const int32_t* q_start;
   int32_t nq;
   int32_t q_rows;  // rows of q and out (a query range outside them is dropped)
+  // FP8 caches with a scale per (slot, kv head) row: [num_blocks, Hkv, bs]
+  // fp32 each (row-scale kernels only; the per-tensor scales are then 1)
+  const float* k_row_scale;
+  const float* v_row_scale;
 };
 
 // Queries of sequence s under MQ (qs = q_start, in memory or in LDS): first

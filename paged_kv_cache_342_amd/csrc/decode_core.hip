@@ -148,8 +148,9 @@ static int elem_size(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_
 
 pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const bool mq = r.q_start != nullptr;  // several queries per sequence: MFMA kernel only
+  const bool rs = r.k_row_scale != nullptr;  // a scale per row: MFMA kernel only
   const int nq = mq ? r.nq : 1;
-  const bool valu = !mq && decode_uses_valu(decode_variant_override(), r.G);
+  const bool valu = !mq && !rs && decode_uses_valu(decode_variant_override(), r.G);
   if (valu && !valu_supports(r.cache_dtype, r.q_dtype, r.D, r.bs, r.G)) {
     set_error("pa_decode: the VALU kernel is not built for group %d, head_dim %d, block size %d",
               r.G, r.D, r.bs);
@@ -196,8 +197,10 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   a.head_tiles = tiles;
   a.out_dtype = r.out_dtype == PA_F32 ? 0 : (r.out_dtype == PA_F16 ? 1 : 2);
   const bool fp8 = r.cache_dtype == PA_FP8_E4M3;
-  a.qk_scale_log2 = r.scale * (fp8 ? r.k_scale : 1.f) * 1.4426950408889634f;
-  a.v_scale = fp8 ? r.v_scale : 1.f;
+  a.qk_scale_log2 = r.scale * (fp8 && !rs ? r.k_scale : 1.f) * 1.4426950408889634f;
+  a.v_scale = fp8 && !rs ? r.v_scale : 1.f;
+  a.k_row_scale = r.k_row_scale;
+  a.v_row_scale = r.v_row_scale;
   a.nq = nq;
   a.q_rows = mq ? r.q_rows : r.B;
   const int ct = r.cache_dtype, qt = r.q_dtype;

@@ -24,6 +24,12 @@
 // not see (past L - n + j for query j of n).  A tile none of whose columns is
 // a query of the sequence skips the segment.
 //
+// FP8 caches with a scale per (slot, kv head) row (RS): each lane also loads
+// the scales of the positions its scores and its V values belong to (four
+// consecutive positions per 16-byte load); a score is multiplied by its K
+// row's scale, and the probability that weights a V row by that row's scale
+// (the denominator takes the probability itself).
+//
 // When the launch also appends each sequence's new row (16-bit caches), the
 // loads of position L - 1 read the caller's row instead of the cache, and
 // the wave that owns the sequence's last chunk stores that row into its slot
@@ -65,6 +71,13 @@ struct ChunkRaw {
   uint32_t v[8][VD];
 };
 
+// Row scales of one chunk: positions 16 * tt + 4 * gq .. + 3 for K and V.
+struct ChunkScales {
+  f32x4 k[2];
+  f32x4 v[2];
+};
+struct NoScales {};
+
 template <int N>
 __device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t* o) {
   if constexpr (N == 4) {
@@ -88,7 +101,7 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <class CT, class QT, int D, int BS, bool MQ>
+template <class CT, class QT, int D, int BS, bool MQ, bool RS>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int e = CT::bytes;
   constexpr int KK = D / 32;   // MFMAs per QK tile
@@ -97,6 +110,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr bool kBf16V = std::is_same<CT, BF16>::value;
   using PT = typename std::conditional<kBf16V, BF16, F16>::type;  // PV operand type
   using Raw = ChunkRaw<CT, D>;
+  using Scales = typename std::conditional<RS, ChunkScales, NoScales>::type;
   constexpr int VD = Raw::VD;
   constexpr int64_t kChunkBytes = (int64_t)BS * D * e;  // one (block, head) chunk
   constexpr int NB = kChunk / BS;
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     if (kCanAppend && a.new_k != nullptr)
       app_row = ld16((lane < kRowLanes ? hc.last_k : hc.last_v) + 16 * (lane % kRowLanes));
 
-    auto load_chunk = [&](int c, Raw& raw) {
+    auto load_chunk = [&](int c, Raw& raw, Scales& scl) {
       const int ctok = tok0 + kChunk * c;  // first position of the chunk
       int id[NB];
 #pragma unroll
@@ -249,6 +263,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         const uint8_t* row = ok ? vbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : hc.last_v;
         load_dwords<VD>(row + W * r * e, raw.v[j]);
       }
+      if constexpr (RS) {
+        // the scales of positions 16*tt + 4*gq .. + 3 (one block; past the end
+        // of the segment the ring's ids stay valid and the scores are masked)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int tc = 16 * tt + 4 * gq;
+          const int bsel = BS == 32 ? 0 : (BS == 16 ? tt : 2 * tt + (gq >> 1));
+          const int64_t off = ((int64_t)id[bsel] * a.Hkv + h) * BS + tc % BS;
+          scl.k[tt] = *reinterpret_cast<const f32x4*>(a.k_row_scale + off);
+          scl.v[tt] = *reinterpret_cast<const f32x4*>(a.v_row_scale + off);
+        }
+      }
     };
 
     float m = -INFINITY, l = 0.f;
@@ -256,7 +282,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < W; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute_chunk = [&](int c, const Raw& raw) {
+    auto compute_chunk = [&](int c, const Raw& raw, const Scales& scl) {
       const int ctok = tok0 + kChunk * c;
       // ---- QK
       i32x4 kop[2][KK];
@@ -288,7 +314,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float raw_s = (j < 4 ? s0[j & 3] : s1[j & 3]) * a.qk_scale_log2;
+        float raw_s = (j < 4 ? s0[j & 3] : s1[j & 3]) * a.qk_scale_log2;
+        if constexpr (RS) raw_s *= scl.k[j >> 2][j & 3];
         const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
         const bool seen = ctok + tc < tok_end && (!MQ || ctok + tc <= qlim);
         sc[j] = seen ? raw_s : -INFINITY;
@@ -311,17 +338,27 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         p[j] = (MQ && sc[j] == -INFINITY) ? 0.f : fast_exp2(sc[j] - m);
         l += p[j];
       }
-      // ---- P as the B operand of PV
+      // ---- P as the B operand of PV (weighted by the V rows' scales under RS;
+      // a masked position's scale may belong to a slot never written, so its
+      // weight is set, not computed)
+      float pw[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (RS)
+          pw[j] = sc[j] == -INFINITY ? 0.f : p[j] * scl.v[j >> 2][j & 3];
+        else
+          pw[j] = p[j];
+      }
       i32x4 pop, plo;
 #pragma unroll
       for (int jp = 0; jp < 4; ++jp) {
         if constexpr (kBf16V) {
-          const uint32_t hi = pack_bf16(p[2 * jp], p[2 * jp + 1]);
+          const uint32_t hi = pack_bf16(pw[2 * jp], pw[2 * jp + 1]);
           const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
           pop[jp] = (int)hi;
-          plo[jp] = (int)pack_bf16(p[2 * jp] - h0, p[2 * jp + 1] - h1);
+          plo[jp] = (int)pack_bf16(pw[2 * jp] - h0, pw[2 * jp + 1] - h1);
         } else {
-          pop[jp] = (int)pack_f16(p[2 * jp], p[2 * jp + 1]);
+          pop[jp] = (int)pack_f16(pw[2 * jp], pw[2 * jp + 1]);
         }
       }
       // ---- V^T as the A operand: 16-bit values per position, then transpose
@@ -363,33 +400,35 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     if (MQ && 16 * ht >= hc.nqs * a.G) {
     } else if constexpr (!kFp8) {
       Raw buf0, buf1;
-      load_chunk(0, buf0);
+      Scales sc0, sc1;
+      load_chunk(0, buf0, sc0);
       for (int c = 0; c < nchunks; c += 2) {
         ring.advance();
-        load_chunk(c + 1, buf1);
-        compute_chunk(c, buf0);
+        load_chunk(c + 1, buf1, sc1);
+        compute_chunk(c, buf0, sc0);
         if (c + 1 >= nchunks) break;
         ring.advance();
-        load_chunk(c + 2, buf0);
-        compute_chunk(c + 1, buf1);
+        load_chunk(c + 2, buf0, sc0);
+        compute_chunk(c + 1, buf1, sc1);
       }
     } else {
       Raw buf0, buf1, buf2;
-      load_chunk(0, buf0);
+      Scales sc0, sc1, sc2;
+      load_chunk(0, buf0, sc0);
       ring.advance();
-      load_chunk(1, buf1);
+      load_chunk(1, buf1, sc1);
       for (int c = 0; c < nchunks; c += 3) {
         ring.advance();
-        load_chunk(c + 2, buf2);
-        compute_chunk(c, buf0);
+        load_chunk(c + 2, buf2, sc2);
+        compute_chunk(c, buf0, sc0);
         if (c + 1 >= nchunks) break;
         ring.advance();
-        load_chunk(c + 3, buf0);
-        compute_chunk(c + 1, buf1);
+        load_chunk(c + 3, buf0, sc0);
+        compute_chunk(c + 1, buf1, sc1);
         if (c + 2 >= nchunks) break;
         ring.advance();
-        load_chunk(c + 4, buf1);
-        compute_chunk(c + 2, buf2);
+        load_chunk(c + 4, buf1, sc1);
+        compute_chunk(c + 2, buf2, sc2);
       }
     }
 
@@ -425,14 +464,25 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-#define PA_MFMA_CASE(CT, QT, D, BS)                                                            \
-  if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS) {                         \
-    if (multi_query)                                                                           \
-      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true>), grid, dim3(64), 0, stream, a); \
-    else                                                                                       \
-      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, false>), grid, dim3(64), 0, stream, a); \
-    return true;                                                                               \
+#define PA_MFMA_CASE(CT, QT, D, BS)                                                                   \
+  if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS) {                                \
+    if (multi_query)                                                                                  \
+      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false>), grid, dim3(64), 0, stream, a); \
+    else                                                                                              \
+      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, false, false>), grid, dim3(64), 0, stream, a); \
+    return true;                                                                                      \
   }
+
+// FP8 caches with a scale per row
+#define PA_MFMA_RS_CASE(QT, D, BS)                                                                    \
+  if (qt == QT::code && head_dim == D && bs == BS) {                                                  \
+    hipLaunchKernelGGL((decode_mfma_kernel<FP8, QT, D, BS, false, true>), grid, dim3(64), 0, stream, a); \
+    return true;                                                                                      \
+  }
+#define PA_MFMA_RS_BS(QT, D) \
+  PA_MFMA_RS_CASE(QT, D, 8)  \
+  PA_MFMA_RS_CASE(QT, D, 16) \
+  PA_MFMA_RS_CASE(QT, D, 32)
 
 #define PA_MFMA_BS(CT, QT, D) \
   PA_MFMA_CASE(CT, QT, D, 8)  \
@@ -441,6 +491,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
 
 bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query, dim3 grid,
                         hipStream_t stream) {
+  if (a.k_row_scale != nullptr) {
+    if (ct != FP8::code || multi_query) return false;
+    PA_MFMA_RS_BS(F16, 64)
+    PA_MFMA_RS_BS(F16, 128)
+    PA_MFMA_RS_BS(BF16, 64)
+    PA_MFMA_RS_BS(BF16, 128)
+    return false;
+  }
   PA_MFMA_BS(F16, F16, 64)
   PA_MFMA_BS(F16, F16, 128)
   PA_MFMA_BS(BF16, BF16, 64)

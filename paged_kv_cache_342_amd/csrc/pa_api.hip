@@ -217,6 +217,49 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
 
+pa_status pa_reshape_and_cache_scaled(const void* key, const void* value, void* k_cache, void* v_cache,
+                                      float* k_scales, float* v_scales, const int64_t* slot_mapping, int32_t T,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                      pa_dtype src_dtype, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_reshape_and_cache_scaled";
+  if (T < 0) return fail(PA_ERR_INVALID_ARG, "%s: T must be >= 0", fn);
+  PA_CHECK_SHAPE("pa_reshape_and_cache_scaled", num_kv_heads, head_dim, block_size, num_blocks);
+  if (!known_dtype(src_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (src_dtype != PA_F16 && src_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: source rows must be f16 or bf16", fn);
+  if (!k_cache || !v_cache || !k_scales || !v_scales) return fail(PA_ERR_INVALID_ARG, "%s: null cache or scale pointer", fn);
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_scales, 16) || !aligned(v_scales, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: cache and scale pointers must be 16-byte aligned", fn);
+  if (T == 0) return PA_OK;
+  if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "%s: null key/value/slot_mapping", fn);
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8))
+    return fail(PA_ERR_INVALID_ARG, "%s: misaligned key/value/slot_mapping", fn);
+  return scatter_rows_launch(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping, T, num_kv_heads,
+                             head_dim, block_size, num_blocks, src_dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
+pa_status pa_decode_scaled(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
+                           const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
+                           int32_t max_context_len, float scale, pa_dtype q_dtype, pa_dtype out_dtype,
+                           void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_decode_scaled";
+  DecodeRequest r;
+  const pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads,
+                                      gqa_group, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                      max_context_len, scale, 1.f, 1.f, q_dtype, PA_FP8_E4M3, out_dtype, workspace,
+                                      workspace_bytes, 1, false, r);
+  if (st != PA_OK || B == 0) return st;
+  if (!k_scales || !v_scales || !aligned(k_scales, 16) || !aligned(v_scales, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned scale pools", fn);
+  r.k_row_scale = k_scales;
+  r.v_row_scale = v_scales;
+  return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
+}
+
 size_t pa_decode_multi_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                                       int32_t block_size, int32_t max_context_len, int32_t max_queries) {
   if (B <= 0 || num_kv_heads <= 0 || gqa_group <= 0 || max_context_len <= 0 || max_queries <= 0) return 0;

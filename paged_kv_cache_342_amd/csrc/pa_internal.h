@@ -56,6 +56,10 @@ struct DecodeRequest {
   const int32_t* q_start;
   int nq;
   int q_rows;
+  // FP8 cache with a scale per (slot, kv head) row ([num_blocks, Hkv, bs]
+  // fp32 each); null = one scale per tensor
+  const float* k_row_scale;
+  const float* v_row_scale;
 };
 
 // 0 = default choice, 1 = VALU/DPP kernel, 2 = MFMA kernel
@@ -69,6 +73,10 @@ pa_status scatter_launch(const void* key, const void* value, void* k_cache, void
                          const int64_t* slots, int T, int Hkv, int D, int bs, int64_t num_blocks,
                          int src_dtype, int cache_dtype, float k_scale, float v_scale,
                          hipStream_t stream);
+
+pa_status scatter_rows_launch(const void* key, const void* value, void* k_cache, void* v_cache, float* k_scales,
+                              float* v_scales, const int64_t* slots, int T, int Hkv, int D, int bs,
+                              int64_t num_blocks, int src_dtype, hipStream_t stream);
 
 pa_status append_last_launch(const void* key, const void* value, void* k_cache, void* v_cache,
                              const int32_t* block_tables, const int32_t* context_lens, int B, int M,

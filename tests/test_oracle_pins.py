@@ -509,3 +509,108 @@ def test_multi_query_pins_catch_planted_mistakes(mistake):
                                                                  vs[s].astype(np.float64), 0.2, 4)[lens[s] - nqs[s]:]))
              <= 1e-12 for s in range(len(lens)))
     assert not ok
+
+
+# ---------------------------------------------------------------- FP8 with a scale per row
+
+def _rows_of_many_magnitudes(seed, n=64, D=128):
+    rng = np.random.default_rng(seed)
+    mag = 10.0 ** rng.uniform(-4, 4, size=(n, 1))
+    return (rng.standard_normal((n, D)) * mag).astype(np.float32)
+
+
+def test_row_scale_puts_each_rows_largest_magnitude_on_448():
+    x = _rows_of_many_magnitudes(1)
+    s = O.row_scale(x)
+    codes = O.e4m3_encode(x, s[:, None])
+    big = np.argmax(np.abs(x), axis=1)
+    top = codes[np.arange(len(x)), big]
+    assert set(np.unique(top & 0x7F).tolist()) == {0x7E}  # +-448, the largest finite code
+    assert np.array_equal(top >> 7, (x[np.arange(len(x)), big] < 0).astype(np.uint8))
+
+
+def test_row_scale_error_bounds():
+    """Normal-range codes carry 3 mantissa bits: a relative error of at most
+    2^-4 after the division by the scale (plus fp32 rounding); below 2^-6 the
+    spacing is 2^-9, so the error is at most half of it, times the scale."""
+    x = _rows_of_many_magnitudes(2)
+    s = O.row_scale(x)
+    back = O.widen_rows(O.e4m3_encode(x, s[:, None]), s)
+    y = np.abs(x.astype(np.float64)) / s[:, None]
+    err = np.abs(back - x)
+    normal = y >= 2.0 ** -6
+    assert np.all(err[normal] <= np.abs(x[normal]) * (2.0 ** -4) * (1 + 1e-6))
+    assert np.all(err[~normal] <= (s[:, None] * np.ones_like(x))[~normal] * 2.0 ** -10 * (1 + 1e-6))
+
+
+def test_row_scale_special_rows():
+    rows = np.zeros((4, 8), np.float32)
+    rows[1, 3] = np.inf
+    rows[2, :] = [np.nan, 1.0, -3.0, 2.0, 0.0, 0.5, np.nan, 1.5]
+    rows[3, 0] = -7.0
+    s = O.row_scale(rows)
+    assert s[0] == 1 and s[1] == 1  # zeros; an infinity
+    assert s[2] == np.float32(3.0) / np.float32(448.0)  # NaN elements do not count
+    assert s[3] == np.float32(7.0) / np.float32(448.0)
+    codes = O.e4m3_encode(rows, s[:, None])
+    assert (codes[0] == 0).all() and codes[1, 3] == 0x7E and codes[3, 0] == 0xFE
+    assert codes[2, 0] == 0x7F and codes[2, 2] == 0xFE
+
+
+def test_row_scales_keep_small_rows_that_one_tensor_scale_flushes():
+    """Rows whose magnitudes span eight decades (more than the ~1e5 E4M3FN
+    covers): one scale per tensor sends the small rows into the subnormal
+    range or to zero, a scale per row keeps them."""
+    x = _rows_of_many_magnitudes(3)
+    t = np.float32(np.abs(x).max()) / np.float32(448.0)
+    per_tensor = O.e4m3_decode(O.e4m3_encode(x, t), t)
+    s = O.row_scale(x)
+    per_row = O.widen_rows(O.e4m3_encode(x, s[:, None]), s)
+    rel = lambda a: np.abs(a - x) / np.maximum(np.abs(x), 1e-30)
+    assert (rel(per_row) > 0.5).mean() < 0.05 and (rel(per_tensor) > 0.5).mean() > 0.2
+
+
+def test_scaled_decode_matches_attention_over_dequantised_rows():
+    """Through the pool and the tables, against torch float64 attention over
+    rows dequantised element by element from the code table."""
+    rng = np.random.default_rng(4)
+    Hkv, G, D, bs, L = 2, 4, 32, 8, 37
+    k = (rng.standard_normal((L, Hkv, D)) * 10.0 ** rng.uniform(-2, 2, size=(L, Hkv, 1))).astype(np.float16)
+    v = (rng.standard_normal((L, Hkv, D)) * 10.0 ** rng.uniform(-2, 2, size=(L, Hkv, 1))).astype(np.float16)
+    nb = 8
+    table = rng.permutation(nb)[:(L + bs - 1) // bs]
+    kc = O.new_pool(nb, Hkv, bs, D, "fp8")
+    vc = O.new_pool(nb, Hkv, bs, D, "fp8")
+    ks = np.full((nb, Hkv, bs), np.nan, np.float32)
+    vs = np.full((nb, Hkv, bs), np.nan, np.float32)
+    O.reshape_and_cache_scaled(k, v, kc, vc, ks, vs, O.slots_for(table, 0, L, bs), bs, "f16")
+    q = rng.standard_normal((1, Hkv * G, D)).astype(np.float16)
+    out = O.decode_scaled(q, kc, vc, ks, vs, table[None], np.array([L]), 0.2, G, "f16")[0]
+    table_vals = O.e4m3_values()
+    kd = np.zeros((L, Hkv, D))
+    vd = np.zeros((L, Hkv, D))
+    for t in range(L):
+        b, o = table[t // bs], t % bs
+        for h in range(Hkv):
+            kd[t, h] = [table_vals[c] * float(ks[b, h, o]) for c in kc[b, h, o]]
+            vd[t, h] = [table_vals[c] * float(vs[b, h, o]) for c in vc[b, h, o]]
+    ref = _sdpa(q[0].astype(np.float64), kd, vd, 0.2, G)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("mistake", ["fnuz_max", "signed_max"])
+def test_row_scale_pins_catch_planted_mistakes(mistake):
+    def bad_scale(rows):
+        x = np.asarray(rows, np.float32)
+        amax = (x.max(axis=-1) if mistake == "signed_max" else np.abs(x).max(axis=-1))
+        div = np.float32(240.0) if mistake == "fnuz_max" else np.float32(448.0)
+        return np.where(amax > 0, amax / div, np.float32(1)).astype(np.float32)
+
+    x = _rows_of_many_magnitudes(1)
+    s = bad_scale(x)
+    codes = O.e4m3_encode(x, s[:, None])
+    big = np.argmax(np.abs(x), axis=1)
+    top_ok = set(np.unique(codes[np.arange(len(x)), big] & 0x7F).tolist()) == {0x7E}
+    back = O.widen_rows(codes, s)
+    bound_ok = np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -4 * (1 + 1e-6) + s[:, None] * 2.0 ** -10)
+    assert not (top_ok and bound_ok)

@@ -42,7 +42,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, row_scales: bool = False):
     """The fp64 oracle over whole sequences of the same batch, until the time budget is spent."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -51,7 +51,18 @@ def cpu_baseline(w, budget_s: float):
     from oracle import pa_oracle as O
 
     log("cpu baseline: building oracle pools")
-    kc, vc = OH.build_pools(w)
+    if row_scales:
+        kc, vc = O.new_pool(w.num_blocks, w.Hkv, w.bs, w.D, "fp8"), O.new_pool(w.num_blocks, w.Hkv, w.bs, w.D, "fp8")
+        ks = np.ones((w.num_blocks, w.Hkv, w.bs), np.float32)
+        vs = ks.copy()
+        for s in range(w.B):
+            L = int(w.context_lens[s])
+            if L:
+                k, v = w.seq_kv(s)
+                O.reshape_and_cache_scaled(k, v, kc, vc, ks, vs, O.slots_for(w.block_tables[s], 0, L, w.bs), w.bs,
+                                           w.src_dtype)
+    else:
+        kc, vc = OH.build_pools(w)
     q = w.query()
     done_seqs = 0
     kv = 0
@@ -60,7 +71,10 @@ def cpu_baseline(w, budget_s: float):
     while t_total < budget_s and passes < 50:
         for s in range(w.B):
             t0 = time.perf_counter()
-            if w.query_start is None:
+            if row_scales:
+                O.decode_scaled(q, kc, vc, ks, vs, w.block_tables, w.context_lens, w.scale, w.group, w.q_dtype,
+                                seqs=[s])
+            elif w.query_start is None:
                 O.decode_one(q[s], kc, vc, w.block_tables[s], int(w.context_lens[s]), w.scale, w.group,
                              w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale)
             else:
@@ -199,6 +213,9 @@ def main():
     ap.add_argument("--identity-tables", action="store_true",
                     help="ablation: move every sequence's blocks into consecutive physical blocks, in order "
                          "(same values, no scattered indirection)")
+    ap.add_argument("--row-scales", action="store_true",
+                    help="FP8 workloads: one scale per (slot, kv head) row (pa_reshape_and_cache_scaled + "
+                         "pa_decode_scaled) instead of one per tensor")
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as two calls, pa_reshape_and_cache then pa_decode")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -222,9 +239,12 @@ def main():
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} bs={w.bs} cache={w.cache_dtype} "
         f"sum(L)={int(w.context_lens.sum())}")
     multi = w.query_start is not None  # several queries per sequence: pa_decode_multi
-    if multi and (args.unfused or args.identity_tables):
-        raise SystemExit("--unfused and --identity-tables apply to the decode workloads only")
-    batch = DeviceBatch(w, device=dev, skip_last_append=not multi)
+    if multi and (args.unfused or args.identity_tables or args.row_scales):
+        raise SystemExit("--unfused, --identity-tables and --row-scales apply to the decode workloads only")
+    if args.row_scales and w.cache_dtype != "fp8":
+        raise SystemExit("--row-scales applies to FP8 workloads")
+    rs = args.row_scales
+    batch = DeviceBatch(w, device=dev, skip_last_append=not multi, row_scales=rs)
     if multi:  # the step re-appends the query tokens' own rows, then attends
         nqs = np.diff(w.query_start).astype(np.int64)
         last = W.WriteOp("append", np.arange(w.B, dtype=np.int64), w.context_lens.astype(np.int64) - nqs,
@@ -261,11 +281,18 @@ def main():
             flush.sum()
 
     def append():
-        pa.reshape_and_cache(k_new, v_new, batch.kc, batch.vc, slots_new, w.k_scale, w.v_scale)
+        if rs:
+            pa.reshape_and_cache_scaled(k_new, v_new, batch.kc, batch.vc, batch.kss, batch.vss, slots_new)
+        else:
+            pa.reshape_and_cache(k_new, v_new, batch.kc, batch.vc, slots_new, w.k_scale, w.v_scale)
 
     def decode():
-        pa.decode(batch.q, batch.kc, batch.vc, batch.tables, batch.lens, w.scale, max_context_len=w.max_context_len,
-                  k_scale=w.k_scale, v_scale=w.v_scale, out=out, workspace=ws)
+        if rs:
+            pa.decode_scaled(batch.q, batch.kc, batch.vc, batch.kss, batch.vss, batch.tables, batch.lens, w.scale,
+                             max_context_len=w.max_context_len, out=out, workspace=ws)
+        else:
+            pa.decode(batch.q, batch.kc, batch.vc, batch.tables, batch.lens, w.scale,
+                      max_context_len=w.max_context_len, k_scale=w.k_scale, v_scale=w.v_scale, out=out, workspace=ws)
 
     def decode_append():
         pa.decode_append(batch.q, batch.kc, batch.vc, k_last, v_last, batch.tables, batch.lens, w.scale,
@@ -277,7 +304,7 @@ def main():
                         max_context_len=w.max_context_len, k_scale=w.k_scale, v_scale=w.v_scale, out=out,
                         workspace=ws)
 
-    two_calls = args.unfused or multi
+    two_calls = args.unfused or multi or rs
     second = decode_multi if multi else decode
 
     def step():
@@ -315,6 +342,8 @@ def main():
     ms_step = float(np.mean(step_ms))
     ms_dec = float(np.mean(dec_ms))
     kv_bytes = w.kv_bytes()
+    if rs:  # each (position, kv head) row also carries a 4-byte K and V scale
+        kv_bytes += int(w.context_lens.astype(np.int64).sum()) * w.Hkv * 4 * 2
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (ms_dec * 1e-3) / 1e9
     # algorithmic flops: 4 * D per (query head, position seen) -- QK and PV
@@ -332,7 +361,7 @@ def main():
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_baseline(w, args.cpu_budget)
+        cpu = cpu_baseline(w, args.cpu_budget, rs)
 
     res = {
         "metric": METRIC,
@@ -352,7 +381,9 @@ def main():
             "block_size": w.bs, "cache_dtype": w.cache_dtype, "q_dtype": w.q_dtype, "seed": w.seed,
             "sum_context_len": int(w.context_lens.sum()), "kv_bytes": kv_bytes, "parallelism": "single-gpu",
             "l2_mall_flush_between_steps": flush is not None, "identity_tables": args.identity_tables,
+            "row_scales": rs,
             "step": ("pa_reshape_and_cache + pa_decode_multi" if multi else
+                     "pa_reshape_and_cache_scaled + pa_decode_scaled" if rs else
                      "pa_reshape_and_cache + pa_decode" if args.unfused else "pa_decode_append"),
             **({"queries_per_seq": w.max_queries, "total_queries": int(w.query_start[-1])} if multi else {}),
         },
@@ -366,8 +397,10 @@ def main():
             "peak": mfma_peak if mfma_bound else HBM_PEAK_GBS,
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": round(tflops / mfma_peak if mfma_bound else achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if args.identity_tables or args.unfused else recorded_traffic(w.name),
+            "traffic": None if args.identity_tables or args.unfused else
+                       recorded_traffic(w.name + ("+row_scales" if rs else "")),
             "kernel": ("pa_decode_multi call: MFMA kernel, (query, head) columns + merge kernel" if multi else
+                       "pa_decode_scaled call: MFMA kernel with row scales + merge kernel" if rs else
                        "pa_decode call: decode kernel (balanced slices) + merge kernel" if args.unfused else
                        "pa_decode_append call: decode kernel (balanced slices, append fused for 16-bit caches; "
                        "fp8: append scatter first) + merge kernel"),

@@ -45,11 +45,20 @@ def new_pool(w, device="cuda", poison=True) -> torch.Tensor:
 class DeviceBatch:
     """Device copy of a workload: pools filled by the library, tables, lengths, query."""
 
-    def __init__(self, w, device="cuda", poison=True, skip_last_append=False):
+    def __init__(self, w, device="cuda", poison=True, skip_last_append=False, row_scales=False):
+        """row_scales: an FP8 cache whose rows carry their own scales (pools self.kss / self.vss,
+        filled by pa.reshape_and_cache_scaled)."""
         self.w = w
         self.device = device
+        self.row_scales = row_scales
+        if row_scales and w.cache_dtype != "fp8":
+            raise ValueError("row scales are for FP8 caches")
         self.kc = new_pool(w, device, poison)
         self.vc = new_pool(w, device, poison)
+        if row_scales:
+            self.kss = torch.full((w.num_blocks, w.Hkv, w.bs), float("nan") if poison else 1.0, dtype=torch.float32,
+                                  device=device)
+            self.vss = self.kss.clone()
         self._kv = {}
         ops = w.ops[:-1] if skip_last_append else w.ops
         for op in ops:
@@ -92,8 +101,12 @@ class DeviceBatch:
         k, v, slots = r
         step = 1 << 16
         for i in range(0, k.shape[0], step):
-            pa.reshape_and_cache(k[i:i + step], v[i:i + step], self.kc, self.vc, slots[i:i + step],
-                                 w.k_scale, w.v_scale)
+            if self.row_scales:
+                pa.reshape_and_cache_scaled(k[i:i + step], v[i:i + step], self.kc, self.vc, self.kss, self.vss,
+                                            slots[i:i + step])
+            else:
+                pa.reshape_and_cache(k[i:i + step], v[i:i + step], self.kc, self.vc, slots[i:i + step],
+                                     w.k_scale, w.v_scale)
 
     def last_rows(self):
         """The row of position L - 1 of every sequence, [B, Hkv, D] each for K and V in the

@@ -10,11 +10,12 @@
 
 namespace pa {
 
-bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query, dim3 grid,
-                        hipStream_t stream);
+bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query,
+                        int tiles_per_wave, dim3 grid, hipStream_t stream);
 bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, int group,
                         dim3 grid, hipStream_t stream);
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
+bool mfma_two_tiles(int ct, int head_dim);
 
 // Workgroups per (KV head, sequence) -- one for decode, more when its
 // queries hold more outputs than a workgroup has threads: merge the slices'
@@ -156,7 +157,12 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
               r.G, r.D, r.bs);
     return PA_ERR_UNSUPPORTED;
   }
-  const int tiles = valu ? 1 : (int)(((int64_t)nq * r.G + 15) / 16);
+  // 16-column tiles of (query, head) columns per KV head; a wave computes one,
+  // or two when a sequence's queries span several (the K/V loads and the V
+  // transposes are then shared)
+  const int col_tiles = valu ? 1 : (int)(((int64_t)nq * r.G + 15) / 16);
+  const int tw = mq && col_tiles >= 2 && mfma_two_tiles(r.cache_dtype, r.D) ? 2 : 1;
+  const int tiles = (col_tiles + tw - 1) / tw;  // waves per (slice, KV head)
   const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq, mq);
   if (r.workspace_bytes < plan.bytes) {
     set_error("pa_decode: workspace of %zu bytes needed, %zu given", plan.bytes, r.workspace_bytes);
@@ -221,7 +227,7 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     a.new_v = fused_append ? reinterpret_cast<const uint8_t*>(r.new_v) + (size_t)s0 * new_row : nullptr;
     const dim3 grid((unsigned)grid_waves);
     const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream)
-                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, grid, stream);
+                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, tw, grid, stream);
     if (!ok) {
       set_error("pa_decode: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d, group %d (%s)",
                 ct, qt, r.D, r.bs, r.G, valu ? "valu" : "mfma");

@@ -22,7 +22,10 @@
 // pairs instead of heads -- column c is query c / G of the sequence and head
 // c % G of the group -- and each column masks the positions its query may
 // not see (past L - n + j for query j of n).  A tile none of whose columns is
-// a query of the sequence skips the segment.
+// a query of the sequence skips the segment.  When a sequence's queries span
+// several tiles, one wave computes TW = 2 tiles per chunk: the K/V loads,
+// their addresses and the V transposes are shared by both, only the
+// products and the softmax are per tile.
 //
 // FP8 caches with a scale per (slot, kv head) row (RS): each lane also loads
 // the scales of the positions its scores and its V values belong to (four
@@ -101,7 +104,7 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <class CT, class QT, int D, int BS, bool MQ, bool RS>
+template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int e = CT::bytes;
   constexpr int KK = D / 32;   // MFMAs per QK tile
@@ -138,11 +141,18 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   Slice sl;
   if (!slice_setup(a, cum, lens, MQ ? qrow : nullptr, k, sl)) return;
 
-  const int col = 16 * ht + r;                 // this lane's column
-  const int cq = MQ ? col / a.G : 0;           // its query within the sequence
-  const int col_head = MQ ? col - cq * a.G : col;  // its head within the group
-  const bool col_ok = MQ ? cq < a.nq : col < a.G;
-  const int head = h * a.G + (col_ok ? col_head : 0);
+  // this lane's column in each of the wave's TW tiles: its query within the
+  // sequence (MQ) and its head within the group
+  int cq[TW], head[TW];
+  bool col_ok[TW];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int col = 16 * (TW * ht + t) + r;
+    cq[t] = MQ ? col / a.G : 0;
+    const int col_head = MQ ? col - cq[t] * a.G : col;
+    col_ok[t] = MQ ? cq[t] < a.nq : col < a.G;
+    head[t] = h * a.G + (col_ok[t] ? col_head : 0);
+  }
   const uint8_t* kbase = a.k_cache + (int64_t)h * kChunkBytes;
   const uint8_t* vbase = a.v_cache + (int64_t)h * kChunkBytes;
 
@@ -151,11 +161,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   for (int s = sl.s_first; s < a.B && !MQ; ++s) {
     const int cs = cum[s], ce = cum[s + 1];
     if (past_slice(sl, cs, ce)) break;
-    if (lens[s] == 0 && col_ok) {
+    if (lens[s] == 0 && col_ok[0]) {
       float z[4 * W];
 #pragma unroll
       for (int i = 0; i < 4 * W; ++i) z[i] = 0.f;
-      store_out(a, s, head, D, 4 * W * gq, z, 4 * W);
+      store_out(a, s, head[0], D, 4 * W * gq, z, 4 * W);
     }
   }
 
@@ -167,7 +177,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   // there is a next segment (past the last one the current segment's header
   // is read again), so segment changes cost no table or query round trips.
   struct Header {
-    i32x4 qop[KK];
+    i32x4 qop[TW][KK];
     IdRing<BS> ring;
     const uint8_t* last_k;  // row of the last position
     const uint8_t* last_v;
@@ -187,14 +197,17 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     }
     // a column that is no query of the sequence reads a row that exists
     // (row 0) and contributes zeros
-    const bool live = MQ ? cq < hd.nqs : col_ok;
-    const int64_t qr = MQ ? (live ? hd.qrow0 + cq : 0) : g.s;
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + (qr * Hq + (live ? head : h * a.G)) * D * 2;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int d = kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
-      const i32x4 x = ld16(qrow + d * 2);
-      hd.qop[kk] = live ? x : i32x4{0, 0, 0, 0};
+    for (int t = 0; t < TW; ++t) {
+      const bool live = MQ ? cq[t] < hd.nqs : col_ok[t];
+      const int64_t qr = MQ ? (live ? hd.qrow0 + cq[t] : 0) : g.s;
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + (qr * Hq + (live ? head[t] : h * a.G)) * D * 2;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int d = kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
+        const i32x4 x = ld16(qrow + d * 2);
+        hd.qop[t][kk] = live ? x : i32x4{0, 0, 0, 0};
+      }
     }
     const int32_t* trow = a.block_tables + (int64_t)g.s * a.M;
     const int blk0 = g.tok0 / BS;
@@ -222,11 +235,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     const int s = cur.s;
     const int cs = cur.cs, ce = cur.ce;
     const int tok0 = cur.tok0, tok_end = cur.tok_end, nchunks = cur.nchunks;
-    const i32x4* qop = hc.qop;
     IdRing<BS>& ring = hc.ring;
     const int lim = hc.lim;
-    const bool live = MQ ? cq < hc.nqs : col_ok;
-    const int qlim = MQ ? lens[s] - hc.nqs + cq : 0;  // last position this column's query sees
+    bool live[TW];
+    int qlim[TW];  // last position each column's query sees (MQ)
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      live[t] = MQ ? cq[t] < hc.nqs : col_ok[t];
+      qlim[t] = MQ ? lens[s] - hc.nqs + cq[t] : 0;
+    }
     // the appended row, stored at the end of the segment: lane i < kRowLanes
     // holds 16 bytes of K, the next kRowLanes lanes 16 bytes of V
     i32x4 app_row = {0, 0, 0, 0};
@@ -277,10 +294,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       }
     };
 
-    float m = -INFINITY, l = 0.f;
-    f32x4 acc[W];
+    float m[TW], l[TW];
+    f32x4 acc[TW][W];
 #pragma unroll
-    for (int i = 0; i < W; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TW; ++t) {
+      m[t] = -INFINITY;
+      l[t] = 0.f;
+#pragma unroll
+      for (int i = 0; i < W; ++i) acc[t][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     auto compute_chunk = [&](int c, const Raw& raw, const Scales& scl) {
       const int ctok = tok0 + kChunk * c;
@@ -303,62 +325,70 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
           for (int u = 0; u < KK; ++u) kop[tt][u] = raw.k[tt][u];
         }
       }
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      f32x4 s0[TW], s1[TW];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s0 = mfma32<QT>(kop[0][kk], qop[kk], s0);
-        s1 = mfma32<QT>(kop[1][kk], qop[kk], s1);
+      for (int t = 0; t < TW; ++t) {
+        s0[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s1[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          s0[t] = mfma32<QT>(kop[0][kk], hc.qop[t][kk], s0[t]);
+          s1[t] = mfma32<QT>(kop[1][kk], hc.qop[t][kk], s1[t]);
+        }
       }
-      // ---- online softmax for this lane's column (head), positions j
-      float sc[8];
-      float mx = -INFINITY;
+      i32x4 pop[TW], plo[TW];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float raw_s = (j < 4 ? s0[j & 3] : s1[j & 3]) * a.qk_scale_log2;
-        if constexpr (RS) raw_s *= scl.k[j >> 2][j & 3];
-        const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
-        const bool seen = ctok + tc < tok_end && (!MQ || ctok + tc <= qlim);
-        sc[j] = seen ? raw_s : -INFINITY;
-        mx = fmaxf(mx, sc[j]);
-      }
-      if (wave_any(mx > m + kRescaleThreshold)) {
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float mn = fmaxf(m, mx);
-        // under MQ a column may have seen no position yet (mn = -inf)
-        const float alpha = (MQ && mn == -INFINITY) ? 1.f : fast_exp2(m - mn);
+      for (int t = 0; t < TW; ++t) {
+        // ---- online softmax for this lane's column (head) of tile t, positions j
+        float sc[8];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < W; ++i) acc[i] *= alpha;
-        l *= alpha;
-        m = mn;
-      }
-      float p[8];
+        for (int j = 0; j < 8; ++j) {
+          float raw_s = (j < 4 ? s0[t][j & 3] : s1[t][j & 3]) * a.qk_scale_log2;
+          if constexpr (RS) raw_s *= scl.k[j >> 2][j & 3];
+          const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
+          const bool seen = ctok + tc < tok_end && (!MQ || ctok + tc <= qlim[t]);
+          sc[j] = seen ? raw_s : -INFINITY;
+          mx = fmaxf(mx, sc[j]);
+        }
+        if (wave_any(mx > m[t] + kRescaleThreshold)) {
+          mx = fmaxf(mx, shfl_xor(mx, 16));
+          mx = fmaxf(mx, shfl_xor(mx, 32));
+          const float mn = fmaxf(m[t], mx);
+          // under MQ a column may have seen no position yet (mn = -inf)
+          const float alpha = (MQ && mn == -INFINITY) ? 1.f : fast_exp2(m[t] - mn);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        p[j] = (MQ && sc[j] == -INFINITY) ? 0.f : fast_exp2(sc[j] - m);
-        l += p[j];
-      }
-      // ---- P as the B operand of PV (weighted by the V rows' scales under RS;
-      // a masked position's scale may belong to a slot never written, so its
-      // weight is set, not computed)
-      float pw[8];
+          for (int i = 0; i < W; ++i) acc[t][i] *= alpha;
+          l[t] *= alpha;
+          m[t] = mn;
+        }
+        float p[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if constexpr (RS)
-          pw[j] = sc[j] == -INFINITY ? 0.f : p[j] * scl.v[j >> 2][j & 3];
-        else
-          pw[j] = p[j];
-      }
-      i32x4 pop, plo;
+        for (int j = 0; j < 8; ++j) {
+          p[j] = (MQ && sc[j] == -INFINITY) ? 0.f : fast_exp2(sc[j] - m[t]);
+          l[t] += p[j];
+        }
+        // ---- P as the B operand of PV (weighted by the V rows' scales under
+        // RS; a masked position's scale may belong to a slot never written, so
+        // its weight is set, not computed)
+        float pw[8];
 #pragma unroll
-      for (int jp = 0; jp < 4; ++jp) {
-        if constexpr (kBf16V) {
-          const uint32_t hi = pack_bf16(pw[2 * jp], pw[2 * jp + 1]);
-          const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
-          pop[jp] = (int)hi;
-          plo[jp] = (int)pack_bf16(pw[2 * jp] - h0, pw[2 * jp + 1] - h1);
-        } else {
-          pop[jp] = (int)pack_f16(pw[2 * jp], pw[2 * jp + 1]);
+        for (int j = 0; j < 8; ++j) {
+          if constexpr (RS)
+            pw[j] = sc[j] == -INFINITY ? 0.f : p[j] * scl.v[j >> 2][j & 3];
+          else
+            pw[j] = p[j];
+        }
+#pragma unroll
+        for (int jp = 0; jp < 4; ++jp) {
+          if constexpr (kBf16V) {
+            const uint32_t hi = pack_bf16(pw[2 * jp], pw[2 * jp + 1]);
+            const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
+            pop[t][jp] = (int)hi;
+            plo[t][jp] = (int)pack_bf16(pw[2 * jp] - h0, pw[2 * jp + 1] - h1);
+          } else {
+            pop[t][jp] = (int)pack_f16(pw[2 * jp], pw[2 * jp + 1]);
+          }
         }
       }
       // ---- V^T as the A operand: 16-bit values per position, then transpose
@@ -386,8 +416,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
           vop[jp] = (dt & 1) ? (int)__builtin_amdgcn_perm(a1, a0, 0x07060302u)
                              : (int)__builtin_amdgcn_perm(a1, a0, 0x05040100u);
         }
-        acc[dt] = mfma32<PT>(vop, pop, acc[dt]);
-        if constexpr (kBf16V) acc[dt] = mfma32<PT>(vop, plo, acc[dt]);
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+          acc[t][dt] = mfma32<PT>(vop, pop[t], acc[t][dt]);
+          if constexpr (kBf16V) acc[t][dt] = mfma32<PT>(vop, plo[t], acc[t][dt]);
+        }
       }
     };
 
@@ -397,7 +430,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     // (past the end every lane reads the last row), so no load sits under a
     // branch and each wait covers only the chunk it needs.  (Under MQ a tile
     // with no query of this sequence among its columns skips the segment.)
-    if (MQ && 16 * ht >= hc.nqs * a.G) {
+    if (MQ && 16 * TW * ht >= hc.nqs * a.G) {
     } else if constexpr (!kFp8) {
       Raw buf0, buf1;
       Scales sc0, sc1;
@@ -432,23 +465,26 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- epilogue: the lane holds head col_head (of query cq), d = 4W*gq + W*jj + dt
-    l += shfl_xor(l, 16);
-    l += shfl_xor(l, 32);
-    if (live) {
-      float v[4 * W];
-      const bool whole = whole_sequence(sl, cs, ce);
-      const float f = whole ? a.v_scale / l : 1.f;
+    // ---- epilogue: per tile the lane holds head[t] (of query cq[t]), d = 4W*gq + W*jj + dt
+    const bool whole = whole_sequence(sl, cs, ce);
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+    for (int t = 0; t < TW; ++t) {
+      l[t] += shfl_xor(l[t], 16);
+      l[t] += shfl_xor(l[t], 32);
+      if (live[t]) {
+        float v[4 * W];
+        const float f = whole ? a.v_scale / l[t] : 1.f;
 #pragma unroll
-        for (int dt = 0; dt < W; ++dt) v[W * jj + dt] = acc[dt][jj] * f;
-      if (whole) {
-        store_out(a, MQ ? hc.qrow0 + cq : s, head, D, 4 * W * gq, v, 4 * W);
-      } else {
-        const int64_t row = part_row(a, sl.k, s, cq, head);
-        store_partial(a, row, D, 4 * W * gq, v, 4 * W);
-        if (gq == 0) store_ml(a, row, m, l);
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int dt = 0; dt < W; ++dt) v[W * jj + dt] = acc[t][dt][jj] * f;
+        if (whole) {
+          store_out(a, MQ ? hc.qrow0 + cq[t] : s, head[t], D, 4 * W * gq, v, 4 * W);
+        } else {
+          const int64_t row = part_row(a, sl.k, s, cq[t], head[t]);
+          store_partial(a, row, D, 4 * W * gq, v, 4 * W);
+          if (gq == 0) store_ml(a, row, m[t], l[t]);
+        }
       }
     }
     if (hc.tail_off >= 0 && lane < 2 * kRowLanes) {
@@ -464,19 +500,44 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-#define PA_MFMA_CASE(CT, QT, D, BS)                                                                   \
-  if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS) {                                \
-    if (multi_query)                                                                                  \
-      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false>), grid, dim3(64), 0, stream, a); \
-    else                                                                                              \
-      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, false, false>), grid, dim3(64), 0, stream, a); \
-    return true;                                                                                      \
+// Two tiles per wave need room for a second query operand, accumulator and
+// softmax state; fp8 caches at head_dim 128 (three row buffers) would spill,
+// so they keep one tile per wave.
+template <class CT, int D>
+constexpr bool kTwoTilesBuilt = !(std::is_same<CT, FP8>::value && D == 128);
+
+bool mfma_two_tiles(int ct, int head_dim) { return !(ct == FP8::code && head_dim == 128); }
+
+template <class CT, class QT, int D, int BS>
+void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, dim3 grid, hipStream_t stream) {
+  if (!multi_query) {
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, false, false, 1>), grid, dim3(64), 0, stream, a);
+    return;
   }
+  if constexpr (kTwoTilesBuilt<CT, D>) {
+    if (tiles_per_wave == 2) {
+      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 2>), grid, dim3(64), 0, stream, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 1>), grid, dim3(64), 0, stream, a);
+}
+
+#define PA_MFMA_CASE(CT, QT, D, BS)                                         \
+  if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS) {      \
+    launch_mfma<CT, QT, D, BS>(a, multi_query, tiles_per_wave, grid, stream); \
+    return true;                                                            \
+  }
+
+#define PA_MFMA_BS(CT, QT, D) \
+  PA_MFMA_CASE(CT, QT, D, 8)  \
+  PA_MFMA_CASE(CT, QT, D, 16) \
+  PA_MFMA_CASE(CT, QT, D, 32)
 
 // FP8 caches with a scale per row
 #define PA_MFMA_RS_CASE(QT, D, BS)                                                                    \
   if (qt == QT::code && head_dim == D && bs == BS) {                                                  \
-    hipLaunchKernelGGL((decode_mfma_kernel<FP8, QT, D, BS, false, true>), grid, dim3(64), 0, stream, a); \
+    hipLaunchKernelGGL((decode_mfma_kernel<FP8, QT, D, BS, false, true, 1>), grid, dim3(64), 0, stream, a); \
     return true;                                                                                      \
   }
 #define PA_MFMA_RS_BS(QT, D) \
@@ -484,13 +545,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   PA_MFMA_RS_CASE(QT, D, 16) \
   PA_MFMA_RS_CASE(QT, D, 32)
 
-#define PA_MFMA_BS(CT, QT, D) \
-  PA_MFMA_CASE(CT, QT, D, 8)  \
-  PA_MFMA_CASE(CT, QT, D, 16) \
-  PA_MFMA_CASE(CT, QT, D, 32)
-
-bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query, dim3 grid,
-                        hipStream_t stream) {
+// tiles_per_wave: 16-column tiles one wave computes (1, or 2 for several
+// queries per sequence spanning more than one tile)
+bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query,
+                        int tiles_per_wave, dim3 grid, hipStream_t stream) {
   if (a.k_row_scale != nullptr) {
     if (ct != FP8::code || multi_query) return false;
     PA_MFMA_RS_BS(F16, 64)

@@ -218,6 +218,7 @@ def main():
                          "pa_decode_scaled) instead of one per tensor")
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as two calls, pa_reshape_and_cache then pa_decode")
+    ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run a plain device copy of this many MiB a few times (outside the timed region), "
                          "to scale profiler byte counters")
@@ -341,6 +342,26 @@ def main():
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev] if two_calls else step_ms
     ms_step = float(np.mean(step_ms))
     ms_dec = float(np.mean(dec_ms))
+
+    # the same step captured once in a HIP graph and replayed (the cache
+    # eviction stays outside the graph and outside the events)
+    graph_ms = None
+    if not args.no_graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step()
+        torch.cuda.synchronize()
+        gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            evict()
+            gev[i][0].record()
+            g.replay()
+            gev[i][1].record()
+        torch.cuda.synchronize()
+        graph_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in gev]))
+        log(f"graph replay: {graph_ms * 1e3:.1f} us per step")
     kv_bytes = w.kv_bytes()
     if rs:  # each (position, kv head) row also carries a 4-byte K and V scale
         kv_bytes += int(w.context_lens.astype(np.int64).sum()) * w.Hkv * 4 * 2
@@ -391,6 +412,7 @@ def main():
         "attention_tflops": round(tflops, 2),
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
         "decode_us": round(ms_dec * 1e3, 2),
+        "graph_replay_us_per_step": None if graph_ms is None else round(graph_ms * 1e3, 2),
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm",
             "achieved": round(tflops if mfma_bound else achieved, 2),

@@ -15,7 +15,6 @@ bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int b
 bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, int group,
                         dim3 grid, hipStream_t stream);
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
-bool mfma_two_tiles(int ct, int head_dim);
 
 // Workgroups per (KV head, sequence) -- one for decode, more when its
 // queries hold more outputs than a workgroup has threads: merge the slices'
@@ -161,7 +160,7 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   // or two when a sequence's queries span several (the K/V loads and the V
   // transposes are then shared)
   const int col_tiles = valu ? 1 : (int)(((int64_t)nq * r.G + 15) / 16);
-  const int tw = mq && col_tiles >= 2 && mfma_two_tiles(r.cache_dtype, r.D) ? 2 : 1;
+  const int tw = mq && col_tiles >= 2 ? 2 : 1;
   const int tiles = (col_tiles + tw - 1) / tw;  // waves per (slice, KV head)
   const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq, mq);
   if (r.workspace_bytes < plan.bytes) {

@@ -424,14 +424,15 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       }
     };
 
-    // Walk over the segment's chunks with the next chunk (two chunks for fp8
-    // caches, whose chunk is half the bytes) in flight while one is computed,
-    // so a wave keeps ~16 KiB requested.  Later chunks are always requested
-    // (past the end every lane reads the last row), so no load sits under a
-    // branch and each wait covers only the chunk it needs.  (Under MQ a tile
-    // with no query of this sequence among its columns skips the segment.)
-    if (MQ && 16 * TW * ht >= hc.nqs * a.G) {
-    } else if constexpr (!kFp8) {
+    // Walk over the segment's chunks with the next chunk in flight while one
+    // is computed (16 KiB requested per wave for 16-bit caches, 8 KiB for
+    // fp8, whose waves are bound by instruction issue rather than by bytes in
+    // flight: a third buffer measured 3% slower there).  Later chunks are
+    // always requested (past the end every lane reads the last row), so no
+    // load sits under a branch and each wait covers only the chunk it needs.
+    // (Under MQ a tile with no query of this sequence among its columns skips
+    // the segment.)
+    if (!MQ || 16 * TW * ht < hc.nqs * a.G) {
       Raw buf0, buf1;
       Scales sc0, sc1;
       load_chunk(0, buf0, sc0);
@@ -443,25 +444,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         ring.advance();
         load_chunk(c + 2, buf0, sc0);
         compute_chunk(c + 1, buf1, sc1);
-      }
-    } else {
-      Raw buf0, buf1, buf2;
-      Scales sc0, sc1, sc2;
-      load_chunk(0, buf0, sc0);
-      ring.advance();
-      load_chunk(1, buf1, sc1);
-      for (int c = 0; c < nchunks; c += 3) {
-        ring.advance();
-        load_chunk(c + 2, buf2, sc2);
-        compute_chunk(c, buf0, sc0);
-        if (c + 1 >= nchunks) break;
-        ring.advance();
-        load_chunk(c + 3, buf0, sc0);
-        compute_chunk(c + 1, buf1, sc1);
-        if (c + 2 >= nchunks) break;
-        ring.advance();
-        load_chunk(c + 4, buf1, sc1);
-        compute_chunk(c + 2, buf2, sc2);
       }
     }
 
@@ -500,27 +482,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// Two tiles per wave need room for a second query operand, accumulator and
-// softmax state; fp8 caches at head_dim 128 (three row buffers) would spill,
-// so they keep one tile per wave.
-template <class CT, int D>
-constexpr bool kTwoTilesBuilt = !(std::is_same<CT, FP8>::value && D == 128);
-
-bool mfma_two_tiles(int ct, int head_dim) { return !(ct == FP8::code && head_dim == 128); }
-
 template <class CT, class QT, int D, int BS>
 void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, dim3 grid, hipStream_t stream) {
   if (!multi_query) {
     hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, false, false, 1>), grid, dim3(64), 0, stream, a);
     return;
   }
-  if constexpr (kTwoTilesBuilt<CT, D>) {
-    if (tiles_per_wave == 2) {
-      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 2>), grid, dim3(64), 0, stream, a);
-      return;
-    }
-  }
-  hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 1>), grid, dim3(64), 0, stream, a);
+  if (tiles_per_wave == 2)
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 2>), grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 1>), grid, dim3(64), 0, stream, a);
 }
 
 #define PA_MFMA_CASE(CT, QT, D, BS)                                         \

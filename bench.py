@@ -213,6 +213,9 @@ def main():
     ap.add_argument("--identity-tables", action="store_true",
                     help="ablation: move every sequence's blocks into consecutive physical blocks, in order "
                          "(same values, no scattered indirection)")
+    ap.add_argument("--group", type=int, default=0,
+                    help="decode workloads: the same lengths, KV heads and dtypes with this many query heads per KV "
+                         "head (a fresh seeded layout and values; for kernel-choice measurements)")
     ap.add_argument("--row-scales", action="store_true",
                     help="FP8 workloads: one scale per (slot, kv head) row (pa_reshape_and_cache_scaled + "
                          "pa_decode_scaled) instead of one per tensor")
@@ -237,6 +240,11 @@ def main():
 
     dev = torch.device("cuda:0")
     w = W.make(args.config)
+    if args.group:
+        if w.query_start is not None or w.name == "shared_prefix":
+            raise SystemExit("--group applies to the plain decode workloads")
+        w = W.custom(f"{w.name}_g{args.group}", w.seed, w.context_lens, w.Hkv * args.group, w.Hkv, w.D, w.bs,
+                     w.cache_dtype, w.q_dtype)
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} bs={w.bs} cache={w.cache_dtype} "
         f"sum(L)={int(w.context_lens.sum())}")
     multi = w.query_start is not None  # several queries per sequence: pa_decode_multi
@@ -401,7 +409,7 @@ def main():
         "dtype": {"f16": "f16", "bf16": "bf16", "fp8": "fp8e4m3"}[w.cache_dtype],
         "data": "synthetic",
         "config": {
-            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+            "workload": w.name, "decode_kernel": os.environ.get("PA_DECODE_VARIANT", "default"), "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
             "block_size": w.bs, "cache_dtype": w.cache_dtype, "q_dtype": w.q_dtype, "seed": w.seed,
             "sum_context_len": int(w.context_lens.sum()), "kv_bytes": kv_bytes, "parallelism": "single-gpu",
             "l2_mall_flush_between_steps": flush is not None, "identity_tables": args.identity_tables,

@@ -139,7 +139,8 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_gro
  *                  max_context_len) bytes; its contents need no
  *                  initialisation and are scratch after the call.
  * Environment: PA_DECODE_VARIANT=valu|mfma forces one of the two kernel
- * families (default: VALU/DPP for gqa_group <= 2, MFMA otherwise).
+ * families (default: MFMA for every group size; the VALU/DPP kernel is built
+ * for groups 1 and 2, and for group 4 at head_dim 128 and block size 16).
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t B,

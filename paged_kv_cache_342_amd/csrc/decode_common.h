@@ -92,12 +92,6 @@ __device__ __forceinline__ void query_range(const DecodeArgs& a, const int* qs, 
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// context length of sequence s, clamped to [0, max_ctx]
-__device__ __forceinline__ int context_len(const DecodeArgs& a, int s) {
-  const int L = uniform(a.context_lens[s]);
-  return L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
-}
-
 __device__ __forceinline__ int wave_inclusive_sum(int x) {
   const int lane = __lane_id();
 #pragma unroll

@@ -140,9 +140,14 @@ int decode_variant_override() {
   return 0;
 }
 
-bool decode_uses_valu(int variant, int G) { return variant == 1 || (variant == 0 && G <= 2); }
-
-bool decode_valu_supported(int ct, int qt, int D, int bs, int G) { return valu_supports(ct, qt, D, bs, G); }
+// The MFMA kernel is the default for every group size: even at groups 1 and 2,
+// where most of its 16-column tile is padding, it issues far fewer
+// instructions per chunk than the VALU/DPP kernel and measured 9-26% faster
+// on both cache dtypes; the VALU/DPP kernel stays selectable.
+bool decode_uses_valu(int variant, int G) {
+  (void)G;
+  return variant == 1;
+}
 
 static int elem_size(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
 

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     // The next chunk (two chunks for fp8 caches) is in flight while one is
     // computed; later chunks are always requested (past the end every lane
     // reads the last row), so no load sits under a branch.
-    if constexpr (e == 2) {
+    if constexpr (true) {
       Raw buf0, buf1;
       load_chunk(0, buf0);
       for (int ch = 0; ch < nchunks; ch += 2) {

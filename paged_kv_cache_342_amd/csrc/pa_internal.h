@@ -65,7 +65,6 @@ struct DecodeRequest {
 // 0 = default choice, 1 = VALU/DPP kernel, 2 = MFMA kernel
 int decode_variant_override();
 bool decode_uses_valu(int variant, int G);
-bool decode_valu_supported(int ct, int qt, int D, int bs, int G);
 
 pa_status decode_launch(const DecodeRequest& r, hipStream_t stream);
 

@@ -256,10 +256,10 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
       }
     };
 
-    // The next chunk (two chunks for fp8 caches) is in flight while one is
-    // computed; later chunks are always requested (past the end every lane
-    // reads the last row), so no load sits under a branch.
-    if constexpr (true) {
+    // The next chunk is in flight while one is computed; later chunks are
+    // always requested (past the end every lane reads the last row), so no
+    // load sits under a branch.
+    {
       Raw buf0, buf1;
       load_chunk(0, buf0);
       for (int ch = 0; ch < nchunks; ch += 2) {
@@ -270,24 +270,6 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
         ring.advance();
         load_chunk(ch + 2, buf0);
         compute_chunk(ch + 1, buf1);
-      }
-    } else {
-      Raw buf0, buf1, buf2;
-      load_chunk(0, buf0);
-      ring.advance();
-      load_chunk(1, buf1);
-      for (int ch = 0; ch < nchunks; ch += 3) {
-        ring.advance();
-        load_chunk(ch + 2, buf2);
-        compute_chunk(ch, buf0);
-        if (ch + 1 >= nchunks) break;
-        ring.advance();
-        load_chunk(ch + 3, buf0);
-        compute_chunk(ch + 1, buf1);
-        if (ch + 2 >= nchunks) break;
-        ring.advance();
-        load_chunk(ch + 4, buf1);
-        compute_chunk(ch + 2, buf2);
       }
     }
 

@@ -202,6 +202,41 @@ def _identity_layout(w, batch, slots_new):
     return pt[b] * w.bs + slots_new % w.bs
 
 
+def hbm_ceilings(dev, mib=512, reps=5):
+    """What plain library kernels reach on this device, timed like the step: a
+    device copy of `mib` MiB (read + written bytes counted) and a sum over 1 GiB
+    (read bytes), each after a read of another 1 GiB buffer evicts L2/MALL.
+    The median over `reps`, in GB/s."""
+    import numpy as np
+    import torch
+
+    evict = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+    src = torch.ones(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    big = torch.ones(1 << 27, dtype=torch.int64, device=dev)
+
+    def timed(fn):
+        ts = []
+        for i in range(reps + 1):
+            evict.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i:
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    t_copy = timed(lambda: dst.copy_(src))
+    t_read = timed(lambda: big.sum())
+    res = {"copy_gbs": round(2 * src.numel() / t_copy / 1e9, 1), "copy_bytes": 2 * src.numel(),
+           "read_gbs": round(big.numel() * 8 / t_read / 1e9, 1), "read_bytes": big.numel() * 8,
+           "kernels": "torch copy_ and sum"}
+    del evict, src, dst, big
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +423,9 @@ def main():
     log(f"step {ms_step * 1e3:.1f} us (median {np.median(step_ms) * 1e3:.1f}), decode {ms_dec * 1e3:.1f} us "
         f"(median {np.median(dec_ms) * 1e3:.1f}), wall/step incl. flush {wall / args.steps * 1e3:.3f} ms")
 
+    ceil = hbm_ceilings(dev)
+    log(f"plain copy {ceil['copy_gbs']} GB/s (read + write), plain read {ceil['read_gbs']} GB/s")
+
     bm = block_manager_bench(w)
     log(f"block manager: {bm['host_us_per_step']} us per step on the host, tail waste {bm['tail_waste']:.4f}")
 
@@ -424,6 +462,8 @@ def main():
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
         "decode_us": round(ms_dec * 1e3, 2),
         "graph_replay_us_per_step": None if graph_ms is None else round(graph_ms * 1e3, 2),
+        "hbm_copy": {**ceil, "frac_of_copy": round(value / ceil["copy_gbs"], 4),
+                     "frac_of_read": round(value / ceil["read_gbs"], 4)},
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm",
             "achieved": round(tflops if mfma_bound else achieved, 2),

@@ -84,8 +84,32 @@ typedef enum {
   PA_ERR_UNSUPPORTED = -2, /* valid but not built: dtype combination, head_dim, block size */
   PA_ERR_WORKSPACE = -3,   /* workspace smaller than pa_decode_workspace_size() */
   PA_ERR_HIP = -4,         /* the HIP runtime refused a launch */
-  PA_ERR_NO_BLOCKS = -5    /* block manager: the pool has too few free blocks */
+  PA_ERR_NO_BLOCKS = -5,   /* block manager: the pool has too few free blocks */
+  PA_ERR_CONTRACT = -6     /* checked build only: the device-side contract is violated */
 } pa_status;
+
+/*
+ * Checked build.  libpa_checked.so (the same sources built with PA_CHECKED)
+ * checks the device-side contract above on the device: before a call
+ * enqueues its work it runs small kernels over the device arrays the
+ * contract bounds, waits for the stream, and returns PA_ERR_CONTRACT (with
+ * pa_last_error_message() naming each violation) without enqueueing
+ * anything else, so a rejected call has no effect.  It is for debugging:
+ * every call waits for its stream.  Under stream capture the checks are
+ * captured with the work and a violation is reported by the next call made
+ * outside a capture.  The bits of what was found:
+ */
+#define PA_VIOLATION_BLOCK_ID 0x01u          /* a table entry a sequence reads lies outside [0, num_blocks) */
+#define PA_VIOLATION_CONTEXT_LEN 0x02u       /* context_lens[s] outside [0, max_context_len] */
+#define PA_VIOLATION_SLOT 0x04u              /* a slot >= num_blocks * block_size */
+#define PA_VIOLATION_SLOT_REPEATED 0x08u     /* a non-negative slot given twice in one call */
+#define PA_VIOLATION_COPY_ID 0x10u           /* a copy pair id outside [0, num_blocks) */
+#define PA_VIOLATION_COPY_DST_REPEATED 0x20u /* two copy pairs with one destination */
+#define PA_VIOLATION_COPY_DST_IS_SRC 0x40u   /* a copy destination that is another pair's source */
+#define PA_VIOLATION_QUERY_START 0x80u       /* query_start not as pa_decode_multi requires */
+
+/* 1 in libpa_checked.so, 0 in libpa.so. */
+int32_t pa_is_checked_build(void);
 
 /*
  * Append rows: for every token n in [0, T) with slot = slot_mapping[n] >= 0,

@@ -1,9 +1,13 @@
-"""Builds libpa.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Builds libpa.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
+libpa_checked.so, the same library whose entry points also check the
+device-side contract on the device (PA_CHECKED; see include/pa.h).
 
     python -m paged_kv_cache_342_amd.build
 
-Objects go to paged_kv_cache_342_amd/_build/, the library to
-paged_kv_cache_342_amd/libpa.so.  Every source is compiled on every call.
+Objects go to paged_kv_cache_342_amd/_build/, the libraries to
+paged_kv_cache_342_amd/.  Every source is compiled on every call.  The two
+libraries share the kernel objects; only the entry points and the check
+kernels are compiled with PA_CHECKED.
 """
 from __future__ import annotations
 
@@ -19,9 +23,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
+LIB_CHECKED = os.path.join(PKG, "libpa_checked.so")
 
 SOURCES = ["pa_api.hip", "decode_core.hip", "decode_mfma.hip", "decode_valu.hip", "cache_ops.hip"]
 HOST_SOURCES = ["block_manager.cpp"]  # host-only C++, built with the host compiler
+CHECKED_SOURCES = ["pa_api.hip", "contract_check.hip"]  # compiled again with PA_CHECKED
 
 ARCH = "gfx950"
 FLAGS = [
@@ -52,33 +58,43 @@ def cxx() -> str:
     raise RuntimeError("no host C++ compiler found")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(job) -> str:
+    src, checked = job
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_checked" if checked else "") + ".o")
     if src in HOST_SOURCES:
         cmd = [cxx(), "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
                "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     else:
-        cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *FLAGS, *(["-DPA_CHECKED"] if checked else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + HOST_SOURCES
-    jobs = min(len(srcs), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
-    with ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    # the slowest source first, so it never waits for a free worker
+    jobs = [(s, False) for s in SOURCES + HOST_SOURCES] + [(s, True) for s in CHECKED_SOURCES]
+    jobs.sort(key=lambda j: j[0] != "decode_mfma.hip")
+    workers = min(len(jobs), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with ThreadPoolExecutor(workers) as ex:
+        objs = dict(zip(jobs, ex.map(_compile, jobs)))
+    release = [objs[(s, False)] for s in SOURCES + HOST_SOURCES]
+    checked = [objs[(s, s in CHECKED_SOURCES)] for s in SOURCES + HOST_SOURCES] + [objs[("contract_check.hip", True)]]
+    _link(release, LIB)
+    _link(checked, LIB_CHECKED)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {LIB_CHECKED}", file=sys.stderr)
     return LIB
 
 

@@ -48,6 +48,14 @@ const char* pa_version(void) { return "pa-mi355x 0.1 (gfx950)"; }
 
 const char* pa_last_error_message(void) { return g_error; }
 
+int32_t pa_is_checked_build(void) {
+#ifdef PA_CHECKED
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 const char* pa_status_string(pa_status s) {
   switch (s) {
     case PA_OK: return "ok";
@@ -56,6 +64,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_WORKSPACE: return "workspace too small";
     case PA_ERR_HIP: return "HIP runtime error";
     case PA_ERR_NO_BLOCKS: return "not enough free blocks";
+    case PA_ERR_CONTRACT: return "device-side contract violated";
   }
   return "unknown status";
 }
@@ -82,6 +91,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "%s: null key/value/slot_mapping", fn);
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8))
     return fail(PA_ERR_INVALID_ARG, "%s: misaligned key/value/slot_mapping", fn);
+  PA_CONTRACT(check_slots_contract(fn, slot_mapping, T, num_blocks * block_size, reinterpret_cast<hipStream_t>(stream)));
   return scatter_launch(key, value, k_cache, v_cache, slot_mapping, T, num_kv_heads, head_dim, block_size,
                         num_blocks, src_dtype, cache_dtype, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream));
 }
@@ -187,6 +197,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                                       max_blocks_per_seq, max_context_len, scale, k_scale, v_scale, q_dtype,
                                       cache_dtype, out_dtype, workspace, workspace_bytes, 1, false, r);
   if (st != PA_OK || B == 0) return st;
+  PA_CONTRACT(check_decode_contract("pa_decode", r, reinterpret_cast<hipStream_t>(stream)));
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -214,6 +225,7 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
   r.new_k = key;
   r.new_v = value;
   r.src_dtype = src_dtype;
+  PA_CONTRACT(check_decode_contract(fn, r, reinterpret_cast<hipStream_t>(stream)));
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -235,6 +247,7 @@ pa_status pa_reshape_and_cache_scaled(const void* key, const void* value, void* 
   if (!key || !value || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "%s: null key/value/slot_mapping", fn);
   if (!aligned(key, 16) || !aligned(value, 16) || !aligned(slot_mapping, 8))
     return fail(PA_ERR_INVALID_ARG, "%s: misaligned key/value/slot_mapping", fn);
+  PA_CONTRACT(check_slots_contract(fn, slot_mapping, T, num_blocks * block_size, reinterpret_cast<hipStream_t>(stream)));
   return scatter_rows_launch(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping, T, num_kv_heads,
                              head_dim, block_size, num_blocks, src_dtype, reinterpret_cast<hipStream_t>(stream));
 }
@@ -257,6 +270,7 @@ pa_status pa_decode_scaled(void* out, const void* q, const void* k_cache, const 
     return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned scale pools", fn);
   r.k_row_scale = k_scales;
   r.v_row_scale = v_scales;
+  PA_CONTRACT(check_decode_contract(fn, r, reinterpret_cast<hipStream_t>(stream)));
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -294,6 +308,7 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
   r.q_start = query_start;
   r.nq = max_queries;
   r.q_rows = total_queries;
+  PA_CONTRACT(check_decode_contract(fn, r, reinterpret_cast<hipStream_t>(stream)));
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -311,6 +326,7 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
   if (N == 0) return PA_OK;
   if (!block_mapping || !aligned(block_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned block_mapping", fn);
   const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(cache_dtype);
+  PA_CONTRACT(check_pairs_contract(fn, block_mapping, N, num_blocks, reinterpret_cast<hipStream_t>(stream)));
   return copy_blocks_launch(k_cache, v_cache, block_mapping, N, block_bytes, num_blocks,
                             reinterpret_cast<hipStream_t>(stream));
 }

@@ -85,4 +85,22 @@ pa_status append_last_launch(const void* key, const void* value, void* k_cache, 
 pa_status copy_blocks_launch(void* k_cache, void* v_cache, const int64_t* pairs, int N,
                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
 
+// Checked build (PA_CHECKED): device-side contract checks run before a
+// call's work; PA_ERR_CONTRACT when violated (contract_check.hip).
+pa_status check_decode_contract(const char* fn, const DecodeRequest& r, hipStream_t stream);
+pa_status check_slots_contract(const char* fn, const int64_t* slots, int T, int64_t num_slots, hipStream_t stream);
+pa_status check_pairs_contract(const char* fn, const int64_t* pairs, int N, int64_t num_blocks, hipStream_t stream);
+
+#ifdef PA_CHECKED
+#define PA_CONTRACT(call)              \
+  do {                                 \
+    const pa_status cst_ = (call);     \
+    if (cst_ != PA_OK) return cst_;    \
+  } while (0)
+#else
+#define PA_CONTRACT(call) \
+  do {                    \
+  } while (0)
+#endif
+
 }  // namespace pa

@@ -28,9 +28,27 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings_and_version():
     lib = pa.library()
-    for code in (0, -1, -2, -3, -4):
-        assert lib.pa_status_string(code)
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.pa_status_string(code) != b"unknown status"
     assert b"gfx950" in lib.pa_version()
+    assert lib.pa_is_checked_build() == 0
+
+
+def test_checked_library_exports_the_same_symbols():
+    """libpa_checked.so (device-side contract checks) declares the same ABI and
+    says it is the checked build; switching back restores libpa.so."""
+    pa.use_checked_library(True)
+    try:
+        lib = pa.library()
+        assert lib.pa_is_checked_build() == 1
+        for n in _declared():
+            assert hasattr(lib, n), n
+        # host validation is unchanged: this fails before any check kernel runs
+        st = lib.pa_copy_blocks(FAKE, FAKE, FAKE, -1, 2, 128, 16, 10, pa.F16, None)
+        assert st == pa.ERR_INVALID_ARG
+    finally:
+        pa.use_checked_library(False)
+    assert pa.library().pa_is_checked_build() == 0
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first

@@ -29,6 +29,10 @@ Cache Problem" on infra.bea.ai = P3):
   in FP16; P2 "Common Misconceptions", capacity formula).
 * FP8 KV cache (P3 "What's Still Unsolved"): OCP E4M3FN codes, one fp32 scale
   per tensor; value = decode(code) x scale.
+* FP4 KV cache (the same passage names FP4): OCP E2M1 codes (the element type
+  of the OCP Microscaling formats: sign, 2 exponent bits, 1 mantissa bit,
+  largest magnitude 6), two per byte, with one fp32 scale per (slot, kv head)
+  row.
 
 Readings where the pages are silent (each stated where it is used): block
 layout [num_blocks, kv_heads, block_size, head_dim]; slot = block x bs +
@@ -38,7 +42,9 @@ an empty context gives an all-zero output; FP8 encode = fp32 division by the
 scale, round to nearest even, saturate to +-448, NaN kept as NaN.
 
 Storage conventions: f16 = numpy.float16; bf16 = numpy.uint16 bit pattern;
-fp8 = numpy.uint8 E4M3FN code.
+fp8 = numpy.uint8 E4M3FN code; fp4 = numpy.uint8 holding two E2M1 codes,
+element 2i in the low nibble and element 2i + 1 in the high one (a row of D
+elements is D / 2 bytes).
 """
 from __future__ import annotations
 
@@ -48,6 +54,7 @@ from typing import Optional
 import numpy as np
 
 E4M3_MAX = 448.0
+E2M1_MAX = 6.0
 
 
 # ---------------------------------------------------------------------------
@@ -141,6 +148,65 @@ def e4m3_decode(codes, scale: float = 1.0) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# FP4 E2M1 codec (the element type of the OCP Microscaling formats spec;
+# "PagedAttention - The KV Cache Problem", "What's Still Unsolved", names FP4
+# KV caches)
+# ---------------------------------------------------------------------------
+
+def e2m1_values() -> np.ndarray:
+    """Value of each of the 16 codes: sign (bit 3), 2 exponent bits (bias 1),
+    1 mantissa bit; exponent 0 is subnormal (0 and 0.5); no infinities, no NaN."""
+    out = np.empty(16, np.float64)
+    for c in range(16):
+        s = -1.0 if c & 0x8 else 1.0
+        e = (c >> 1) & 0x3
+        m = c & 0x1
+        out[c] = s * (0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0))
+    return out
+
+
+_E2M1 = e2m1_values()
+_E2M1_POS = _E2M1[:8]  # codes 0..7: the non-negative values, in increasing order
+
+
+def e2m1_encode(x, scale) -> np.ndarray:
+    """Quantise to E2M1 codes (one per uint8): y = fp32(x) / fp32(scale)
+    (correctly rounded fp32 division), then the nearest of the eight
+    magnitudes with ties to the even code (mantissa bit 0), magnitudes beyond
+    6 saturating to 6, the sign kept (-0 stays -0).  E2M1 has no NaN: a NaN
+    element is stored as +0 (reading: the row's scale ignores it, and zero
+    keeps it out of the attention sums)."""
+    with np.errstate(over="ignore", invalid="ignore", divide="ignore"):
+        y = np.asarray(x, np.float32) / np.asarray(scale, np.float32)
+    nan = np.isnan(y)
+    neg = np.signbit(y) & ~nan
+    a = np.where(nan, 0.0, np.minimum(np.abs(y).astype(np.float64), E2M1_MAX))
+    hi = np.clip(np.searchsorted(_E2M1_POS, a, side="left"), 0, 7)  # first magnitude >= a
+    lo = np.clip(hi - 1, 0, None)
+    d_hi = _E2M1_POS[hi] - a
+    d_lo = a - _E2M1_POS[lo]
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return (code | np.where(neg, np.uint8(0x8), np.uint8(0))).astype(np.uint8)
+
+
+def e2m1_pack(codes) -> np.ndarray:
+    """Codes [..., D] (D even) -> bytes [..., D / 2]: element 2i in the low
+    nibble, element 2i + 1 in the high nibble."""
+    c = np.asarray(codes, np.uint8)
+    return (c[..., 0::2] & 0xF) | ((c[..., 1::2] & 0xF) << 4)
+
+
+def e2m1_unpack(packed) -> np.ndarray:
+    """Bytes [..., D / 2] -> codes [..., D]."""
+    p = np.asarray(packed, np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
+# ---------------------------------------------------------------------------
 # widening of storage dtypes to fp64 (exact)
 # ---------------------------------------------------------------------------
 
@@ -189,6 +255,8 @@ def new_pool(num_blocks: int, kv_heads: int, bs: int, head_dim: int, dtype: str,
     shape = (num_blocks, kv_heads, bs, head_dim)
     if dtype == "fp8":
         return np.full(shape, POISON["fp8"] if poison else 0, np.uint8)
+    if dtype == "fp4":  # no NaN code: the row scales of an unwritten slot are NaN instead
+        return np.full(shape[:-1] + (head_dim // 2,), 0x77 if poison else 0, np.uint8)
     bits = np.full(shape, POISON[dtype] if poison else 0, np.uint16)
     return bits.view(np.float16) if dtype == "f16" else bits
 
@@ -219,22 +287,23 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, bs: int, cache
 # which suits a cache that grows one token at a time)
 # ---------------------------------------------------------------------------
 
-def row_scale(rows32: np.ndarray) -> np.ndarray:
+def row_scale(rows32: np.ndarray, qmax: float = E4M3_MAX) -> np.ndarray:
     """Scale of each row (last axis = the row's elements, fp32): its largest
-    magnitude, NaN elements left out, divided by 448 in fp32, so that element
-    lands on the largest finite E4M3FN value; 1 for a row of zeros or one
-    holding an infinity."""
+    magnitude, NaN elements left out, divided by qmax (448 for E4M3FN, 6 for
+    E2M1) in fp32, so that element lands on the largest finite code; 1 for a
+    row of zeros or one holding an infinity."""
     x = np.abs(np.asarray(rows32, np.float32))
     x = np.where(np.isnan(x), np.float32(0), x)
     amax = x.max(axis=-1)
     ok = (amax > 0) & np.isfinite(amax)
-    return np.where(ok, amax / np.float32(E4M3_MAX), np.float32(1)).astype(np.float32)
+    return np.where(ok, amax / np.float32(qmax), np.float32(1)).astype(np.float32)
 
 
 def reshape_and_cache_scaled(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping, bs: int,
-                             src_dtype: str):
-    """Token n's rows into slot_mapping[n] of an FP8 cache, each (token, head)
-    row encoded against its own scale, which goes to the scale pools
+                             src_dtype: str, cache_dtype: str = "fp8"):
+    """Token n's rows into slot_mapping[n] of an FP8 (E4M3FN) or FP4 (E2M1,
+    two codes per byte) cache, each (token, head) row encoded against its own
+    scale -- largest magnitude / 448, or / 6 -- which goes to the scale pools
     [num_blocks, kv_heads, bs] (fp32); a negative slot writes nothing."""
     slots = np.asarray(slot_mapping, np.int64)
     keep = slots >= 0
@@ -242,25 +311,35 @@ def reshape_and_cache_scaled(key, value, k_cache, v_cache, k_scales, v_scales, s
     o = slots[keep] % bs
     for src, cache, scales in ((key, k_cache, k_scales), (value, v_cache, v_scales)):
         x = widen(np.asarray(src)[keep], src_dtype).astype(np.float32)  # [n, kv_heads, D]
-        s = row_scale(x)  # [n, kv_heads]
-        cache[b, :, o, :] = e4m3_encode(x, s[..., None])
+        if cache_dtype == "fp4":
+            s = row_scale(x, E2M1_MAX)  # [n, kv_heads]
+            cache[b, :, o, :] = e2m1_pack(e2m1_encode(x, s[..., None]))
+        else:
+            s = row_scale(x)
+            cache[b, :, o, :] = e4m3_encode(x, s[..., None])
         scales[b, :, o] = s
 
 
-def widen_rows(codes, scales) -> np.ndarray:
-    """fp64 values of E4M3FN codes [..., D] times their rows' scales [...]: exact."""
-    return _E4M3[np.asarray(codes, np.uint8)] * np.asarray(scales, np.float32).astype(np.float64)[..., None]
+def widen_rows(codes, scales, cache_dtype: str = "fp8") -> np.ndarray:
+    """fp64 values of a cache's rows [..., D] (FP8 codes, or FP4 bytes
+    [..., D / 2]) times their rows' scales [...]: exact."""
+    s = np.asarray(scales, np.float32).astype(np.float64)[..., None]
+    if cache_dtype == "fp4":
+        return _E2M1[e2m1_unpack(codes)] * s
+    return _E4M3[np.asarray(codes, np.uint8)] * s
 
 
 def decode_scaled(q, k_cache, v_cache, k_scales, v_scales, block_tables, context_lens, scale: float,
-                  group: int, q_dtype: str, seqs=None) -> np.ndarray:
-    """fp64 decode over an FP8 cache with a scale per row [B, Hq, D]."""
+                  group: int, q_dtype: str, seqs=None, cache_dtype: str = "fp8") -> np.ndarray:
+    """fp64 decode over an FP8 or FP4 cache with a scale per row [B, Hq, D]."""
     q = np.asarray(q)
     out = []
     for s in (range(q.shape[0]) if seqs is None else seqs):
         L = int(context_lens[s])
-        k = widen_rows(gather_kv(k_cache, block_tables[s], L), gather_kv(k_scales[..., None], block_tables[s], L)[..., 0])
-        v = widen_rows(gather_kv(v_cache, block_tables[s], L), gather_kv(v_scales[..., None], block_tables[s], L)[..., 0])
+        k = widen_rows(gather_kv(k_cache, block_tables[s], L), gather_kv(k_scales[..., None], block_tables[s], L)[..., 0],
+                       cache_dtype)
+        v = widen_rows(gather_kv(v_cache, block_tables[s], L), gather_kv(v_scales[..., None], block_tables[s], L)[..., 0],
+                       cache_dtype)
         out.append(attend(widen(q[s], q_dtype), k, v, scale, group))
     return np.stack(out) if out else np.zeros((0,) + q.shape[1:])
 

@@ -614,3 +614,149 @@ def test_row_scale_pins_catch_planted_mistakes(mistake):
     back = O.widen_rows(codes, s)
     bound_ok = np.all(np.abs(back - x) <= np.abs(x) * 2.0 ** -4 * (1 + 1e-6) + s[:, None] * 2.0 ** -10)
     assert not (top_ok and bound_ok)
+
+
+# ---------------------------------------------------------------- FP4 E2M1 with a scale per row
+
+# The eight magnitudes of the E2M1 element type as the OCP Microscaling
+# formats spec lists them, by code 0b0000 .. 0b0111 (the sign is bit 3).
+_E2M1_SPEC = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_table_against_spec_values():
+    vals = O.e2m1_values()
+    assert vals[:8].tolist() == _E2M1_SPEC
+    assert vals[8:].tolist() == [-v for v in _E2M1_SPEC]
+    assert math.copysign(1.0, vals[8]) == -1.0  # 0b1000 is -0
+
+
+def _e2m1_brute(y):
+    """Nearest signed E2M1 value to each fp32 y by scanning all 16 codes; among
+    equally near codes the one with mantissa bit 0; NaN -> 0."""
+    out = []
+    for v in np.asarray(y, np.float64).ravel():
+        if math.isnan(v):
+            out.append(0)
+            continue
+        best = None
+        for c in range(16):
+            cv = _E2M1_SPEC[c & 7] * (-1.0 if c & 8 else 1.0)
+            if (c & 8) != (8 if math.copysign(1.0, v) < 0 else 0):
+                continue  # the sign is kept, so only codes of v's sign compete
+            d = abs(min(abs(v), 6.0) - abs(cv))
+            key = (d, c & 1)
+            if best is None or key < best[0]:
+                best = (key, c)
+        out.append(best[1])
+    return np.array(out, np.uint8).reshape(np.shape(y))
+
+
+def test_e2m1_encode_against_brute_force():
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(4000) * 3, np.arange(-28, 29) * 0.25,  # every tie
+                        [1e30, -1e30, 6.0000005, 5.9999995, 0.0, -0.0, 1e-30, np.inf, -np.inf]]).astype(np.float32)
+    for scale in (1.0, 0.37, 2.0 ** -9, 1e4):
+        ours = O.e2m1_encode(x, scale)
+        with np.errstate(over="ignore"):
+            ref = _e2m1_brute(x.astype(np.float32) / np.float32(scale))
+        assert np.array_equal(ours, ref), scale
+
+
+def test_e2m1_encode_ties_saturation_and_specials():
+    enc = lambda v: int(O.e2m1_encode(np.array([v], np.float32), 1.0)[0])
+    # ties go to the code whose mantissa bit is 0
+    assert [enc(v) for v in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)] == [0, 2, 2, 4, 4, 6, 6]
+    assert [enc(v) for v in (0.2500001, 0.7499999, 5.0000005)] == [1, 1, 7]
+    assert enc(7.0) == 7 and enc(-1e30) == 0xF and enc(np.inf) == 7
+    assert enc(-0.3) == 0x9 and enc(-0.0) == 0x8 and enc(np.nan) == 0
+
+
+def test_e2m1_packing():
+    assert O.e2m1_pack(np.array([1, 2], np.uint8)).tolist() == [0x21]
+    assert O.e2m1_pack(np.array([0xF, 0x0, 0x7, 0x8], np.uint8)).tolist() == [0x0F, 0x87]
+    rng = np.random.default_rng(22)
+    c = rng.integers(0, 16, size=(5, 3, 64)).astype(np.uint8)
+    p = O.e2m1_pack(c)
+    assert p.shape == (5, 3, 32) and np.array_equal(O.e2m1_unpack(p), c)
+
+
+def test_fp4_row_scale_puts_each_rows_largest_magnitude_on_6_and_bounds_the_error():
+    x = _rows_of_many_magnitudes(23)
+    s = O.row_scale(x, 6.0)
+    codes = O.e2m1_encode(x, s[:, None])
+    big = np.argmax(np.abs(x), axis=1)
+    assert set(np.unique(codes[np.arange(len(x)), big] & 7).tolist()) == {7}
+    back = O.widen_rows(O.e2m1_pack(codes), s, "fp4")
+    y = np.abs(x) / s[:, None]
+    # half the gap between neighbouring magnitudes: 0.25 up to 2, 0.5 up to 4, 1 up to 6
+    half_gap = np.where(y <= 2, 0.25, np.where(y <= 4, 0.5, 1.0)) * s[:, None]
+    assert np.all(np.abs(back - x) <= half_gap * (1 + 1e-6))
+    assert np.array_equal(O.row_scale(np.array([[0.0, -3.0, np.nan]], np.float32), 6.0), [np.float32(0.5)])
+
+
+def test_fp4_scaled_decode_matches_attention_over_dequantised_rows():
+    """Through the pool and the tables, against torch float64 attention over
+    rows dequantised nibble by nibble with the spec's values."""
+    rng = np.random.default_rng(24)
+    Hkv, G, D, bs, L = 2, 4, 32, 8, 37
+    k = (rng.standard_normal((L, Hkv, D)) * 10.0 ** rng.uniform(-2, 2, size=(L, Hkv, 1))).astype(np.float16)
+    v = (rng.standard_normal((L, Hkv, D)) * 10.0 ** rng.uniform(-2, 2, size=(L, Hkv, 1))).astype(np.float16)
+    nb = 8
+    table = rng.permutation(nb)[:(L + bs - 1) // bs]
+    kc = O.new_pool(nb, Hkv, bs, D, "fp4")
+    vc = O.new_pool(nb, Hkv, bs, D, "fp4")
+    assert kc.shape == (nb, Hkv, bs, D // 2)
+    ks = np.full((nb, Hkv, bs), np.nan, np.float32)
+    vs = np.full((nb, Hkv, bs), np.nan, np.float32)
+    O.reshape_and_cache_scaled(k, v, kc, vc, ks, vs, O.slots_for(table, 0, L, bs), bs, "f16", "fp4")
+    q = rng.standard_normal((1, Hkv * G, D)).astype(np.float16)
+    out = O.decode_scaled(q, kc, vc, ks, vs, table[None], np.array([L]), 0.2, G, "f16", cache_dtype="fp4")[0]
+
+    def nibble_value(byte, hi):
+        c = (int(byte) >> 4) & 0xF if hi else int(byte) & 0xF
+        return _E2M1_SPEC[c & 7] * (-1.0 if c & 8 else 1.0)
+
+    kd = np.zeros((L, Hkv, D))
+    vd = np.zeros((L, Hkv, D))
+    for t in range(L):
+        b, o = table[t // bs], t % bs
+        for h in range(Hkv):
+            kd[t, h] = [nibble_value(kc[b, h, o, d // 2], d % 2) * float(ks[b, h, o]) for d in range(D)]
+            vd[t, h] = [nibble_value(vc[b, h, o, d // 2], d % 2) * float(vs[b, h, o]) for d in range(D)]
+    ref = _sdpa(q[0].astype(np.float64), kd, vd, 0.2, G)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+    # and the dequantised rows are the source rows within the codec's bound
+    assert np.all(np.abs(kd - k.astype(np.float64)) <= np.abs(k).max(axis=-1, keepdims=True) / 6 * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("mistake", ["tie_to_odd", "swapped_nibbles", "sign_dropped", "e4m3_max"])
+def test_fp4_pins_catch_planted_mistakes(mistake):
+    """Each plausible slip in an E2M1 encoder fails the brute-force pin or the
+    bound pin above."""
+    def bad_encode(x, scale):
+        y = np.asarray(x, np.float32) / np.asarray(scale, np.float32)
+        a = np.minimum(np.abs(y).astype(np.float64), 6.0)
+        d = np.abs(a[..., None] - np.array(_E2M1_SPEC))
+        if mistake == "tie_to_odd":
+            d = d - 1e-12 * (np.arange(8) % 2)
+        else:
+            d = d + 1e-12 * (np.arange(8) % 2)
+        code = np.argmin(d, axis=-1).astype(np.uint8)
+        if mistake != "sign_dropped":
+            code |= np.where(np.signbit(y), np.uint8(8), np.uint8(0))
+        return code
+
+    def bad_pack(c):
+        p = O.e2m1_pack(c)
+        return ((p >> 4) | (p << 4)) & 0xFF if mistake == "swapped_nibbles" else p
+
+    x = np.concatenate([np.arange(-24, 25) * 0.25, np.random.default_rng(25).standard_normal(199)]).astype(np.float32)
+    s = np.float32(np.abs(x).max()) / np.float32(448.0 if mistake == "e4m3_max" else 6.0)
+    codes = bad_encode(x, s)
+    brute_ok = np.array_equal(codes, _e2m1_brute(x / s))
+    back = O.widen_rows(bad_pack(codes), s, "fp4")
+    y = np.abs(x) / s
+    half_gap = np.where(y <= 2, 0.25, np.where(y <= 4, 0.5, 1.0)) * s
+    bound_ok = np.all(np.abs(back - x) <= half_gap * (1 + 1e-6))
+    top_ok = codes[np.argmax(np.abs(x))] & 7 == 7
+    assert not (brute_ok and bound_ok and top_ok)

@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "pa_decode KV GB/s (fraction of HBM peak) + seq·heads/s on 1 MI355X"
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 2500.0}  # dense 16-bit MFMA (fp8 KV is widened to 16 bits)
+# dense 16-bit MFMA (fp8 and fp4 KV are widened to 16 bits)
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 2500.0, "fp4": 2500.0}
 CSRC = os.path.join(ROOT, "paged_kv_cache_342_amd", "csrc")
 # sources of the kernels a pa_decode call runs; profiler traffic recorded for
 # other sources is stale and is not reported
@@ -52,7 +53,8 @@ def cpu_baseline(w, budget_s: float, row_scales: bool = False):
 
     log("cpu baseline: building oracle pools")
     if row_scales:
-        kc, vc = O.new_pool(w.num_blocks, w.Hkv, w.bs, w.D, "fp8"), O.new_pool(w.num_blocks, w.Hkv, w.bs, w.D, "fp8")
+        cd = w.cache_dtype
+        kc, vc = O.new_pool(w.num_blocks, w.Hkv, w.bs, w.D, cd), O.new_pool(w.num_blocks, w.Hkv, w.bs, w.D, cd)
         ks = np.ones((w.num_blocks, w.Hkv, w.bs), np.float32)
         vs = ks.copy()
         for s in range(w.B):
@@ -60,7 +62,7 @@ def cpu_baseline(w, budget_s: float, row_scales: bool = False):
             if L:
                 k, v = w.seq_kv(s)
                 O.reshape_and_cache_scaled(k, v, kc, vc, ks, vs, O.slots_for(w.block_tables[s], 0, L, w.bs), w.bs,
-                                           w.src_dtype)
+                                           w.src_dtype, cd)
     else:
         kc, vc = OH.build_pools(w)
     q = w.query()
@@ -73,7 +75,7 @@ def cpu_baseline(w, budget_s: float, row_scales: bool = False):
             t0 = time.perf_counter()
             if row_scales:
                 O.decode_scaled(q, kc, vc, ks, vs, w.block_tables, w.context_lens, w.scale, w.group, w.q_dtype,
-                                seqs=[s])
+                                seqs=[s], cache_dtype=cd)
             elif w.query_start is None:
                 O.decode_one(q[s], kc, vc, w.block_tables[s], int(w.context_lens[s]), w.scale, w.group,
                              w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale)
@@ -82,7 +84,7 @@ def cpu_baseline(w, budget_s: float, row_scales: bool = False):
                                w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale, seqs=[s])
             t_total += time.perf_counter() - t0
             done_seqs += 1
-            kv += int(w.context_lens[s]) * w.Hkv * w.D * 2 * (1 if w.cache_dtype == "fp8" else 2)
+            kv += int(w.context_lens[s]) * w.Hkv * w.D * 2 * {"fp8": 8, "fp4": 4}.get(w.cache_dtype, 16) // 8
             if t_total >= budget_s:
                 break
         passes += 1
@@ -254,6 +256,9 @@ def main():
     ap.add_argument("--row-scales", action="store_true",
                     help="FP8 workloads: one scale per (slot, kv head) row (pa_reshape_and_cache_scaled + "
                          "pa_decode_scaled) instead of one per tensor")
+    ap.add_argument("--fp4", action="store_true",
+                    help="decode workloads: the same lengths and shapes with an FP4 (E2M1) cache, a scale per row "
+                         "(fresh seeded values; implies --row-scales)")
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as two calls, pa_reshape_and_cache then pa_decode")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
@@ -280,13 +285,18 @@ def main():
             raise SystemExit("--group applies to the plain decode workloads")
         w = W.custom(f"{w.name}_g{args.group}", w.seed, w.context_lens, w.Hkv * args.group, w.Hkv, w.D, w.bs,
                      w.cache_dtype, w.q_dtype)
+    if args.fp4:
+        if w.query_start is not None or w.name == "shared_prefix":
+            raise SystemExit("--fp4 applies to the plain decode workloads")
+        w = W.custom(f"{w.name}_fp4", w.seed, w.context_lens, w.Hq, w.Hkv, w.D, w.bs, "fp4", w.q_dtype)
+        args.row_scales = True
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} bs={w.bs} cache={w.cache_dtype} "
         f"sum(L)={int(w.context_lens.sum())}")
     multi = w.query_start is not None  # several queries per sequence: pa_decode_multi
     if multi and (args.unfused or args.identity_tables or args.row_scales):
         raise SystemExit("--unfused, --identity-tables and --row-scales apply to the decode workloads only")
-    if args.row_scales and w.cache_dtype != "fp8":
-        raise SystemExit("--row-scales applies to FP8 workloads")
+    if args.row_scales and w.cache_dtype not in ("fp8", "fp4"):
+        raise SystemExit("--row-scales applies to FP8 (and FP4) workloads")
     rs = args.row_scales
     batch = DeviceBatch(w, device=dev, skip_last_append=not multi, row_scales=rs)
     if multi:  # the step re-appends the query tokens' own rows, then attends
@@ -444,7 +454,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": {"f16": "f16", "bf16": "bf16", "fp8": "fp8e4m3"}[w.cache_dtype],
+        "dtype": {"f16": "f16", "bf16": "bf16", "fp8": "fp8e4m3", "fp4": "fp4e2m1"}[w.cache_dtype],
         "data": "synthetic",
         "config": {
             "workload": w.name, "decode_kernel": os.environ.get("PA_DECODE_VARIANT", "default"), "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,

@@ -40,7 +40,8 @@
  *   - Element dtypes: PA_F16 / PA_BF16 are IEEE half / bfloat16;
  *     PA_FP8_E4M3 is the OCP E4M3FN 8-bit format (bias 7, max 448, no
  *     infinities, S.1111.111 = NaN) with one fp32 scale per tensor:
- *     value = decode(code) * scale.
+ *     value = decode(code) * scale, or one per row (the *_scaled calls);
+ *     PA_FP4_E2M1 is OCP E2M1 (max 6), only with a scale per row.
  *   - Ownership: the caller allocates and owns every buffer.  All pointers
  *     are device pointers except where stated; each must be 16-byte aligned.
  *     The library never allocates, frees or synchronises device memory and
@@ -75,7 +76,8 @@ typedef enum {
   PA_F32 = 0,
   PA_F16 = 1,
   PA_BF16 = 2,
-  PA_FP8_E4M3 = 3
+  PA_FP8_E4M3 = 3,
+  PA_FP4_E2M1 = 4 /* OCP E2M1, two per byte (element 2i in the low nibble); row-scaled caches only */
 } pa_dtype;
 
 typedef enum {
@@ -196,34 +198,49 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  * call that fails has no effect.
  */
 /*
- * FP8 cache with one scale per (slot, kv head) row ("PagedAttention - The KV
- * Cache Problem", section "What's Still Unsolved": FP8/FP4 quantized KV
- * caches).  pa_reshape_and_cache_scaled writes each (token, head) row as
- * E4M3FN codes of fp32(x) / s with s = (largest |x| of the row, NaN left out)
- * / 448 in fp32 -- 1 for a row of zeros or one holding an infinity -- and
- * stores s at the row's place in the scale pools; the encoder is the one of
- * pa_reshape_and_cache.  A row's scale is fixed when the row is written, so
- * appending one token at a time never re-encodes earlier rows, and rows of
- * very different magnitudes keep their own precision.
+ * FP8 or FP4 cache with one scale per (slot, kv head) row ("PagedAttention -
+ * The KV Cache Problem", section "What's Still Unsolved": FP8/FP4 quantized
+ * KV caches).  pa_reshape_and_cache_scaled writes each (token, head) row as
+ * codes of fp32(x) / s with s = (largest |x| of the row, NaN left out) / qmax
+ * in fp32 -- 1 for a row of zeros or one holding an infinity -- and stores s
+ * at the row's place in the scale pools.
+ *   PA_FP8_E4M3: qmax = 448, the encoder of pa_reshape_and_cache; a row is
+ *                  head_dim bytes.
+ *   PA_FP4_E2M1: qmax = 6; OCP E2M1 codes (0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ *                  negatives; the element type of the OCP Microscaling
+ *                  formats), nearest with ties to the even code, saturating
+ *                  at 6, a NaN element stored as +0; two codes per byte,
+ *                  element 2i in the low nibble, so a row is head_dim / 2
+ *                  bytes and the caches are [num_blocks, num_kv_heads,
+ *                  block_size, head_dim / 2].
+ * A row's scale is fixed when the row is written, so appending one token at
+ * a time never re-encodes earlier rows, and rows of very different
+ * magnitudes keep their own precision.
  *   k_scales, v_scales [num_blocks, num_kv_heads, block_size] fp32 (device;
- *                  4 bytes per 128-byte row at head_dim 128)
- *   k_cache, v_cache  PA_FP8_E4M3; key, value f16 or bf16; slot_mapping as
- *                  for pa_reshape_and_cache.
+ *                  4 bytes per 128-byte FP8 row at head_dim 128, per 64-byte
+ *                  FP4 row)
+ *   cache_dtype    PA_FP8_E4M3 or PA_FP4_E2M1; key, value f16 or bf16;
+ *                  slot_mapping as for pa_reshape_and_cache.
  * pa_decode_scaled is pa_decode over such a cache: K[t, h, :] =
  * k_scales[b, h, t % bs] * decode(k_cache[b, h, t % bs, :]) with
  * b = block_tables[s][t / bs], V likewise; the workspace is pa_decode's.
- * The kernel is the MFMA one for every group size.
+ * The kernel is the MFMA one for every group size.  pa_copy_blocks_scaled
+ * is pa_copy_blocks for such a cache: it copies the blocks' rows and their
+ * scales.
  */
 pa_status pa_reshape_and_cache_scaled(const void* key, const void* value, void* k_cache, void* v_cache,
                                       float* k_scales, float* v_scales, const int64_t* slot_mapping, int32_t T,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                      pa_dtype src_dtype, pa_stream_t stream);
+                                      pa_dtype src_dtype, pa_dtype cache_dtype, pa_stream_t stream);
+pa_status pa_copy_blocks_scaled(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                                const int64_t* block_mapping, int32_t N, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, pa_dtype cache_dtype, pa_stream_t stream);
 pa_status pa_decode_scaled(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
                            const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
                            int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                            int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
-                           int32_t max_context_len, float scale, pa_dtype q_dtype, pa_dtype out_dtype,
-                           void* workspace, size_t workspace_bytes, pa_stream_t stream);
+                           int32_t max_context_len, float scale, pa_dtype q_dtype, pa_dtype cache_dtype,
+                           pa_dtype out_dtype, void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /*
  * Several query tokens per sequence over the same paged cache: the tokens of
@@ -270,7 +287,8 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
 /*
  * Copy-on-write: for each n < N with (src, dst) = block_mapping[n],
  *   k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src]
- * byte for byte (whole [num_kv_heads, block_size, head_dim] chunks).
+ * byte for byte (whole [num_kv_heads, block_size, head_dim] chunks; an
+ * FP4 chunk is [num_kv_heads, block_size, head_dim / 2] bytes).
  *   block_mapping  [N, 2] int64, device; pairs with an id outside
  *                  [0, num_blocks) or src == dst are skipped.
  * N == 0 is a no-op.

@@ -22,12 +22,19 @@ LIB_PATH = os.path.join(_PKG, "libpa.so")
 # the device and reject a violating call (include/pa.h, "Checked build")
 LIB_CHECKED_PATH = os.path.join(_PKG, "libpa_checked.so")
 
-F32, F16, BF16, FP8_E4M3 = 0, 1, 2, 3
+F32, F16, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NO_BLOCKS, ERR_CONTRACT = 0, -1, -2, -3, -4, -5, -6
 VIOLATION_BLOCK_ID, VIOLATION_CONTEXT_LEN, VIOLATION_SLOT, VIOLATION_SLOT_REPEATED = 0x01, 0x02, 0x04, 0x08
 VIOLATION_COPY_ID, VIOLATION_COPY_DST_REPEATED, VIOLATION_COPY_DST_IS_SRC, VIOLATION_QUERY_START = 0x10, 0x20, 0x40, 0x80
 
-_TORCH_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3}
+# an FP4 cache holds two E2M1 codes per byte: torch.float4_e2m1fn_x2, last dim head_dim / 2
+_TORCH_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3,
+               torch.float4_e2m1fn_x2: FP4_E2M1}
+
+
+def _head_dim(cache: torch.Tensor) -> int:
+    """head_dim of a cache [num_blocks, Hkv, bs, row]: the row holds two FP4 codes per element."""
+    return cache.shape[-1] * (2 if cache.dtype == torch.float4_e2m1fn_x2 else 1)
 
 _libs = {}
 _checked = os.environ.get("PA_LIBRARY", "") == "checked"
@@ -74,10 +81,10 @@ def _load(path: str) -> ctypes.CDLL:
     lib.pa_decode_append.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32,
                                      f32, f32, i32, i32, i32, p, sz, p]
     lib.pa_decode_append.restype = ctypes.c_int
-    lib.pa_reshape_and_cache_scaled.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i64, i32, p]
+    lib.pa_reshape_and_cache_scaled.argtypes = [p, p, p, p, p, p, p, i32, i32, i32, i32, i64, i32, i32, p]
     lib.pa_reshape_and_cache_scaled.restype = ctypes.c_int
     lib.pa_decode_scaled.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32, i32, i32,
-                                     p, sz, p]
+                                     i32, p, sz, p]
     lib.pa_decode_scaled.restype = ctypes.c_int
     lib.pa_decode_multi_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
     lib.pa_decode_multi_workspace_size.restype = sz
@@ -86,6 +93,8 @@ def _load(path: str) -> ctypes.CDLL:
     lib.pa_decode_multi.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [p, p, p, i32, i32, i32, i32, i64, i32, p]
     lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_copy_blocks_scaled.argtypes = [p, p, p, p, p, i32, i32, i32, i32, i64, i32, p]
+    lib.pa_copy_blocks_scaled.restype = ctypes.c_int
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_last_error_message.argtypes = []
@@ -240,8 +249,9 @@ def decode_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 def reshape_and_cache_scaled(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                              k_scales: torch.Tensor, v_scales: torch.Tensor, slot_mapping: torch.Tensor) -> None:
-    """Write key/value rows [T, Hkv, D] (f16/bf16) into an FP8 cache [num_blocks, Hkv, bs, D], each
-    (token, head) row against its own scale (largest magnitude / 448), stored in k_scales / v_scales
+    """Write key/value rows [T, Hkv, D] (f16/bf16) into an FP8 cache [num_blocks, Hkv, bs, D]
+    (float8_e4m3fn) or an FP4 cache [num_blocks, Hkv, bs, D / 2] (float4_e2m1fn_x2), each (token,
+    head) row against its own scale (largest magnitude / 448, or / 6), stored in k_scales / v_scales
     [num_blocks, Hkv, bs] float32."""
     for t, n in ((key, "key"), (value, "value"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _require(t, n)
@@ -249,22 +259,27 @@ def reshape_and_cache_scaled(key: torch.Tensor, value: torch.Tensor, k_cache: to
     _require(v_scales, "v_scales", torch.float32)
     _require(slot_mapping, "slot_mapping", torch.int64)
     T, Hkv, D = key.shape
-    nb, Hkv2, bs, D2 = k_cache.shape
-    if (value.shape != key.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D)
+    nb, Hkv2, bs, _ = k_cache.shape
+    if (value.shape != key.shape or v_cache.shape != k_cache.shape or (Hkv2, _head_dim(k_cache)) != (Hkv, D)
             or slot_mapping.shape != (T,) or k_scales.shape != (nb, Hkv, bs) or v_scales.shape != k_scales.shape):
         raise ValueError("shape mismatch between key/value, caches, scale pools and slot_mapping")
-    if k_cache.dtype != torch.float8_e4m3fn or v_cache.dtype != torch.float8_e4m3fn:
-        raise ValueError("row scales are for FP8 (float8_e4m3fn) caches")
+    _scaled_cache(k_cache, v_cache)
     _check(library().pa_reshape_and_cache_scaled(
         _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(slot_mapping),
-        T, Hkv, D, bs, nb, _TORCH_CODE.get(key.dtype, -9), _stream(k_cache)))
+        T, Hkv, D, bs, nb, _TORCH_CODE.get(key.dtype, -9), _TORCH_CODE[k_cache.dtype], _stream(k_cache)))
+
+
+def _scaled_cache(k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+    ok = (torch.float8_e4m3fn, torch.float4_e2m1fn_x2)
+    if k_cache.dtype not in ok or v_cache.dtype != k_cache.dtype:
+        raise ValueError("row scales are for FP8 (float8_e4m3fn) and FP4 (float4_e2m1fn_x2) caches")
 
 
 def decode_scaled(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: torch.Tensor,
                   v_scales: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                   max_context_len: Optional[int] = None, out: Optional[torch.Tensor] = None,
                   out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """decode() over an FP8 cache whose rows carry their own scales ([num_blocks, Hkv, bs] float32)."""
+    """decode() over an FP8 or FP4 cache whose rows carry their own scales ([num_blocks, Hkv, bs] float32)."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _require(t, n)
     _require(k_scales, "k_scales", torch.float32)
@@ -272,12 +287,11 @@ def decode_scaled(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _require(block_tables, "block_tables", torch.int32)
     _require(context_lens, "context_lens", torch.int32)
     B, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape
-    if D2 != D or v_cache.shape != k_cache.shape or Hq % Hkv or k_scales.shape != (nb, Hkv, bs) \
+    nb, Hkv, bs, _ = k_cache.shape
+    _scaled_cache(k_cache, v_cache)
+    if _head_dim(k_cache) != D or v_cache.shape != k_cache.shape or Hq % Hkv or k_scales.shape != (nb, Hkv, bs) \
             or v_scales.shape != k_scales.shape:
         raise ValueError("q, caches and scale pools do not agree")
-    if k_cache.dtype != torch.float8_e4m3fn or v_cache.dtype != torch.float8_e4m3fn:
-        raise ValueError("row scales are for FP8 (float8_e4m3fn) caches")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [B, M] and context_lens [B]")
     M = block_tables.shape[1]
@@ -293,7 +307,7 @@ def decode_scaled(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _check(library().pa_decode_scaled(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(block_tables),
         _ptr(context_lens), B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, _TORCH_CODE.get(q.dtype, -9),
-        _TORCH_CODE.get(out.dtype, -9), _ptr(workspace), ws_bytes, _stream(q)))
+        _TORCH_CODE[k_cache.dtype], _TORCH_CODE.get(out.dtype, -9), _ptr(workspace), ws_bytes, _stream(q)))
     return out
 
 
@@ -347,11 +361,29 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: tor
     _require(k_cache, "k_cache")
     _require(v_cache, "v_cache")
     _require(block_mapping, "block_mapping", torch.int64)
-    nb, Hkv, bs, D = k_cache.shape
+    nb, Hkv, bs, _ = k_cache.shape
     N = block_mapping.shape[0] if block_mapping.numel() else 0
     _check(library().pa_copy_blocks(
-        _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping) if N else None, N, Hkv, D, bs, nb,
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping) if N else None, N, Hkv, _head_dim(k_cache), bs, nb,
         _TORCH_CODE.get(k_cache.dtype, -9), _stream(k_cache)))
+
+
+def copy_blocks_scaled(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
+                       block_mapping: torch.Tensor) -> None:
+    """copy_blocks() for an FP8 or FP4 cache with row scales: the blocks' rows and their scales."""
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _require(t, n)
+    _require(k_scales, "k_scales", torch.float32)
+    _require(v_scales, "v_scales", torch.float32)
+    _require(block_mapping, "block_mapping", torch.int64)
+    _scaled_cache(k_cache, v_cache)
+    nb, Hkv, bs, _ = k_cache.shape
+    if v_cache.shape != k_cache.shape or k_scales.shape != (nb, Hkv, bs) or v_scales.shape != k_scales.shape:
+        raise ValueError("caches and scale pools do not agree")
+    N = block_mapping.shape[0] if block_mapping.numel() else 0
+    _check(library().pa_copy_blocks_scaled(
+        _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(block_mapping) if N else None, N, Hkv,
+        _head_dim(k_cache), bs, nb, _TORCH_CODE[k_cache.dtype], _stream(k_cache)))
 
 
 def version() -> str:

@@ -85,18 +85,42 @@ __global__ __launch_bounds__(256) void scatter_kernel(const uint8_t* __restrict_
   store_row8<ST, kFp8>(kx, vx, k_cache, v_cache, dst_elem, k_scale, v_scale);
 }
 
-// Scale of one row for an FP8 cache with a scale per (slot, kv head) row:
-// the row's largest magnitude maps to 448, the largest finite E4M3FN value;
-// a row of zeros, or one holding an infinity, keeps scale 1.
-__device__ __forceinline__ float row_scale(float amax) {
-  return amax > 0.f && amax <= 3.402823466e38f ? amax / 448.0f : 1.0f;
+// Scale of one row for a cache with a scale per (slot, kv head) row: the
+// row's largest magnitude maps to qmax, the largest finite code (448 for
+// E4M3FN, 6 for E2M1); a row of zeros, or one holding an infinity, keeps
+// scale 1.
+__device__ __forceinline__ float row_scale(float amax, float qmax) {
+  return amax > 0.f && amax <= 3.402823466e38f ? amax / qmax : 1.0f;
+}
+
+// E2M1 code of fp32(x) / scale (IEEE division): the nearest of 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6 with ties to the code whose mantissa bit is 0 (the
+// thresholds below are the midpoints; a tie takes the side of the even
+// code), magnitudes beyond 6 saturating, the sign kept (-0 too).  E2M1 has
+// no NaN: a NaN element is stored as +0.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float scale) {
+  const float y = x / scale;
+  if (y != y) return 0u;
+  const float a = fabsf(y);
+  const uint32_t m = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return m | ((__float_as_uint(y) >> 28) & 0x8u);
+}
+
+// eight elements -> eight E2M1 codes in one dword, element 2i in the low
+// nibble of byte i
+__device__ __forceinline__ uint32_t encode8_fp4(const float* x, float scale) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w |= e2m1_code(x[i], scale) << (4 * i);
+  return w;
 }
 
 // One thread per 8 elements of one (token, kv head) row, the D / 8 threads
 // of a row being adjacent lanes: they share the row's largest magnitude
-// (NaN elements do not count), then write their codes; the first writes the
-// row's K and V scales.
-template <class ST>
+// (NaN elements do not count), then write their codes (8 bytes of E4M3FN,
+// or 4 bytes of E2M1 with kFp4); the first writes the row's K and V scales.
+template <class ST, bool kFp4>
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint8_t* __restrict__ key,
                                                            const uint8_t* __restrict__ value,
                                                            uint8_t* __restrict__ k_cache,
@@ -133,13 +157,19 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint8_t* __rest
     va = fmaxf(va, shfl_xor(va, m));
   }
   if (slot < 0 || slot >= num_blocks * bs) return;
-  const float ks = row_scale(ka), vs = row_scale(va);
+  constexpr float qmax = kFp4 ? 6.0f : 448.0f;
+  const float ks = row_scale(ka, qmax), vs = row_scale(va, qmax);
   const int64_t b = slot / bs;
   const int o = (int)(slot - b * bs);
   const int64_t srow = (b * Hkv + h) * bs + o;
   const int64_t dst_elem = srow * D + chunk * 8;
-  *reinterpret_cast<i32x2*>(k_cache + dst_elem) = encode8_fp8(kf, ks);
-  *reinterpret_cast<i32x2*>(v_cache + dst_elem) = encode8_fp8(vf, vs);
+  if constexpr (kFp4) {
+    *reinterpret_cast<uint32_t*>(k_cache + dst_elem / 2) = encode8_fp4(kf, ks);
+    *reinterpret_cast<uint32_t*>(v_cache + dst_elem / 2) = encode8_fp4(vf, vs);
+  } else {
+    *reinterpret_cast<i32x2*>(k_cache + dst_elem) = encode8_fp8(kf, ks);
+    *reinterpret_cast<i32x2*>(v_cache + dst_elem) = encode8_fp8(vf, vs);
+  }
   if (chunk == 0) {
     k_scales[srow] = ks;
     v_scales[srow] = vs;
@@ -148,7 +178,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint8_t* __rest
 
 pa_status scatter_rows_launch(const void* key, const void* value, void* k_cache, void* v_cache, float* k_scales,
                               float* v_scales, const int64_t* slots, int T, int Hkv, int D, int bs,
-                              int64_t num_blocks, int src_dtype, hipStream_t stream) {
+                              int64_t num_blocks, int src_dtype, int cache_dtype, hipStream_t stream) {
   if (T == 0) return PA_OK;
   const int64_t threads = (int64_t)T * Hkv * (D / 8);
   const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
@@ -156,11 +186,18 @@ pa_status scatter_rows_launch(const void* key, const void* value, void* k_cache,
   auto V = reinterpret_cast<const uint8_t*>(value);
   auto KC = reinterpret_cast<uint8_t*>(k_cache);
   auto VC = reinterpret_cast<uint8_t*>(v_cache);
-  if (src_dtype == PA_F16)
-    hipLaunchKernelGGL((scatter_rows_kernel<F16>), grid, block, 0, stream, K, V, KC, VC, k_scales, v_scales, slots,
-                       T, Hkv, D, bs, num_blocks);
+  const bool fp4 = cache_dtype == PA_FP4_E2M1;
+  if (src_dtype == PA_F16 && fp4)
+    hipLaunchKernelGGL((scatter_rows_kernel<F16, true>), grid, block, 0, stream, K, V, KC, VC, k_scales, v_scales,
+                       slots, T, Hkv, D, bs, num_blocks);
+  else if (src_dtype == PA_F16)
+    hipLaunchKernelGGL((scatter_rows_kernel<F16, false>), grid, block, 0, stream, K, V, KC, VC, k_scales, v_scales,
+                       slots, T, Hkv, D, bs, num_blocks);
+  else if (fp4)
+    hipLaunchKernelGGL((scatter_rows_kernel<BF16, true>), grid, block, 0, stream, K, V, KC, VC, k_scales, v_scales,
+                       slots, T, Hkv, D, bs, num_blocks);
   else
-    hipLaunchKernelGGL((scatter_rows_kernel<BF16>), grid, block, 0, stream, K, V, KC, VC, k_scales, v_scales,
+    hipLaunchKernelGGL((scatter_rows_kernel<BF16, false>), grid, block, 0, stream, K, V, KC, VC, k_scales, v_scales,
                        slots, T, Hkv, D, bs, num_blocks);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) {

@@ -27,11 +27,15 @@
 // their addresses and the V transposes are shared by both, only the
 // products and the softmax are per tile.
 //
-// FP8 caches with a scale per (slot, kv head) row (RS): each lane also loads
-// the scales of the positions its scores and its V values belong to (four
-// consecutive positions per 16-byte load); a score is multiplied by its K
-// row's scale, and the probability that weights a V row by that row's scale
-// (the denominator takes the probability itself).
+// FP8 and FP4 caches with a scale per (slot, kv head) row (RS): each lane
+// also loads the scales of the positions its scores and its V values belong
+// to (four consecutive positions per 16-byte load); a score is multiplied by
+// its K row's scale, and the probability that weights a V row by that row's
+// scale (the denominator takes the probability itself).  An FP4 row is
+// head_dim / 2 bytes: a lane takes a quarter of each K row as one load (so
+// the k-slot order puts D/4 consecutive elements in each lane group) and
+// head_dim / 16 elements of each V row; the hardware converts two E2M1 codes
+// per instruction, exactly, to 16 bits.
 //
 // When the launch also appends each sequence's new row (16-bit caches), the
 // loads of position L - 1 read the caller's row instead of the cache, and
@@ -44,9 +48,10 @@
 // so the accumulator is rescaled rarely.  The result is exact regardless,
 // since numerator and denominator share the same reference.
 //
-// P for the PV product: fp16 when V is fp16 or fp8 (fp8 -> fp16 is exact),
-// and a two-term bf16 split (hi + lo) when V is bf16, so the probabilities
-// keep ~16 bits.  Scores use q * k products of the 16-bit inputs, exact in
+// P for the PV product: fp16 when V is fp16 or fp8 with a scale per tensor
+// (fp8 -> fp16 is exact), and a two-term bf16 split (hi + lo) when V is bf16
+// or carries row scales, so the weights keep ~16 bits (and, with row scales,
+// the range of fp32: p * scale reaches 2^8 * max|V| / 6 for FP4).  Scores use q * k products of the 16-bit inputs, exact in
 // the fp32 accumulator; scale * log2(e) is applied in fp32 afterwards.
 #include <type_traits>
 
@@ -65,11 +70,15 @@ __device__ __forceinline__ f32x4 mfma32<BF16>(i32x4 a, i32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Registers of one 32-position chunk, as loaded from memory.
+// Registers of one 32-position chunk, as loaded from memory.  A lane takes
+// a quarter of each of 16 K rows per tile (KB bytes) and 1/16 of each of 8
+// V rows (VB bytes).
 template <class CT, int D>
 struct ChunkRaw {
-  static constexpr int KR = D * CT::bytes / 64;  // 16-byte K loads per lane per 16-row tile
-  static constexpr int VD = D * CT::bytes / 64;  // dwords of V per lane per position
+  static constexpr int KB = D * CT::bits / 32;          // K bytes per lane per 16-row tile
+  static constexpr int VB = D * CT::bits / 128;         // V bytes per lane per position
+  static constexpr int KR = KB >= 16 ? KB / 16 : 1;     // 16-byte K loads (FP4 at D = 64: one 8-byte load)
+  static constexpr int VD = VB >= 4 ? VB / 4 : 1;       // dwords of V per lane per position
   i32x4 k[2][KR];
   uint32_t v[8][VD];
 };
@@ -81,16 +90,18 @@ struct ChunkScales {
 };
 struct NoScales {};
 
-template <int N>
-__device__ __forceinline__ void load_dwords(const uint8_t* p, uint32_t* o) {
-  if constexpr (N == 4) {
+template <int BYTES>
+__device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* o) {
+  if constexpr (BYTES == 16) {
     i32x4 x = ld16_stream(p);
     o[0] = x[0]; o[1] = x[1]; o[2] = x[2]; o[3] = x[3];
-  } else if constexpr (N == 2) {
+  } else if constexpr (BYTES == 8) {
     i32x2 x = ld8_stream(p);
     o[0] = x[0]; o[1] = x[1];
-  } else {
+  } else if constexpr (BYTES == 4) {
     o[0] = ld4_stream(p);
+  } else {
+    o[0] = ld2_stream(p);
   }
 }
 
@@ -106,19 +117,22 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 
 template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int e = CT::bytes;
+  constexpr int RB = D * CT::bits / 8;  // bytes per cache row
   constexpr int KK = D / 32;   // MFMAs per QK tile
   constexpr int W = D / 16;    // V values per lane per position (one output d-run)
   constexpr bool kFp8 = std::is_same<CT, FP8>::value;
-  constexpr bool kBf16V = std::is_same<CT, BF16>::value;
+  constexpr bool kFp4 = std::is_same<CT, FP4>::value;
+  // PV in bf16 with P split in two terms: for bf16 caches, and for caches
+  // with row scales, whose weights p * scale can exceed the fp16 range
+  constexpr bool kBf16V = std::is_same<CT, BF16>::value || RS;
   using PT = typename std::conditional<kBf16V, BF16, F16>::type;  // PV operand type
   using Raw = ChunkRaw<CT, D>;
   using Scales = typename std::conditional<RS, ChunkScales, NoScales>::type;
   constexpr int VD = Raw::VD;
-  constexpr int64_t kChunkBytes = (int64_t)BS * D * e;  // one (block, head) chunk
+  constexpr int64_t kChunkBytes = (int64_t)BS * RB;  // one (block, head) chunk
   constexpr int NB = kChunk / BS;
-  constexpr bool kCanAppend = !kFp8;   // new rows are stored as given
-  constexpr int kRowLanes = D * e / 16;  // lanes that hold one row, 16 bytes each
+  constexpr bool kCanAppend = !kFp8 && !kFp4;  // new rows are stored as given
+  constexpr int kRowLanes = RB / 16;  // lanes that hold one row, 16 bytes each
 
   constexpr int kScan = MQ ? kScanMaxMQ : kScanMax;
   __shared__ int cum[kScan + 1];
@@ -204,7 +218,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       const uint8_t* qrow = reinterpret_cast<const uint8_t*>(a.q) + (qr * Hq + (live ? head[t] : h * a.G)) * D * 2;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int d = kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
+        // the k-slot order of the K loads: lane group gq holds a quarter of
+        // each row (FP4), two 16-byte pieces (fp8) or four (16-bit)
+        const int d = kFp4 ? (D / 4) * gq + 8 * kk : kFp8 ? 64 * (kk >> 1) + 16 * gq + 8 * (kk & 1) : 32 * kk + 8 * gq;
         const i32x4 x = ld16(qrow + d * 2);
         hd.qop[t][kk] = live ? x : i32x4{0, 0, 0, 0};
       }
@@ -215,9 +231,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
     int id = uniform(trow[(g.tok_end - 1) / BS]);
     const bool id_ok = id >= 0 && (int64_t)id < a.num_blocks;
     if (!id_ok) id = 0;
-    const int64_t off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * D * e;
+    const int64_t off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * RB;
     const bool app = kCanAppend && a.new_k != nullptr && g.tok_end == lens[g.s];
-    const int64_t nrow = ((int64_t)g.s * a.Hkv + h) * D * e;
+    const int64_t nrow = ((int64_t)g.s * a.Hkv + h) * RB;
     hd.last_k = app ? a.new_k + nrow : kbase + off;
     hd.last_v = app ? a.new_v + nrow : vbase + off;
     hd.lim = g.tok_end - (app ? 1 : 0);
@@ -264,11 +280,16 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         const int tc = 16 * tt + r;
         const int bsel = BS == 32 ? 0 : (BS == 16 ? tt : 2 * tt + (r >> 3));
         const bool ok = ctok + tc < lim;
-        const uint8_t* row = ok ? kbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : hc.last_k;
+        const uint8_t* row = ok ? kbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * RB : hc.last_k;
+        if constexpr (kFp4 && Raw::KB == 8) {
+          const i32x2 x = ld8_stream(row + 8 * gq);
+          raw.k[tt][0] = i32x4{x[0], x[1], 0, 0};
+        } else {
 #pragma unroll
-        for (int u = 0; u < Raw::KR; ++u) {
-          const int off = kFp8 ? 64 * u + 16 * gq : (32 * u + 8 * gq) * 2;
-          raw.k[tt][u] = ld16_stream(row + off);
+          for (int u = 0; u < Raw::KR; ++u) {
+            const int off = kFp4 ? 16 * gq : kFp8 ? 64 * u + 16 * gq : (32 * u + 8 * gq) * 2;
+            raw.k[tt][u] = ld16_stream(row + off);
+          }
         }
       }
       // V: whole rows, position slot j -> 16*(j>>2) + 4*gq + (j&3)
@@ -277,8 +298,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
         const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
         const int bsel = BS == 32 ? 0 : (BS == 16 ? (j >> 2) : 2 * (j >> 2) + (gq >> 1));
         const bool ok = ctok + tc < lim;
-        const uint8_t* row = ok ? vbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * D * e : hc.last_v;
-        load_dwords<VD>(row + W * r * e, raw.v[j]);
+        const uint8_t* row = ok ? vbase + (int64_t)id[bsel] * blk_stride + (tc % BS) * RB : hc.last_v;
+        load_bytes<Raw::VB>(row + Raw::VB * r, raw.v[j]);
       }
       if constexpr (RS) {
         // the scales of positions 16*tt + 4*gq .. + 3 (one block; past the end
@@ -310,7 +331,11 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       i32x4 kop[2][KK];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        if constexpr (kFp8) {
+        if constexpr (kFp4) {
+          // dword kk of the lane's piece: the 8 elements MFMA kk takes
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) kop[tt][kk] = fp4x8_to_16<QT>((uint32_t)raw.k[tt][0][kk]);
+        } else if constexpr (kFp8) {
 #pragma unroll
           for (int u = 0; u < Raw::KR; ++u) {
             const i32x2 lo = fp8x4_to_16<QT>((uint32_t)raw.k[tt][u][0]);
@@ -395,10 +420,20 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
       uint32_t vt[8][W / 2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        if constexpr (kFp8) {
+        if constexpr (kFp4) {
+          if constexpr (W == 8) {
+            const i32x4 x = fp4x8_to_16<PT>(raw.v[j][0]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vt[j][i] = (uint32_t)x[i];
+          } else {
+            const i32x2 x = fp4x4_to_16<PT>(raw.v[j][0]);
+            vt[j][0] = (uint32_t)x[0];
+            vt[j][1] = (uint32_t)x[1];
+          }
+        } else if constexpr (kFp8) {
 #pragma unroll
           for (int i = 0; i < VD; ++i) {
-            const i32x2 x = fp8x4_to_16<F16>(raw.v[j][i]);
+            const i32x2 x = fp8x4_to_16<PT>(raw.v[j][i]);
             vt[j][2 * i] = (uint32_t)x[0];
             vt[j][2 * i + 1] = (uint32_t)x[1];
           }
@@ -505,27 +540,34 @@ void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, dim3
   PA_MFMA_CASE(CT, QT, D, 16) \
   PA_MFMA_CASE(CT, QT, D, 32)
 
-// FP8 caches with a scale per row
-#define PA_MFMA_RS_CASE(QT, D, BS)                                                                    \
-  if (qt == QT::code && head_dim == D && bs == BS) {                                                  \
-    hipLaunchKernelGGL((decode_mfma_kernel<FP8, QT, D, BS, false, true, 1>), grid, dim3(64), 0, stream, a); \
-    return true;                                                                                      \
+// FP8 and FP4 caches with a scale per row
+#define PA_MFMA_RS_CASE(CT, QT, D, BS)                                                               \
+  if (qt == QT::code && head_dim == D && bs == BS) {                                                 \
+    hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, false, true, 1>), grid, dim3(64), 0, stream, a); \
+    return true;                                                                                     \
   }
-#define PA_MFMA_RS_BS(QT, D) \
-  PA_MFMA_RS_CASE(QT, D, 8)  \
-  PA_MFMA_RS_CASE(QT, D, 16) \
-  PA_MFMA_RS_CASE(QT, D, 32)
+#define PA_MFMA_RS_BS(CT, QT, D) \
+  PA_MFMA_RS_CASE(CT, QT, D, 8)  \
+  PA_MFMA_RS_CASE(CT, QT, D, 16) \
+  PA_MFMA_RS_CASE(CT, QT, D, 32)
 
 // tiles_per_wave: 16-column tiles one wave computes (1, or 2 for several
 // queries per sequence spanning more than one tile)
 bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query,
                         int tiles_per_wave, dim3 grid, hipStream_t stream) {
   if (a.k_row_scale != nullptr) {
-    if (ct != FP8::code || multi_query) return false;
-    PA_MFMA_RS_BS(F16, 64)
-    PA_MFMA_RS_BS(F16, 128)
-    PA_MFMA_RS_BS(BF16, 64)
-    PA_MFMA_RS_BS(BF16, 128)
+    if (multi_query) return false;
+    if (ct == FP8::code) {
+      PA_MFMA_RS_BS(FP8, F16, 64)
+      PA_MFMA_RS_BS(FP8, F16, 128)
+      PA_MFMA_RS_BS(FP8, BF16, 64)
+      PA_MFMA_RS_BS(FP8, BF16, 128)
+    } else if (ct == FP4::code) {
+      PA_MFMA_RS_BS(FP4, F16, 64)
+      PA_MFMA_RS_BS(FP4, F16, 128)
+      PA_MFMA_RS_BS(FP4, BF16, 64)
+      PA_MFMA_RS_BS(FP4, BF16, 128)
+    }
     return false;
   }
   PA_MFMA_BS(F16, F16, 64)

@@ -26,8 +26,11 @@ static pa_status fail(pa_status s, const char* fmt, ...) {
 }
 
 static bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
-static bool known_dtype(int d) { return d >= PA_F32 && d <= PA_FP8_E4M3; }
-static int elem_bytes(int d) { return d == PA_FP8_E4M3 ? 1 : (d == PA_F32 ? 4 : 2); }
+static bool known_dtype(int d) { return d >= PA_F32 && d <= PA_FP4_E2M1; }
+// bytes of one cache row of head_dim elements
+static int64_t row_bytes(int head_dim, int d) {
+  return d == PA_FP4_E2M1 ? head_dim / 2 : (int64_t)head_dim * (d == PA_FP8_E4M3 ? 1 : (d == PA_F32 ? 4 : 2));
+}
 
 #define PA_CHECK_SHAPE(fn, Hkv, D, bs, num_blocks)                                                  \
   do {                                                                                              \
@@ -81,6 +84,8 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
   if (!known_dtype(src_dtype) || !known_dtype(cache_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (src_dtype != PA_F16 && src_dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "%s: source rows must be f16 or bf16", fn);
+  if (cache_dtype == PA_FP4_E2M1)
+    return fail(PA_ERR_UNSUPPORTED, "%s: fp4 caches take a scale per row (pa_reshape_and_cache_scaled)", fn);
   if (cache_dtype != src_dtype && cache_dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "%s: cache dtype must equal the source dtype or be fp8-e4m3", fn);
   if (cache_dtype == PA_FP8_E4M3 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
@@ -116,7 +121,8 @@ static pa_status decode_request(const char* fn, void* out, const void* q, const 
                                 int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
                                 int32_t max_context_len, float scale, float k_scale, float v_scale,
                                 pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
-                                size_t workspace_bytes, int nq, bool multi_query, DecodeRequest& r) {
+                                size_t workspace_bytes, int nq, bool multi_query, bool row_scales,
+                                DecodeRequest& r) {
   if (B < 0) return fail(PA_ERR_INVALID_ARG, "%s: B must be >= 0", fn);
   if (B > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: at most 65535 sequences per call", fn);
   if (num_kv_heads < 1) return fail(PA_ERR_INVALID_ARG, "%s: num_kv_heads must be >= 1 (got %d)", fn, num_kv_heads);
@@ -132,9 +138,12 @@ static pa_status decode_request(const char* fn, void* out, const void* q, const 
   if (!known_dtype(q_dtype) || !known_dtype(cache_dtype) || !known_dtype(out_dtype))
     return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (q_dtype != PA_F16 && q_dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: q must be f16 or bf16", fn);
-  if (cache_dtype != q_dtype && cache_dtype != PA_FP8_E4M3)
-    return fail(PA_ERR_UNSUPPORTED, "%s: cache dtype must equal the q dtype or be fp8-e4m3", fn);
-  if (out_dtype == PA_FP8_E4M3) return fail(PA_ERR_UNSUPPORTED, "%s: out must be f32, f16 or bf16", fn);
+  if (cache_dtype == PA_FP4_E2M1 && !row_scales)
+    return fail(PA_ERR_UNSUPPORTED, "%s: fp4 caches take a scale per row (pa_decode_scaled)", fn);
+  if (cache_dtype != q_dtype && cache_dtype != PA_FP8_E4M3 && cache_dtype != PA_FP4_E2M1)
+    return fail(PA_ERR_UNSUPPORTED, "%s: cache dtype must equal the q dtype or be fp8-e4m3 (or fp4-e2m1)", fn);
+  if (out_dtype != PA_F32 && out_dtype != PA_F16 && out_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: out must be f32, f16 or bf16", fn);
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
   if (cache_dtype == PA_FP8_E4M3 && !(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
     return fail(PA_ERR_INVALID_ARG, "%s: fp8 scales must be finite and > 0", fn);
@@ -195,7 +204,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const pa_status st = decode_request("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, B,
                                       num_kv_heads, gqa_group, head_dim, block_size, num_blocks,
                                       max_blocks_per_seq, max_context_len, scale, k_scale, v_scale, q_dtype,
-                                      cache_dtype, out_dtype, workspace, workspace_bytes, 1, false, r);
+                                      cache_dtype, out_dtype, workspace, workspace_bytes, 1, false, false, r);
   if (st != PA_OK || B == 0) return st;
   PA_CONTRACT(check_decode_contract("pa_decode", r, reinterpret_cast<hipStream_t>(stream)));
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
@@ -214,7 +223,7 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
   const pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads,
                                       gqa_group, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                       max_context_len, scale, k_scale, v_scale, q_dtype, cache_dtype, out_dtype,
-                                      workspace, workspace_bytes, 1, false, r);
+                                      workspace, workspace_bytes, 1, false, false, r);
   if (st != PA_OK) return st;
   if (!known_dtype(src_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (cache_dtype == PA_FP8_E4M3 ? (src_dtype != PA_F16 && src_dtype != PA_BF16) : src_dtype != cache_dtype)
@@ -232,14 +241,16 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
 pa_status pa_reshape_and_cache_scaled(const void* key, const void* value, void* k_cache, void* v_cache,
                                       float* k_scales, float* v_scales, const int64_t* slot_mapping, int32_t T,
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                                      pa_dtype src_dtype, pa_stream_t stream) {
+                                      pa_dtype src_dtype, pa_dtype cache_dtype, pa_stream_t stream) {
   g_error[0] = 0;
   const char* fn = "pa_reshape_and_cache_scaled";
   if (T < 0) return fail(PA_ERR_INVALID_ARG, "%s: T must be >= 0", fn);
   PA_CHECK_SHAPE("pa_reshape_and_cache_scaled", num_kv_heads, head_dim, block_size, num_blocks);
-  if (!known_dtype(src_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (!known_dtype(src_dtype) || !known_dtype(cache_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (src_dtype != PA_F16 && src_dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "%s: source rows must be f16 or bf16", fn);
+  if (cache_dtype != PA_FP8_E4M3 && cache_dtype != PA_FP4_E2M1)
+    return fail(PA_ERR_UNSUPPORTED, "%s: row scales are for fp8-e4m3 and fp4-e2m1 caches", fn);
   if (!k_cache || !v_cache || !k_scales || !v_scales) return fail(PA_ERR_INVALID_ARG, "%s: null cache or scale pointer", fn);
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_scales, 16) || !aligned(v_scales, 16))
     return fail(PA_ERR_INVALID_ARG, "%s: cache and scale pointers must be 16-byte aligned", fn);
@@ -249,22 +260,25 @@ pa_status pa_reshape_and_cache_scaled(const void* key, const void* value, void* 
     return fail(PA_ERR_INVALID_ARG, "%s: misaligned key/value/slot_mapping", fn);
   PA_CONTRACT(check_slots_contract(fn, slot_mapping, T, num_blocks * block_size, reinterpret_cast<hipStream_t>(stream)));
   return scatter_rows_launch(key, value, k_cache, v_cache, k_scales, v_scales, slot_mapping, T, num_kv_heads,
-                             head_dim, block_size, num_blocks, src_dtype, reinterpret_cast<hipStream_t>(stream));
+                             head_dim, block_size, num_blocks, src_dtype, cache_dtype,
+                             reinterpret_cast<hipStream_t>(stream));
 }
 
 pa_status pa_decode_scaled(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scales,
                            const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
                            int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                            int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,
-                           int32_t max_context_len, float scale, pa_dtype q_dtype, pa_dtype out_dtype,
-                           void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+                           int32_t max_context_len, float scale, pa_dtype q_dtype, pa_dtype cache_dtype,
+                           pa_dtype out_dtype, void* workspace, size_t workspace_bytes, pa_stream_t stream) {
   g_error[0] = 0;
   const char* fn = "pa_decode_scaled";
+  if (cache_dtype != PA_FP8_E4M3 && cache_dtype != PA_FP4_E2M1)
+    return fail(PA_ERR_UNSUPPORTED, "%s: row scales are for fp8-e4m3 and fp4-e2m1 caches", fn);
   DecodeRequest r;
   const pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads,
                                       gqa_group, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                                      max_context_len, scale, 1.f, 1.f, q_dtype, PA_FP8_E4M3, out_dtype, workspace,
-                                      workspace_bytes, 1, false, r);
+                                      max_context_len, scale, 1.f, 1.f, q_dtype, cache_dtype, out_dtype, workspace,
+                                      workspace_bytes, 1, false, true, r);
   if (st != PA_OK || B == 0) return st;
   if (!k_scales || !v_scales || !aligned(k_scales, 16) || !aligned(v_scales, 16))
     return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned scale pools", fn);
@@ -301,7 +315,7 @@ pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const v
   const pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads,
                                       gqa_group, head_dim, block_size, num_blocks, max_blocks_per_seq,
                                       max_context_len, scale, k_scale, v_scale, q_dtype, cache_dtype, out_dtype,
-                                      workspace, workspace_bytes, max_queries, true, r);
+                                      workspace, workspace_bytes, max_queries, true, false, r);
   if (st != PA_OK) return st;
   if (B == 0 || total_queries == 0) return PA_OK;
   if (!query_start || !aligned(query_start, 4)) return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned query_start", fn);
@@ -325,10 +339,34 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* block_mapp
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return fail(PA_ERR_INVALID_ARG, "%s: cache pointers must be 16-byte aligned", fn);
   if (N == 0) return PA_OK;
   if (!block_mapping || !aligned(block_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned block_mapping", fn);
-  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_bytes(cache_dtype);
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * row_bytes(head_dim, cache_dtype);
   PA_CONTRACT(check_pairs_contract(fn, block_mapping, N, num_blocks, reinterpret_cast<hipStream_t>(stream)));
   return copy_blocks_launch(k_cache, v_cache, block_mapping, N, block_bytes, num_blocks,
                             reinterpret_cast<hipStream_t>(stream));
+}
+
+pa_status pa_copy_blocks_scaled(void* k_cache, void* v_cache, float* k_scales, float* v_scales,
+                                const int64_t* block_mapping, int32_t N, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int64_t num_blocks, pa_dtype cache_dtype, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_copy_blocks_scaled";
+  if (N < 0) return fail(PA_ERR_INVALID_ARG, "%s: N must be >= 0", fn);
+  PA_CHECK_SHAPE("pa_copy_blocks_scaled", num_kv_heads, head_dim, block_size, num_blocks);
+  if (cache_dtype != PA_FP8_E4M3 && cache_dtype != PA_FP4_E2M1)
+    return fail(PA_ERR_UNSUPPORTED, "%s: row scales are for fp8-e4m3 and fp4-e2m1 caches", fn);
+  if (!k_cache || !v_cache || !k_scales || !v_scales) return fail(PA_ERR_INVALID_ARG, "%s: null cache or scale pointer", fn);
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_scales, 16) || !aligned(v_scales, 16))
+    return fail(PA_ERR_INVALID_ARG, "%s: cache and scale pointers must be 16-byte aligned", fn);
+  if (N == 0) return PA_OK;
+  if (!block_mapping || !aligned(block_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned block_mapping", fn);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  PA_CONTRACT(check_pairs_contract(fn, block_mapping, N, num_blocks, st));
+  const pa_status s1 = copy_blocks_launch(k_cache, v_cache, block_mapping, N,
+                                          (int64_t)num_kv_heads * block_size * row_bytes(head_dim, cache_dtype),
+                                          num_blocks, st);
+  if (s1 != PA_OK) return s1;
+  return copy_blocks_launch(k_scales, v_scales, block_mapping, N, (int64_t)num_kv_heads * block_size * 4, num_blocks,
+                            st);
 }
 
 }  // extern "C"

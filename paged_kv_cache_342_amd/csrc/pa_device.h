@@ -15,10 +15,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// element-type tags
-struct F16 { static constexpr int bytes = 2; static constexpr int code = 1; };
-struct BF16 { static constexpr int bytes = 2; static constexpr int code = 2; };
-struct FP8 { static constexpr int bytes = 1; static constexpr int code = 3; };
+// element-type tags (bits per element; codes are pa_dtype values)
+struct F16 { static constexpr int bytes = 2; static constexpr int bits = 16; static constexpr int code = 1; };
+struct BF16 { static constexpr int bytes = 2; static constexpr int bits = 16; static constexpr int code = 2; };
+struct FP8 { static constexpr int bytes = 1; static constexpr int bits = 8; static constexpr int code = 3; };
+// OCP E2M1, two per byte, element 2i in the low nibble
+struct FP4 { static constexpr int bits = 4; static constexpr int code = 4; };
 
 constexpr int kWave = 64;
 // log2 of the largest factor by which an un-rescaled probability may exceed 1
@@ -80,6 +82,34 @@ __device__ __forceinline__ i32x2 fp8x4_to_16<BF16>(uint32_t w) {
   return r;
 }
 
+// eight E2M1 codes in a dword (element 2i in the low nibble of byte i) ->
+// eight 16-bit values (four dwords), exact: every E2M1 value (0, 0.5 .. 6
+// and their negatives) is representable in both fp16 and bf16.  The
+// hardware converts one byte (two codes) per instruction, low nibble to
+// the low half.
+template <class T>
+__device__ __forceinline__ i32x4 fp4x8_to_16(uint32_t w);
+template <>
+__device__ __forceinline__ i32x4 fp4x8_to_16<F16>(uint32_t w) {
+  return i32x4{__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3))};
+}
+template <>
+__device__ __forceinline__ i32x4 fp4x8_to_16<BF16>(uint32_t w) {
+  return i32x4{__builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2)),
+               __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3))};
+}
+// the four codes of the low two bytes -> four 16-bit values (two dwords)
+template <class T>
+__device__ __forceinline__ i32x2 fp4x4_to_16(uint32_t w) {
+  const i32x4 x = fp4x8_to_16<T>(w);
+  return i32x2{x[0], x[1]};
+}
+
 // fp32 -> 16-bit storage, round to nearest even
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -131,6 +161,9 @@ __device__ __forceinline__ i32x2 ld8_stream(const void* p) {
 }
 __device__ __forceinline__ int ld4_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const int*>(p));
+}
+__device__ __forceinline__ uint32_t ld2_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
 }
 __device__ __forceinline__ i32x2 ld8(const void* p) { return *reinterpret_cast<const i32x2*>(p); }
 __device__ __forceinline__ int ld4(const void* p) { return *reinterpret_cast<const int*>(p); }

@@ -75,7 +75,7 @@ pa_status scatter_launch(const void* key, const void* value, void* k_cache, void
 
 pa_status scatter_rows_launch(const void* key, const void* value, void* k_cache, void* v_cache, float* k_scales,
                               float* v_scales, const int64_t* slots, int T, int Hkv, int D, int bs,
-                              int64_t num_blocks, int src_dtype, hipStream_t stream);
+                              int64_t num_blocks, int src_dtype, int cache_dtype, hipStream_t stream);
 
 pa_status append_last_launch(const void* key, const void* value, void* k_cache, void* v_cache,
                              const int32_t* block_tables, const int32_t* context_lens, int B, int M,

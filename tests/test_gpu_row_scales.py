@@ -1,5 +1,6 @@
-"""FP8 caches with one scale per (slot, kv head) row: the scatter bit for bit
-(codes and scales) and the decode against the oracle.
+"""FP8 and FP4 caches with one scale per (slot, kv head) row: the scatter bit
+for bit (codes and scales), the block copy bit for bit, and the decode
+against the oracle.
 
 Decode bound: rows of unit magnitude meet the FP8 gate (max-abs 3e-2,
 relative L2 1e-3).  Rows spread over six decades are checked against a bound
@@ -38,7 +39,11 @@ def _rows(w, spread, seed):
 
 def _pools(w, k, v, slots):
     nb, Hkv, bs, D = w.num_blocks, w.Hkv, w.bs, w.D
-    kc = torch.full((nb, Hkv, bs, D), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    cd = w.cache_dtype
+    if cd == "fp4":
+        kc = torch.full((nb, Hkv, bs, D // 2), 0x77, dtype=torch.uint8, device="cuda").view(torch.float4_e2m1fn_x2)
+    else:
+        kc = torch.full((nb, Hkv, bs, D), 0x7F, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
     vc = kc.clone()
     kss = torch.full((nb, Hkv, bs), float("nan"), dtype=torch.float32, device="cuda")
     vss = kss.clone()
@@ -47,10 +52,10 @@ def _pools(w, k, v, slots):
         pa.reshape_and_cache_scaled(storage_to_torch(k[i:i + step], "bf16").cuda(),
                                     storage_to_torch(v[i:i + step], "bf16").cuda(), kc, vc, kss, vss,
                                     torch.from_numpy(slots[i:i + step]).cuda())
-    okc, ovc = O.new_pool(nb, Hkv, bs, D, "fp8"), O.new_pool(nb, Hkv, bs, D, "fp8")
+    okc, ovc = O.new_pool(nb, Hkv, bs, D, cd), O.new_pool(nb, Hkv, bs, D, cd)
     oks = np.full((nb, Hkv, bs), np.nan, np.float32)
     ovs = oks.copy()
-    O.reshape_and_cache_scaled(k, v, okc, ovc, oks, ovs, slots, bs, "bf16")
+    O.reshape_and_cache_scaled(k, v, okc, ovc, oks, ovs, slots, bs, "bf16", cd)
     return (kc, vc, kss, vss), (okc, ovc, oks, ovs)
 
 
@@ -59,8 +64,9 @@ def _same_bits(t, a):
                           t.cpu().numpy().view(np.uint32), a.view(np.uint8) if a.dtype == np.uint8 else a.view(np.uint32))
 
 
-def test_scatter_with_row_scales_is_bit_exact():
-    w = W.custom("rs_scatter", 61, [1, 15, 16, 17, 100, 300], 8, 4, 128, 16, "fp8")
+@pytest.mark.parametrize("cd", ["fp8", "fp4"])
+def test_scatter_with_row_scales_is_bit_exact(cd):
+    w = W.custom(f"rs_scatter_{cd}", 61, [1, 15, 16, 17, 100, 300], 8, 4, 128, 16, cd)
     k, v, slots = _rows(w, 3.0, 62)
     # special rows: zeros, an infinity, NaN elements, a skipped token
     k[0] = 0
@@ -71,12 +77,25 @@ def test_scatter_with_row_scales_is_bit_exact():
     assert _same_bits(kc, okc) and _same_bits(vc, ovc)
     assert np.array_equal(kss.cpu().numpy(), oks, equal_nan=True)
     assert np.array_equal(vss.cpu().numpy(), ovs, equal_nan=True)
+    if cd == "fp4":  # E2M1 ties: every tie of the grid, both signs, through the same path
+        t = np.arange(-24, 25, dtype=np.float32) * 0.25
+        row = np.zeros((1, w.Hkv, 128), np.float32)
+        row[0, 0, :49] = t
+        row[0, 0, 49] = 6.0  # the row's scale is then exactly 1
+        kt = W.to_storage(row, "bf16")
+        kc = torch.zeros(tuple(kc.shape), dtype=torch.uint8, device="cuda").view(torch.float4_e2m1fn_x2)
+        vc = kc.clone()
+        pa.reshape_and_cache_scaled(storage_to_torch(kt, "bf16").cuda(), storage_to_torch(kt, "bf16").cuda(), kc, vc,
+                                    kss, vss, torch.tensor([0], dtype=torch.int64, device="cuda"))
+        assert float(kss[0, 0, 0]) == 1.0
+        want = O.e2m1_pack(O.e2m1_encode(row[0, 0], 1.0))
+        assert np.array_equal(kc[0, 0, 0].cpu().view(torch.uint8).numpy(), want)
 
 
-def _bound(ovc, ovs, spread):
+def _bound(ovc, ovs, spread, cd="fp8"):
     if spread == 0:
         return 3e-2
-    vmax = np.nanmax(np.abs(O.widen_rows(ovc, ovs)))
+    vmax = np.nanmax(np.abs(O.widen_rows(ovc, ovs, cd)))
     return 3e-2 + 2.0 ** -10 * vmax
 
 
@@ -84,28 +103,33 @@ def _bound(ovc, ovs, spread):
 @pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("q", ["f16", "bf16"])
 @pytest.mark.parametrize("spread", [0.0, 3.0])
-def test_decode_with_row_scales(D, bs, q, spread):
+@pytest.mark.parametrize("cd", ["fp8", "fp4"])
+def test_decode_with_row_scales(D, bs, q, spread, cd):
     lens = [0, 1, 7, 31, 33, 64, 129, 300, 517, 1031]
     for g in (1, 2, 4, 8, 16):
-        w = W.custom(f"rs_D{D}_bs{bs}_{q}_g{g}", 70 + g, lens, 2 * g, 2, D, bs, "fp8", q)
+        w = W.custom(f"rs_{cd}_D{D}_bs{bs}_{q}_g{g}", 70 + g, lens, 2 * g, 2, D, bs, cd, q)
         k, v, slots = _rows(w, spread, 80 + g)
         (kc, vc, kss, vss), (okc, ovc, oks, ovs) = _pools(w, k, v, slots)
         qd = storage_to_torch(w.query(), q).cuda()
         out = pa.decode_scaled(qd, kc, vc, kss, vss, torch.from_numpy(w.block_tables).cuda(),
                                torch.from_numpy(w.context_lens).cuda(), w.scale,
                                out_dtype=torch.float32).cpu().numpy().astype(np.float64)
-        ref = O.decode_scaled(w.query(), okc, ovc, oks, ovs, w.block_tables, w.context_lens, w.scale, g, q)
+        ref = O.decode_scaled(w.query(), okc, ovc, oks, ovs, w.block_tables, w.context_lens, w.scale, g, q,
+                              cache_dtype=cd)
         ma, rel = errors(out, ref)
-        bound = _bound(ovc, ovs, spread)
-        log(f"[row scales D={D} bs={bs} q={q} g={g} spread={spread}] max_abs={ma:.2e} (bound {bound:.2e}) "
+        bound = _bound(ovc, ovs, spread, cd)
+        log(f"[row scales {cd} D={D} bs={bs} q={q} g={g} spread={spread}] max_abs={ma:.2e} (bound {bound:.2e}) "
             f"rel_l2={rel:.2e}")
         assert np.isfinite(out).all() and ma <= bound and rel <= 1e-3
 
 
-def test_decode_with_row_scales_heavy_tail_full_size_sampled():
+@pytest.mark.parametrize("cd", ["fp8", "fp4"])
+def test_decode_with_row_scales_heavy_tail_full_size_sampled(cd):
     """The heavy-tailed batch (256 sequences, log-normal lengths) with rows
     spread over six decades of magnitude, checked on sampled sequences."""
     w = W.heavy_tail(bs=16)
+    if cd == "fp4":
+        w = W.custom("heavy_tail_fp4", w.seed, w.context_lens, w.Hq, w.Hkv, w.D, w.bs, "fp4", w.q_dtype)
     k, v, slots = _rows(w, 3.0, 90)
     (kc, vc, kss, vss), (okc, ovc, oks, ovs) = _pools(w, k, v, slots)
     qd = storage_to_torch(w.query(), w.q_dtype).cuda()
@@ -115,10 +139,10 @@ def test_decode_with_row_scales_heavy_tail_full_size_sampled():
     order = np.argsort(w.context_lens)
     seqs = sorted({int(order[-1]), int(order[-2]), int(order[0]), int(order[len(order) // 2])})
     ref = O.decode_scaled(w.query(), okc, ovc, oks, ovs, w.block_tables, w.context_lens, w.scale, w.group,
-                          w.q_dtype, seqs=seqs)
+                          w.q_dtype, seqs=seqs, cache_dtype=cd)
     ma, rel = errors(out[seqs], ref)
-    bound = _bound(ovc, ovs, 3.0)
-    log(f"[row scales heavy tail] max_abs={ma:.2e} (bound {bound:.2e}) rel_l2={rel:.2e}")
+    bound = _bound(ovc, ovs, 3.0, cd)
+    log(f"[row scales heavy tail {cd}] max_abs={ma:.2e} (bound {bound:.2e}) rel_l2={rel:.2e}")
     assert np.isfinite(out).all() and ma <= bound and rel <= 1e-3
 
 
@@ -133,3 +157,64 @@ def test_row_scale_calls_reject_bad_arguments():
     with pytest.raises(ValueError):
         pa.decode_scaled(torch.zeros((1, 4, 64), dtype=torch.float16, device="cuda"), f16cache, f16cache, kss, vss,
                          torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.context_lens).cuda(), 0.1)
+
+
+@pytest.mark.parametrize("cd", ["fp8", "fp4"])
+def test_copy_blocks_scaled_is_bit_exact(cd):
+    """Copy-on-write of a row-scaled cache copies the rows and their scales;
+    the oracle's copy of the same pools agrees byte for byte."""
+    w = W.custom(f"rs_copy_{cd}", 65, [40, 100, 7], 8, 4, 128, 16, cd)
+    k, v, slots = _rows(w, 2.0, 66)
+    (kc, vc, kss, vss), (okc, ovc, oks, ovs) = _pools(w, k, v, slots)
+    used = [int(b) for b in w.block_tables[1][:5]]
+    free = sorted(set(range(w.num_blocks)) - {int(b) for b in w.block_tables.ravel() if b >= 0})[:4]
+    pairs = np.array([[used[0], free[0]], [used[3], free[1]], [used[3], free[2]], [used[1], used[1]]], np.int64)
+    pa.copy_blocks_scaled(kc, vc, kss, vss, torch.from_numpy(pairs).cuda())
+    O.copy_blocks(okc, ovc, pairs)
+    O.copy_blocks(oks, ovs, pairs)
+    assert _same_bits(kc, okc) and _same_bits(vc, ovc)
+    assert np.array_equal(kss.cpu().numpy(), oks, equal_nan=True)
+    assert np.array_equal(vss.cpu().numpy(), ovs, equal_nan=True)
+    assert np.isfinite(oks[free[1]]).all() and np.array_equal(oks[free[1]], oks[used[3]])
+
+
+def test_fp4_cache_needs_row_scales():
+    w = W.custom("fp4_plain", 67, [20], 4, 2, 64, 16, "fp4")
+    k, v, slots = _rows(w, 1.0, 68)
+    (kc, vc, kss, vss), _ = _pools(w, k, v, slots)
+    lib = pa.library()
+    # the plain calls refuse an FP4 cache on the host, before any launch
+    st = lib.pa_reshape_and_cache(pa._ptr(storage_to_torch(k, "bf16").cuda()), pa._ptr(storage_to_torch(v, "bf16").cuda()),
+                                  pa._ptr(kc), pa._ptr(vc), pa._ptr(torch.from_numpy(slots).cuda()), len(slots), 2, 64,
+                                  16, w.num_blocks, pa.BF16, pa.FP4_E2M1, 1.0, 1.0, None)
+    assert st == pa.ERR_UNSUPPORTED
+    q = torch.zeros((1, 4, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        pa.decode(q, kc, vc, torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.context_lens).cuda(), 0.1)
+
+
+@pytest.mark.parametrize("cd", ["fp8", "fp4"])
+def test_row_scales_with_large_magnitudes_stay_finite(cd):
+    """Rows near 1e5: a V weight p * scale then reaches 2^8 * 1e5 / 6 (FP4)
+    or / 448 (FP8), beyond fp16; the kernel takes PV in bf16 for row-scaled
+    caches, so the result stays finite and accurate."""
+    w = W.custom(f"rs_big_{cd}", 69, [1, 40, 300, 1031], 16, 4, 128, 16, cd, "bf16")
+    rng = np.random.default_rng(70)
+    ks, vs, slots = [], [], []
+    for s in range(w.B):
+        L = int(w.context_lens[s])
+        k, v = w.seq_kv(s)
+        f = (1e5 * rng.uniform(0.5, 1.0, size=(2, L, w.Hkv, 1))).astype(np.float32)
+        ks.append(W.to_storage(W.storage_to_f32(k, "bf16") * f[0] * 1e-5, "bf16"))  # K stays unit-sized
+        vs.append(W.to_storage(W.storage_to_f32(v, "bf16") * f[1], "bf16"))
+        slots.append(O.slots_for(w.block_tables[s], 0, L, w.bs))
+    k, v, slots = np.concatenate(ks), np.concatenate(vs), np.concatenate(slots).astype(np.int64)
+    (kc, vc, kss, vss), (okc, ovc, oks, ovs) = _pools(w, k, v, slots)
+    out = pa.decode_scaled(storage_to_torch(w.query(), "bf16").cuda(), kc, vc, kss, vss,
+                           torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.context_lens).cuda(), w.scale,
+                           out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    ref = O.decode_scaled(w.query(), okc, ovc, oks, ovs, w.block_tables, w.context_lens, w.scale, w.group, "bf16",
+                          cache_dtype=cd)
+    ma, rel = errors(out, ref)
+    log(f"[row scales {cd}, |V| ~ 1e5] max_abs={ma:.2e} rel_l2={rel:.2e}")
+    assert np.isfinite(out).all() and rel <= 1e-3

@@ -85,7 +85,7 @@ class Workload:
     Hkv: int
     D: int
     bs: int
-    cache_dtype: str  # f16 | bf16 | fp8
+    cache_dtype: str  # f16 | bf16 | fp8 | fp4 (fp4: two E2M1 codes per byte, row-scaled only)
     src_dtype: str  # dtype of the key/value rows handed to the scatter (f16 | bf16)
     q_dtype: str  # f16 | bf16
     scale: float
@@ -128,8 +128,8 @@ class Workload:
 
     def kv_bytes(self) -> int:
         """Bytes of K and V the decode batch attends over (each row once per KV head)."""
-        e = 1 if self.cache_dtype == "fp8" else 2
-        return int(self.context_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * e
+        bits = {"fp8": 8, "fp4": 4}.get(self.cache_dtype, 16)
+        return int(self.context_lens.astype(np.int64).sum()) * self.Hkv * self.D * 2 * bits // 8
 
 
 def _deal_tables(rng, lens, bs, num_blocks):
@@ -324,10 +324,12 @@ def custom(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, bs: int, cache
     rng = _rng(seed, _LENS)
     nblk = int(((lens + bs - 1) // bs).sum())
     pool = num_blocks if num_blocks is not None else max(1, math.ceil(1.1 * nblk) + 1)
-    src = "bf16" if cache_dtype == "fp8" else cache_dtype
+    src = "bf16" if cache_dtype in ("fp8", "fp4") else cache_dtype
     w = _uniform_batch(name, seed, len(lens), Hq, Hkv, D, bs, src, lens, pool, rng, scale)
     w.q_dtype = q_dtype or src
     w._q = _plain_q(seed, len(lens), Hq, D, w.q_dtype)
+    if cache_dtype == "fp4":  # rows carry their own scales; no per-tensor scale
+        w.cache_dtype = "fp4"
     if cache_dtype == "fp8":
         w.cache_dtype = "fp8"
         kmax = vmax = 1e-30

@@ -39,6 +39,25 @@ constexpr int kScanMax = 4096;    // sequences one launch scans in LDS
 // with several queries per sequence the first query rows are kept in LDS as
 // well; three arrays of this many entries leave room for four waves per CU
 constexpr int kScanMaxMQ = 3072;
+// Kernels that run two waves per SIMD (eight per CU) scan half as many, so
+// that eight workgroups' arrays fit the 160 KiB of LDS.
+constexpr int kScanMax2 = 2048;
+constexpr int kScanMaxMQ2 = 1536;
+
+// Which MFMA kernels run two waves per SIMD: FP4.  Its waves are bound by
+// instruction issue at one wave per SIMD (5% of their cycles waiting on
+// memory), and its registers fit the 256 of two waves without spilling; a
+// second wave per SIMD took the FP4 decode of the 8B-shaped and the
+// heavy-tailed batches 15-16% faster.  fp8 with a scale per tensor also
+// fits, but measured 4% slower there (twice the slices, so more segments
+// per wave).  The host sizes launches (scan capacity, slices) with the same
+// rule.
+__host__ __device__ constexpr bool mfma_two_waves(int cache_code, bool row_scales, int tiles_per_wave) {
+  return cache_code == 4 && row_scales && tiles_per_wave == 1;
+}
+__host__ __device__ constexpr int scan_capacity(bool multi_query, bool two_waves) {
+  return two_waves ? (multi_query ? kScanMaxMQ2 : kScanMax2) : (multi_query ? kScanMaxMQ : kScanMax);
+}
 constexpr int kIdAhead = 6;       // chunks of block ids held ahead of the loads
 
 struct DecodeArgs {

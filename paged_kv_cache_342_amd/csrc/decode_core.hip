@@ -105,23 +105,26 @@ static int segment_cost() {
   return n >= 0 && n <= 64 ? n : 2;
 }
 
-static int waves_per_cu() {
+// waves the grid gives each CU: one per SIMD, or two for the kernels that
+// run two per SIMD
+static int waves_per_cu(bool two_waves) {
   const char* v = std::getenv("PA_DECODE_WAVES_PER_CU");
   const int n = v ? std::atoi(v) : 0;
-  return n >= 1 && n <= 32 ? n : 4;
+  return n >= 1 && n <= 32 ? n : (two_waves ? 8 : 4);
 }
 
 DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq,
-                       bool multi_query) {
+                       bool multi_query, bool two_waves) {
   (void)bs;
   DecodePlan p{};
-  const int64_t waves = (int64_t)waves_per_cu() * num_cu;
+  const int64_t waves = (int64_t)waves_per_cu(two_waves) * num_cu;
   const int64_t per = (int64_t)Hkv * head_tiles;
   p.nslices = (int)std::max<int64_t>(1, (waves + per - 1) / per);
   p.min_slice = 4;
   p.seg_cost = segment_cost();
   const int64_t chunks = ((int64_t)std::max(max_ctx, 1) + kChunk - 1) / kChunk + p.seg_cost;
-  int64_t sub = std::min<int64_t>(multi_query ? kScanMaxMQ : kScanMax, INT_MAX / chunks);
+  // the kernel's LDS scan arrays bound the sequences of one launch
+  int64_t sub = std::min<int64_t>(scan_capacity(multi_query, two_waves), INT_MAX / chunks);
   p.sub_batch = (int)std::max<int64_t>(1, std::min<int64_t>(sub, std::max(B, 1)));
   const size_t Hq = (size_t)Hkv * G * std::max(nq, 1);  // partial rows per (slice, sequence)
   const size_t rows = (size_t)p.nslices + p.sub_batch;
@@ -130,6 +133,12 @@ DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int he
   p.acc_off = p.ml_off + align256(sizeof(float) * 2 * rows * Hq);
   p.bytes = p.acc_off + align256(sizeof(float) * (size_t)D * rows * Hq);
   return p;
+}
+
+size_t decode_workspace_bound(int B, int Hkv, int G, int D, int bs, int max_ctx, int nq, bool multi_query) {
+  const int cu = device_cu_count();
+  return std::max(plan_decode(B, Hkv, G, D, bs, max_ctx, 1, cu, nq, multi_query, false).bytes,
+                  plan_decode(B, Hkv, G, D, bs, max_ctx, 1, cu, nq, multi_query, true).bytes);
 }
 
 int decode_variant_override() {
@@ -167,10 +176,16 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const int col_tiles = valu ? 1 : (int)(((int64_t)nq * r.G + 15) / 16);
   const int tw = mq && col_tiles >= 2 ? 2 : 1;
   const int tiles = (col_tiles + tw - 1) / tw;  // waves per (slice, KV head)
-  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq, mq);
+  const bool two_waves = !valu && mfma_two_waves(r.cache_dtype, rs, tw);
+  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq, mq,
+                                      two_waves);
   if (r.workspace_bytes < plan.bytes) {
     set_error("pa_decode: workspace of %zu bytes needed, %zu given", plan.bytes, r.workspace_bytes);
     return PA_ERR_WORKSPACE;
+  }
+  if (plan.sub_batch > scan_capacity(mq, two_waves)) {  // cannot happen: plan_decode caps it
+    set_error("pa_decode: internal error: %d sequences per launch exceed the kernel's scan arrays", plan.sub_batch);
+    return PA_ERR_HIP;
   }
   const int64_t grid_waves = (int64_t)plan.nslices * r.Hkv * tiles;
   if (grid_waves >= ((int64_t)1 << 31)) {

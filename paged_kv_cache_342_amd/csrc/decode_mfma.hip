@@ -115,8 +115,14 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+template <class CT, bool RS, int TW>
+struct MfmaWaves {
+  static constexpr int value = mfma_two_waves(CT::code, RS, TW) ? 2 : 1;
+};
+
 template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MfmaWaves<CT, RS, TW>::value)))
+void decode_mfma_kernel(DecodeArgs a) {
   constexpr int RB = D * CT::bits / 8;  // bytes per cache row
   constexpr int KK = D / 32;   // MFMAs per QK tile
   constexpr int W = D / 16;    // V values per lane per position (one output d-run)
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   constexpr bool kCanAppend = !kFp8 && !kFp4;  // new rows are stored as given
   constexpr int kRowLanes = RB / 16;  // lanes that hold one row, 16 bytes each
 
-  constexpr int kScan = MQ ? kScanMaxMQ : kScanMax;
+  constexpr int kScan = scan_capacity(MQ, MfmaWaves<CT, RS, TW>::value == 2);
   __shared__ int cum[kScan + 1];
   __shared__ int lens[kScan];
   __shared__ int qrow[MQ ? kScan + 1 : 1];
@@ -152,6 +158,9 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(DecodeArgs a) {
   const int ht = rest % a.head_tiles;
   const int k = rest / a.head_tiles;
 
+  // the host sizes every launch to the scan arrays (scan_capacity); a launch
+  // that did not fit would write past them
+  if (a.B > kScan) return;
   Slice sl;
   if (!slice_setup(a, cum, lens, MQ ? qrow : nullptr, k, sl)) return;
 

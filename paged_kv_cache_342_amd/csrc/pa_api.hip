@@ -106,8 +106,7 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_gro
   if (B <= 0 || num_kv_heads <= 0 || gqa_group <= 0 || max_context_len <= 0) return 0;
   if ((head_dim != 64 && head_dim != 128) || (block_size != 8 && block_size != 16 && block_size != 32)) return 0;
   // one query-head tile per KV head gives the most slices of any kernel choice
-  return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, 1, device_cu_count(), 1,
-                     false).bytes;
+  return decode_workspace_bound(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, 1, false);
 }
 
 }  // extern "C"
@@ -157,10 +156,10 @@ static pa_status decode_request(const char* fn, void* out, const void* q, const 
     return fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer argument", fn);
   const int full = max_blocks_per_seq * block_size;
   const int plan_ctx = max_context_len > 0 ? max_context_len : full;
-  const DecodePlan plan = plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx, 1, device_cu_count(), nq,
-                                      multi_query);
-  if (!workspace || workspace_bytes < plan.bytes)
-    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes,
+  const size_t need = decode_workspace_bound(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx, nq,
+                                             multi_query);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   r.out = out;
@@ -293,8 +292,8 @@ size_t pa_decode_multi_workspace_size(int32_t B, int32_t num_kv_heads, int32_t g
   if (B <= 0 || num_kv_heads <= 0 || gqa_group <= 0 || max_context_len <= 0 || max_queries <= 0) return 0;
   if ((head_dim != 64 && head_dim != 128) || (block_size != 8 && block_size != 16 && block_size != 32)) return 0;
   if (max_queries > kMaxQueries) return 0;
-  return plan_decode(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, 1, device_cu_count(),
-                     max_queries, true).bytes;
+  return decode_workspace_bound(B, num_kv_heads, gqa_group, head_dim, block_size, max_context_len, max_queries,
+                                true);
 }
 
 pa_status pa_decode_multi(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -28,8 +28,13 @@ int device_cu_count();
 
 // nq: queries per sequence at most (1 for decode); partial rows scale with it.
 // multi_query: the launch uses the several-queries kernel (fewer sequences per launch).
+// two_waves: the kernel runs two waves per SIMD (twice the slices, half the
+// sequences per launch: mfma_two_waves()).
 DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq,
-                       bool multi_query);
+                       bool multi_query, bool two_waves);
+// Workspace bytes that cover every kernel choice for these sizes (one tile
+// per KV head, either occupancy).
+size_t decode_workspace_bound(int B, int Hkv, int G, int D, int bs, int max_ctx, int nq, bool multi_query);
 
 struct DecodeRequest {
   void* out;

@@ -218,3 +218,22 @@ def test_row_scales_with_large_magnitudes_stay_finite(cd):
     ma, rel = errors(out, ref)
     log(f"[row scales {cd}, |V| ~ 1e5] max_abs={ma:.2e} rel_l2={rel:.2e}")
     assert np.isfinite(out).all() and rel <= 1e-3
+
+
+def test_fp4_batch_across_launches():
+    """FP4 kernels run two waves per SIMD and scan 2,048 sequences per launch:
+    a batch of 2,100 short sequences is two launches.  Every sequence against
+    the oracle."""
+    rng = np.random.default_rng(71)
+    lens = rng.integers(0, 48, size=2100)
+    w = W.custom("rs_fp4_launches", 72, lens, 8, 2, 64, 16, "fp4", "bf16")
+    k, v, slots = _rows(w, 1.0, 73)
+    (kc, vc, kss, vss), (okc, ovc, oks, ovs) = _pools(w, k, v, slots)
+    out = pa.decode_scaled(storage_to_torch(w.query(), "bf16").cuda(), kc, vc, kss, vss,
+                           torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.context_lens).cuda(), w.scale,
+                           out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+    ref = O.decode_scaled(w.query(), okc, ovc, oks, ovs, w.block_tables, w.context_lens, w.scale, w.group, "bf16",
+                          cache_dtype="fp4")
+    ma, rel = errors(out, ref)
+    log(f"[fp4, 2100 sequences in two launches] max_abs={ma:.2e} rel_l2={rel:.2e}")
+    assert np.isfinite(out).all() and ma <= _bound(ovc, ovs, 1.0, "fp4") and rel <= 1e-3

@@ -97,6 +97,21 @@ def test_decode_append_edge_sweep(cache, q, D, bs):
             _check_append(w, variant=v)
 
 
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_append_fp8_source_dtypes(src, D):
+    """fp8 caches take f16 and bf16 rows, encoded before the decode attends:
+    scales that saturate some elements (a quarter of the amax), and sequences
+    whose last chunk holds only the new row."""
+    lens = [1, 32, 33, 64, 65, 97, 300, 0, 17]
+    for g in (1, 4, 8):
+        w = W.custom(f"append_fp8_{src}_D{D}_g{g}", 310 + g, lens, 2 * g, 2, D, 16, "fp8", src, src_dtype=src)
+        w.k_scale = float(np.float32(w.k_scale) * np.float32(0.25))
+        w.v_scale = float(np.float32(w.v_scale) * np.float32(0.25))
+        for v in (["valu", "mfma"] if g <= 2 else ["mfma"]):
+            _check_append(w, variant=v, label=f"[src={src}]")
+
+
 def test_decode_append_batch_split_into_launches():
     """Several launches (a huge length bound shrinks the sequences one launch
     scans): each launch reads its own sequences' new rows."""

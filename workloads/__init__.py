@@ -318,13 +318,15 @@ def heavy_tail(seed: int = 3425, bs: int = 16, B: int = 256) -> Workload:
 
 def custom(name: str, seed: int, lens, Hq: int, Hkv: int, D: int, bs: int, cache_dtype: str,
            q_dtype: Optional[str] = None, num_blocks: Optional[int] = None,
-           scale: Optional[float] = None) -> Workload:
-    """A plain batch with the given lengths (edge-case sweeps)."""
+           scale: Optional[float] = None, src_dtype: Optional[str] = None) -> Workload:
+    """A plain batch with the given lengths (edge-case sweeps).  The rows handed
+    to the scatter are in src_dtype: the cache dtype for 16-bit caches, bf16
+    (or f16 when given) for fp8 and fp4 caches."""
     lens = np.asarray(lens, np.int32)
     rng = _rng(seed, _LENS)
     nblk = int(((lens + bs - 1) // bs).sum())
     pool = num_blocks if num_blocks is not None else max(1, math.ceil(1.1 * nblk) + 1)
-    src = "bf16" if cache_dtype in ("fp8", "fp4") else cache_dtype
+    src = (src_dtype or "bf16") if cache_dtype in ("fp8", "fp4") else cache_dtype
     w = _uniform_batch(name, seed, len(lens), Hq, Hkv, D, bs, src, lens, pool, rng, scale)
     w.q_dtype = q_dtype or src
     w._q = _plain_q(seed, len(lens), Hq, D, w.q_dtype)

@@ -115,6 +115,13 @@ def decode_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def traffic_key(name: str, row_scales: bool) -> str:
+    """The name a bench line's recorded traffic is kept under: the workload's
+    name (as the bench builds it, with its --fp4 / --group suffix), plus
+    '+row_scales' for the calls with a scale per row."""
+    return name + ("+row_scales" if row_scales else "")
+
+
 def recorded_traffic(workload: str):
     """HBM bytes per pa_decode call (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy
     of known size) from the committed rocprofv3 record, if it was taken on the
@@ -239,6 +246,24 @@ def hbm_ceilings(dev, mib=512, reps=5):
     return res
 
 
+def select_workload(config: str, group: int = 0, fp4: bool = False):
+    """The synthetic batch of a bench line: the named workload, or its lengths
+    and shapes with `group` query heads per KV head, or with an FP4 cache."""
+    import workloads as W
+
+    w = W.make(config)
+    if group:
+        if w.query_start is not None or w.name == "shared_prefix":
+            raise SystemExit("--group applies to the plain decode workloads")
+        w = W.custom(f"{w.name}_g{group}", w.seed, w.context_lens, w.Hkv * group, w.Hkv, w.D, w.bs,
+                     w.cache_dtype, w.q_dtype)
+    if fp4:
+        if w.query_start is not None or w.name == "shared_prefix":
+            raise SystemExit("--fp4 applies to the plain decode workloads")
+        w = W.custom(f"{w.name}_fp4", w.seed, w.context_lens, w.Hq, w.Hkv, w.D, w.bs, "fp4", w.q_dtype)
+    return w
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,16 +304,8 @@ def main():
     from workloads.device import DeviceBatch
 
     dev = torch.device("cuda:0")
-    w = W.make(args.config)
-    if args.group:
-        if w.query_start is not None or w.name == "shared_prefix":
-            raise SystemExit("--group applies to the plain decode workloads")
-        w = W.custom(f"{w.name}_g{args.group}", w.seed, w.context_lens, w.Hkv * args.group, w.Hkv, w.D, w.bs,
-                     w.cache_dtype, w.q_dtype)
+    w = select_workload(args.config, args.group, args.fp4)
     if args.fp4:
-        if w.query_start is not None or w.name == "shared_prefix":
-            raise SystemExit("--fp4 applies to the plain decode workloads")
-        w = W.custom(f"{w.name}_fp4", w.seed, w.context_lens, w.Hq, w.Hkv, w.D, w.bs, "fp4", w.q_dtype)
         args.row_scales = True
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} bs={w.bs} cache={w.cache_dtype} "
         f"sum(L)={int(w.context_lens.sum())}")
@@ -481,7 +498,7 @@ def main():
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": round(tflops / mfma_peak if mfma_bound else achieved / HBM_PEAK_GBS, 4),
             "traffic": None if args.identity_tables or args.unfused else
-                       recorded_traffic(w.name + ("+row_scales" if rs else "")),
+                       recorded_traffic(traffic_key(w.name, rs)),
             "kernel": ("pa_decode_multi call: MFMA kernel, (query, head) columns + merge kernel" if multi else
                        "pa_decode_scaled call: MFMA kernel with row scales + merge kernel" if rs else
                        "pa_decode call: decode kernel (balanced slices) + merge kernel" if args.unfused else

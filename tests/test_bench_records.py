@@ -1,0 +1,54 @@
+"""The bench's recorded profiler traffic: every bench line whose HBM bytes are
+recorded finds its record under the name the bench looks it up by, and each
+record points at a committed summary.  (The lookup itself returns nothing
+once the decode sources change; that is checked too.)  No GPU is needed:
+the workloads are built on the host and only their names are used."""
+import json
+import os
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (config, --row-scales, --fp4) of the bench lines with profiler records
+LINES = [
+    ("llama8b", False, False),
+    ("llama70b", False, False),
+    ("heavy_tail", False, False),
+    ("shared_prefix", False, False),
+    ("spec_decode", False, False),
+    ("chunked_prefill", False, False),
+    ("heavy_tail", True, False),
+    ("llama8b", True, True),
+    ("heavy_tail", True, True),
+]
+
+
+def _record():
+    with open(bench.TRAFFIC_FILE) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("config,row_scales,fp4", LINES)
+def test_every_profiled_line_finds_its_record(config, row_scales, fp4):
+    w = bench.select_workload(config, 0, fp4)
+    key = bench.traffic_key(w.name, row_scales or fp4)
+    rec = _record()["workloads"]
+    assert key in rec, f"no recorded traffic under {key!r}"
+    r = rec[key]
+    assert os.path.exists(os.path.join(ROOT, r["summary"]))
+    # the record's algorithmic bytes are the bench's: K and V rows of every
+    # position and KV head (plus two 4-byte scales per row with row scales)
+    kv = w.kv_bytes() + (int(w.context_lens.sum()) * w.Hkv * 8 if (row_scales or fp4) else 0)
+    assert r["algorithmic_kv_bytes"] == kv
+    assert 0.5 * kv < r["hbm_bytes_per_call"] < 4 * kv
+
+
+def test_records_are_dropped_when_the_sources_change(monkeypatch):
+    key = bench.traffic_key("llama8b", False)
+    if _record()["decode_source_sha256_16"] == bench.decode_source_hash():
+        assert bench.recorded_traffic(key) == _record()["workloads"][key]["hbm_bytes_per_call"]
+    monkeypatch.setattr(bench, "decode_source_hash", lambda: "0" * 16)
+    assert bench.recorded_traffic(key) is None

@@ -59,6 +59,10 @@ __host__ __device__ constexpr int scan_capacity(bool multi_query, bool two_waves
   return two_waves ? (multi_query ? kScanMaxMQ2 : kScanMax2) : (multi_query ? kScanMaxMQ : kScanMax);
 }
 constexpr int kIdAhead = 6;       // chunks of block ids held ahead of the loads
+// Several queries per sequence spanning at least this many tile pairs (16-bit
+// caches): a workgroup of this many waves, one per SIMD, shares each K/V
+// chunk through LDS instead of every wave loading it.
+constexpr int kSharedWaves = 4;
 
 struct DecodeArgs {
   void* out;                   // [B, Hq, D] (already offset to this launch's first sequence)

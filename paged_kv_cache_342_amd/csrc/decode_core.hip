@@ -11,7 +11,7 @@
 namespace pa {
 
 bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query,
-                        int tiles_per_wave, dim3 grid, hipStream_t stream);
+                        int tiles_per_wave, int waves_per_group, dim3 grid, hipStream_t stream);
 bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, int group,
                         dim3 grid, hipStream_t stream);
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
@@ -141,6 +141,13 @@ size_t decode_workspace_bound(int B, int Hkv, int G, int D, int bs, int max_ctx,
                   plan_decode(B, Hkv, G, D, bs, max_ctx, 1, cu, nq, multi_query, true).bytes);
 }
 
+// PA_DECODE_MQ_SHARED=0 keeps one wave per workgroup for every batch (for
+// comparisons)
+static bool mq_shared_enabled() {
+  const char* v = std::getenv("PA_DECODE_MQ_SHARED");
+  return !(v && v[0] == '0');
+}
+
 int decode_variant_override() {
   const char* v = std::getenv("PA_DECODE_VARIANT");
   if (!v) return 0;
@@ -177,6 +184,12 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const int tw = mq && col_tiles >= 2 ? 2 : 1;
   const int tiles = (col_tiles + tw - 1) / tw;  // waves per (slice, KV head)
   const bool two_waves = !valu && mfma_two_waves(r.cache_dtype, rs, tw);
+  // queries spanning kSharedWaves or more tile pairs of a 16-bit cache: the
+  // waves of a workgroup share each K/V chunk through LDS
+  const bool shared = mq && !rs && tw == 2 && tiles >= kSharedWaves &&
+                      (r.cache_dtype == PA_F16 || r.cache_dtype == PA_BF16) && mq_shared_enabled();
+  const int group_waves = shared ? kSharedWaves : 1;
+  const int group_tiles = (tiles + group_waves - 1) / group_waves;  // workgroups per (slice, KV head)
   const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq, mq,
                                       two_waves);
   if (r.workspace_bytes < plan.bytes) {
@@ -219,7 +232,7 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   a.nslices = plan.nslices;
   a.min_slice = plan.min_slice;
   a.seg_cost = plan.seg_cost;
-  a.head_tiles = tiles;
+  a.head_tiles = group_tiles;
   a.out_dtype = r.out_dtype == PA_F32 ? 0 : (r.out_dtype == PA_F16 ? 1 : 2);
   const bool fp8 = r.cache_dtype == PA_FP8_E4M3;
   a.qk_scale_log2 = r.scale * (fp8 && !rs ? r.k_scale : 1.f) * 1.4426950408889634f;
@@ -244,9 +257,9 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     a.context_lens = r.context_lens + s0;
     a.new_k = fused_append ? reinterpret_cast<const uint8_t*>(r.new_k) + (size_t)s0 * new_row : nullptr;
     a.new_v = fused_append ? reinterpret_cast<const uint8_t*>(r.new_v) + (size_t)s0 * new_row : nullptr;
-    const dim3 grid((unsigned)grid_waves);
+    const dim3 grid((unsigned)((int64_t)plan.nslices * r.Hkv * group_tiles));
     const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream)
-                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, tw, grid, stream);
+                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, tw, group_waves, grid, stream);
     if (!ok) {
       set_error("pa_decode: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d, group %d (%s)",
                 ct, qt, r.D, r.bs, r.G, valu ? "valu" : "mfma");

@@ -120,8 +120,17 @@ struct MfmaWaves {
   static constexpr int value = mfma_two_waves(CT::code, RS, TW) ? 2 : 1;
 };
 
-template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(MfmaWaves<CT, RS, TW>::value)))
+// NW > 1 (several queries per sequence, 16-bit caches): a workgroup of NW
+// waves, one per SIMD, walks one slice for NW consecutive tile pairs and
+// shares each K/V chunk through LDS.  Every lane loads a few 16-byte pieces
+// of the chunk and stores them into one of two LDS stages; after a barrier
+// each wave reads its MFMA operands from the stage in the byte pattern the
+// one-wave kernel loads from memory.  All waves of the workgroup walk the
+// same segments and chunks, so every barrier is reached by all of them; a
+// wave whose tiles hold no query of the sequence loads and waits but does
+// not compute.
+template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW, int NW = 1>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MfmaWaves<CT, RS, TW>::value)))
 void decode_mfma_kernel(DecodeArgs a) {
   constexpr int RB = D * CT::bits / 8;  // bytes per cache row
   constexpr int KK = D / 32;   // MFMAs per QK tile
@@ -144,8 +153,18 @@ void decode_mfma_kernel(DecodeArgs a) {
   __shared__ int cum[kScan + 1];
   __shared__ int lens[kScan];
   __shared__ int qrow[MQ ? kScan + 1 : 1];
+  constexpr bool kShared = NW > 1;
+  static_assert(!kShared || (MQ && !RS && CT::bits == 16), "shared chunks: several queries, 16-bit caches");
+  // LDS stages: [2 stages][K, V][kChunk rows] at a pitch of RB + 16 bytes, so
+  // that the 16 rows one K read spans fall on different banks
+  constexpr int kPitch = RB + 16;
+  constexpr int kPieceRow = RB / 16;                        // 16-byte pieces per row
+  constexpr int kPieces = 2 * kChunk * kPieceRow / (64 * NW);  // pieces each lane loads
+  static_assert(!kShared || kPieces * 64 * NW == 2 * kChunk * kPieceRow, "pieces per lane");
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kShared ? 2 * 2 * kChunk * kPitch : 16];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;  // wave within the workgroup
   const int r = lane & 15;   // A-operand row / B-operand column / C column
   const int gq = lane >> 4;  // k-slot group
   const int Hq = a.Hkv * a.G;
@@ -153,9 +172,11 @@ void decode_mfma_kernel(DecodeArgs a) {
 
   // wave -> (slice, head tile, KV head); the KV head varies fastest, so the
   // workgroups of one KV head land on the same XCD
+  // (with NW waves per workgroup, head_tiles counts workgroups per slice and
+  // KV head, and wave wv takes tile pair NW * that + wv)
   const int h = blockIdx.x % a.Hkv;
   const int rest = blockIdx.x / a.Hkv;
-  const int ht = rest % a.head_tiles;
+  const int ht = (rest % a.head_tiles) * NW + wv;
   const int k = rest / a.head_tiles;
 
   // the host sizes every launch to the scan arrays (scan_capacity); a launch
@@ -209,15 +230,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     int qrow0;              // row of the sequence's first query
     int nqs;                // its queries (1 for decode)
   };
-  auto load_header = [&](const Segment& g, Header& hd) {
-    hd.qrow0 = g.s;
-    hd.nqs = 1;
-    if constexpr (MQ) {
-      int row0, n;
-      query_range(a, qrow, g.s, lens[g.s], row0, n);
-      hd.qrow0 = uniform(row0);
-      hd.nqs = uniform(n);
-    }
+  auto load_query = [&](const Segment& g, Header& hd) {
     // a column that is no query of the sequence reads a row that exists
     // (row 0) and contributes zeros
 #pragma unroll
@@ -234,6 +247,21 @@ void decode_mfma_kernel(DecodeArgs a) {
         hd.qop[t][kk] = live ? x : i32x4{0, 0, 0, 0};
       }
     }
+  };
+  // The shared-chunk kernel loads a segment's query when the segment starts
+  // rather than a segment ahead: a second query buffer would not fit its
+  // registers, and its segments (long query chunks) are long.
+  constexpr bool kQueryLate = kShared;
+  auto load_header = [&](const Segment& g, Header& hd) {
+    hd.qrow0 = g.s;
+    hd.nqs = 1;
+    if constexpr (MQ) {
+      int row0, n;
+      query_range(a, qrow, g.s, lens[g.s], row0, n);
+      hd.qrow0 = uniform(row0);
+      hd.nqs = uniform(n);
+    }
+    if constexpr (!kQueryLate) load_query(g, hd);
     const int32_t* trow = a.block_tables + (int64_t)g.s * a.M;
     const int blk0 = g.tok0 / BS;
     hd.ring.start(trow + blk0, (g.tok_end + BS - 1) / BS - blk0);
@@ -253,6 +281,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   if (cur.s < 0) return;
   Header hc, hn;
   load_header(cur, hc);
+  if constexpr (kQueryLate) load_query(cur, hc);
   Segment nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
   load_header(nxt.s >= 0 ? nxt : cur, hn);
 
@@ -476,7 +505,87 @@ void decode_mfma_kernel(DecodeArgs a) {
     // load sits under a branch and each wait covers only the chunk it needs.
     // (Under MQ a tile with no query of this sequence among its columns skips
     // the segment.)
-    if (!MQ || 16 * TW * ht < hc.nqs * a.G) {
+    if constexpr (kShared) {
+      // this lane's pieces of chunk c: K rows, then V rows, kPieceRow per row
+      auto sh_load = [&](int c, i32x4* piece) {
+        const int ctok = tok0 + kChunk * c;
+        int id[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int x = ring.id(c, i);
+          id[i] = (x < 0 || (int64_t)x >= a.num_blocks) ? 0 : x;
+        }
+#pragma unroll
+        for (int q = 0; q < kPieces; ++q) {
+          const int pc = (int)threadIdx.x + 64 * NW * q;
+          const int kv = pc / (kChunk * kPieceRow);
+          const int rem = pc - kv * (kChunk * kPieceRow);
+          const int pos = rem / kPieceRow;
+          const int col = rem - pos * kPieceRow;
+          int bid = id[0];
+#pragma unroll
+          for (int i = 1; i < NB; ++i)
+            if (pos / BS == i) bid = id[i];
+          const bool ok = ctok + pos < lim;
+          const uint8_t* src = ok ? (kv ? vbase : kbase) + (int64_t)bid * blk_stride + (pos % BS) * RB
+                                  : (kv ? hc.last_v : hc.last_k);
+          piece[q] = ld16_stream(src + 16 * col);
+        }
+      };
+      auto sh_store = [&](int c, const i32x4* piece) {
+        uint8_t* sb = stage + (c & 1) * 2 * kChunk * kPitch;
+#pragma unroll
+        for (int q = 0; q < kPieces; ++q) {
+          const int pc = (int)threadIdx.x + 64 * NW * q;
+          const int kv = pc / (kChunk * kPieceRow);
+          const int rem = pc - kv * (kChunk * kPieceRow);
+          const int pos = rem / kPieceRow;
+          const int col = rem - pos * kPieceRow;
+          *reinterpret_cast<i32x4*>(sb + (kv * kChunk + pos) * kPitch + 16 * col) = piece[q];
+        }
+      };
+      // the wave's operands of chunk c, in the byte pattern of load_chunk
+      auto sh_read = [&](int c, Raw& raw) {
+        const uint8_t* sb = stage + (c & 1) * 2 * kChunk * kPitch;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int u = 0; u < Raw::KR; ++u)
+            raw.k[tt][u] = *reinterpret_cast<const i32x4*>(sb + (16 * tt + r) * kPitch + (32 * u + 8 * gq) * 2);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
+          const uint8_t* row = sb + (kChunk + tc) * kPitch + Raw::VB * r;
+          if constexpr (Raw::VB == 16) {
+            const i32x4 x = *reinterpret_cast<const i32x4*>(row);
+            raw.v[j][0] = x[0]; raw.v[j][1] = x[1]; raw.v[j][2] = x[2]; raw.v[j][3] = x[3];
+          } else {
+            const i32x2 x = *reinterpret_cast<const i32x2*>(row);
+            raw.v[j][0] = x[0]; raw.v[j][1] = x[1];
+          }
+        }
+      };
+      const bool has = 16 * TW * ht < hc.nqs * a.G;
+      i32x4 pieces[kPieces];
+      sh_load(0, pieces);
+      sh_store(0, pieces);
+      __syncthreads();
+      for (int c = 0; c < nchunks; ++c) {
+        const bool more = c + 1 < nchunks;
+        if (more) {
+          ring.advance();
+          sh_load(c + 1, pieces);
+        }
+        if (has) {
+          Raw raw;
+          Scales scl;
+          sh_read(c, raw);
+          compute_chunk(c, raw, scl);
+        }
+        if (more) sh_store(c + 1, pieces);
+        __syncthreads();
+      }
+    } else if (!MQ || 16 * TW * ht < hc.nqs * a.G) {
       Raw buf0, buf1;
       Scales sc0, sc1;
       load_chunk(0, buf0, sc0);
@@ -521,16 +630,25 @@ void decode_mfma_kernel(DecodeArgs a) {
     if (nxt.s < 0) break;
     cur = nxt;
     hc = hn;
+    if constexpr (kQueryLate) load_query(cur, hc);
     nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
     load_header(nxt.s >= 0 ? nxt : cur, hn);
   }
 }
 
 template <class CT, class QT, int D, int BS>
-void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, dim3 grid, hipStream_t stream) {
+void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, int waves_per_group, dim3 grid,
+                 hipStream_t stream) {
   if (!multi_query) {
     hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, false, false, 1>), grid, dim3(64), 0, stream, a);
     return;
+  }
+  if constexpr (CT::bits == 16) {
+    if (waves_per_group == kSharedWaves) {
+      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 2, kSharedWaves>), grid,
+                         dim3(64 * kSharedWaves), 0, stream, a);
+      return;
+    }
   }
   if (tiles_per_wave == 2)
     hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 2>), grid, dim3(64), 0, stream, a);
@@ -540,7 +658,7 @@ void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, dim3
 
 #define PA_MFMA_CASE(CT, QT, D, BS)                                         \
   if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS) {      \
-    launch_mfma<CT, QT, D, BS>(a, multi_query, tiles_per_wave, grid, stream); \
+    launch_mfma<CT, QT, D, BS>(a, multi_query, tiles_per_wave, waves_per_group, grid, stream); \
     return true;                                                            \
   }
 
@@ -561,9 +679,10 @@ void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, dim3
   PA_MFMA_RS_CASE(CT, QT, D, 32)
 
 // tiles_per_wave: 16-column tiles one wave computes (1, or 2 for several
-// queries per sequence spanning more than one tile)
+// queries per sequence spanning more than one tile); waves_per_group: 1, or
+// kSharedWaves for the kernel whose waves share K/V chunks through LDS
 bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query,
-                        int tiles_per_wave, dim3 grid, hipStream_t stream) {
+                        int tiles_per_wave, int waves_per_group, dim3 grid, hipStream_t stream) {
   if (a.k_row_scale != nullptr) {
     if (multi_query) return false;
     if (ct == FP8::code) {

@@ -117,3 +117,20 @@ def test_multi_query_more_sequences_than_one_launch_scans():
     w = W.multi_query("mq_many_seqs", 49, lens, nqs, 4, 2, 64, 16, "f16")
     seqs = [0, 1, 3070, 3071, 3072, 3073, 3099] + [int(i) for i in np.nonzero(np.array(nqs) > 0)[0][:5]]
     _check_multi(w, seqs=sorted(set(seqs)))
+
+
+@pytest.mark.parametrize("cache,D,bs,G", [("bf16", 128, 16, 4), ("f16", 64, 8, 8), ("bf16", 128, 32, 4),
+                                          ("f16", 128, 16, 16)])
+def test_shared_chunk_kernel_equals_one_wave_kernel(cache, D, bs, G, monkeypatch):
+    """Queries spanning four or more tile pairs run the kernel whose waves
+    share each K/V chunk through LDS.  It reads the bytes the one-wave kernel
+    reads (PA_DECODE_MQ_SHARED=0) and does the same arithmetic, so the two
+    must agree bit for bit, and both with the oracle.  Some sequences have
+    fewer queries than the workgroup has tiles, so some waves only load."""
+    lens = [40, 300, 1031, 77, 513, 64, 129, 2050]
+    nqs = [32, 64, 40, 5, 64, 64, 1, 48]
+    w = W.multi_query(f"mq_shared_{cache}_D{D}_bs{bs}_g{G}", 330 + G, lens, nqs, 2 * G, 2, D, bs, cache)
+    g, out = _check_multi(w, label="[shared chunks]")
+    monkeypatch.setenv("PA_DECODE_MQ_SHARED", "0")
+    one = g.decode_multi().cpu().numpy()
+    assert np.array_equal(out.astype(np.float32), one)

@@ -63,6 +63,9 @@ constexpr int kIdAhead = 6;       // chunks of block ids held ahead of the loads
 // caches): a workgroup of this many waves, one per SIMD, shares each K/V
 // chunk through LDS instead of every wave loading it.
 constexpr int kSharedWaves = 4;
+// The same with one tile per wave and two waves per SIMD, the default from
+// this many tiles on: a workgroup of this many waves.
+constexpr int kSharedWaves1 = 8;
 
 struct DecodeArgs {
   void* out;                   // [B, Hq, D] (already offset to this launch's first sequence)

@@ -141,11 +141,17 @@ size_t decode_workspace_bound(int B, int Hkv, int G, int D, int bs, int max_ctx,
                   plan_decode(B, Hkv, G, D, bs, max_ctx, 1, cu, nq, multi_query, true).bytes);
 }
 
-// PA_DECODE_MQ_SHARED=0 keeps one wave per workgroup for every batch (for
-// comparisons)
-static bool mq_shared_enabled() {
+// Long query chunks on a 16-bit cache: 2 = workgroups of kSharedWaves1 waves
+// with one tile each at two waves per SIMD (the default: 16 x 64-query
+// chunked prefill 122 us against 144 us for mode 1 and 145 us for mode 0),
+// 1 = kSharedWaves waves with two tiles each at one wave per SIMD (also where
+// the queries span fewer than kSharedWaves1 tiles), 0 = one wave per
+// workgroup (PA_DECODE_MQ_SHARED, for comparisons)
+static int mq_shared_mode() {
   const char* v = std::getenv("PA_DECODE_MQ_SHARED");
-  return !(v && v[0] == '0');
+  if (v && v[0] == '0') return 0;
+  if (v && v[0] == '1') return 1;
+  return 2;
 }
 
 int decode_variant_override() {
@@ -181,14 +187,15 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   // or two when a sequence's queries span several (the K/V loads and the V
   // transposes are then shared)
   const int col_tiles = valu ? 1 : (int)(((int64_t)nq * r.G + 15) / 16);
-  const int tw = mq && col_tiles >= 2 ? 2 : 1;
-  const int tiles = (col_tiles + tw - 1) / tw;  // waves per (slice, KV head)
-  const bool two_waves = !valu && mfma_two_waves(r.cache_dtype, rs, tw);
   // queries spanning kSharedWaves or more tile pairs of a 16-bit cache: the
   // waves of a workgroup share each K/V chunk through LDS
-  const bool shared = mq && !rs && tw == 2 && tiles >= kSharedWaves &&
-                      (r.cache_dtype == PA_F16 || r.cache_dtype == PA_BF16) && mq_shared_enabled();
-  const int group_waves = shared ? kSharedWaves : 1;
+  const int shared_mode = mq && !rs && (r.cache_dtype == PA_F16 || r.cache_dtype == PA_BF16) ? mq_shared_mode() : 0;
+  const bool shared1 = shared_mode == 2 && col_tiles >= kSharedWaves1;  // one tile per wave
+  const int tw = mq && col_tiles >= 2 && !shared1 ? 2 : 1;
+  const int tiles = (col_tiles + tw - 1) / tw;  // waves per (slice, KV head)
+  const bool two_waves = !valu && (shared1 || mfma_two_waves(r.cache_dtype, rs, tw));
+  const bool shared = shared1 || (shared_mode >= 1 && tw == 2 && tiles >= kSharedWaves);
+  const int group_waves = shared1 ? kSharedWaves1 : (shared ? kSharedWaves : 1);
   const int group_tiles = (tiles + group_waves - 1) / group_waves;  // workgroups per (slice, KV head)
   const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq, mq,
                                       two_waves);

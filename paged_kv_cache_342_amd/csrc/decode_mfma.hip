@@ -115,14 +115,15 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <class CT, bool RS, int TW>
+template <class CT, bool RS, int TW, int NW>
 struct MfmaWaves {
-  static constexpr int value = mfma_two_waves(CT::code, RS, TW) ? 2 : 1;
+  static constexpr int value = (NW == kSharedWaves1 || mfma_two_waves(CT::code, RS, TW)) ? 2 : 1;
 };
 
 // NW > 1 (several queries per sequence, 16-bit caches): a workgroup of NW
-// waves, one per SIMD, walks one slice for NW consecutive tile pairs and
-// shares each K/V chunk through LDS.  Every lane loads a few 16-byte pieces
+// waves walks one slice for NW consecutive groups of TW tiles (NW = 4 waves
+// of two tiles at one wave per SIMD, or NW = 8 waves of one tile at two per
+// SIMD) and shares each K/V chunk through LDS.  Every lane loads a few 16-byte pieces
 // of the chunk and stores them into one of two LDS stages; after a barrier
 // each wave reads its MFMA operands from the stage in the byte pattern the
 // one-wave kernel loads from memory.  All waves of the workgroup walk the
@@ -130,7 +131,7 @@ struct MfmaWaves {
 // wave whose tiles hold no query of the sequence loads and waits but does
 // not compute.
 template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW, int NW = 1>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MfmaWaves<CT, RS, TW>::value)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MfmaWaves<CT, RS, TW, NW>::value)))
 void decode_mfma_kernel(DecodeArgs a) {
   constexpr int RB = D * CT::bits / 8;  // bytes per cache row
   constexpr int KK = D / 32;   // MFMAs per QK tile
@@ -149,7 +150,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   constexpr bool kCanAppend = !kFp8 && !kFp4;  // new rows are stored as given
   constexpr int kRowLanes = RB / 16;  // lanes that hold one row, 16 bytes each
 
-  constexpr int kScan = scan_capacity(MQ, MfmaWaves<CT, RS, TW>::value == 2);
+  constexpr int kScan = scan_capacity(MQ, MfmaWaves<CT, RS, TW, NW>::value == 2);
   __shared__ int cum[kScan + 1];
   __shared__ int lens[kScan];
   __shared__ int qrow[MQ ? kScan + 1 : 1];
@@ -647,6 +648,11 @@ void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, int 
     if (waves_per_group == kSharedWaves) {
       hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 2, kSharedWaves>), grid,
                          dim3(64 * kSharedWaves), 0, stream, a);
+      return;
+    }
+    if (waves_per_group == kSharedWaves1) {
+      hipLaunchKernelGGL((decode_mfma_kernel<CT, QT, D, BS, true, false, 1, kSharedWaves1>), grid,
+                         dim3(64 * kSharedWaves1), 0, stream, a);
       return;
     }
   }

@@ -121,16 +121,20 @@ def test_multi_query_more_sequences_than_one_launch_scans():
 
 @pytest.mark.parametrize("cache,D,bs,G", [("bf16", 128, 16, 4), ("f16", 64, 8, 8), ("bf16", 128, 32, 4),
                                           ("f16", 128, 16, 16)])
-def test_shared_chunk_kernel_equals_one_wave_kernel(cache, D, bs, G, monkeypatch):
-    """Queries spanning four or more tile pairs run the kernel whose waves
-    share each K/V chunk through LDS.  It reads the bytes the one-wave kernel
-    reads (PA_DECODE_MQ_SHARED=0) and does the same arithmetic, so the two
-    must agree bit for bit, and both with the oracle.  Some sequences have
-    fewer queries than the workgroup has tiles, so some waves only load."""
+@pytest.mark.parametrize("mode", ["1", "2"])
+def test_shared_chunk_kernel_equals_one_wave_kernel(cache, D, bs, G, mode, monkeypatch):
+    """Queries spanning several tiles run a kernel whose waves share each K/V
+    chunk through LDS: four waves of two tiles (mode 1) or eight waves of one
+    tile at two waves per SIMD (mode 2, the default).  Either reads the bytes
+    the one-wave kernel reads (PA_DECODE_MQ_SHARED=0) and does the same
+    arithmetic per tile, so they must agree bit for bit, and with the oracle.
+    Some sequences have fewer queries than the workgroup has tiles, so some
+    waves only load."""
     lens = [40, 300, 1031, 77, 513, 64, 129, 2050]
     nqs = [32, 64, 40, 5, 64, 64, 1, 48]
     w = W.multi_query(f"mq_shared_{cache}_D{D}_bs{bs}_g{G}", 330 + G, lens, nqs, 2 * G, 2, D, bs, cache)
-    g, out = _check_multi(w, label="[shared chunks]")
+    monkeypatch.setenv("PA_DECODE_MQ_SHARED", mode)
+    g, out = _check_multi(w, label=f"[shared chunks, mode {mode}]")
     monkeypatch.setenv("PA_DECODE_MQ_SHARED", "0")
     one = g.decode_multi().cpu().numpy()
     assert np.array_equal(out.astype(np.float32), one)

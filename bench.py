@@ -246,12 +246,18 @@ def hbm_ceilings(dev, mib=512, reps=5):
     return res
 
 
-def select_workload(config: str, group: int = 0, fp4: bool = False):
-    """The synthetic batch of a bench line: the named workload, or its lengths
-    and shapes with `group` query heads per KV head, or with an FP4 cache."""
+def select_workload(config: str, group: int = 0, fp4: bool = False, block_size: int = 0):
+    """The synthetic batch of a bench line: the named workload (the heavy-tailed
+    one at another block size), or its lengths and shapes with `group` query
+    heads per KV head, or with an FP4 cache."""
     import workloads as W
 
-    w = W.make(config)
+    if block_size:
+        if config != "heavy_tail":
+            raise SystemExit("--block-size applies to the heavy_tail workload (its block size is swept)")
+        w = W.make(config, bs=block_size)
+    else:
+        w = W.make(config)
     if group:
         if w.query_start is not None or w.name == "shared_prefix":
             raise SystemExit("--group applies to the plain decode workloads")
@@ -284,6 +290,8 @@ def main():
     ap.add_argument("--fp4", action="store_true",
                     help="decode workloads: the same lengths and shapes with an FP4 (E2M1) cache, a scale per row "
                          "(fresh seeded values; implies --row-scales)")
+    ap.add_argument("--block-size", type=int, default=0, choices=[0, 8, 16, 32],
+                    help="heavy_tail: the same lengths and values in blocks of 8, 16 (its default) or 32 positions")
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as two calls, pa_reshape_and_cache then pa_decode")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
@@ -304,7 +312,7 @@ def main():
     from workloads.device import DeviceBatch
 
     dev = torch.device("cuda:0")
-    w = select_workload(args.config, args.group, args.fp4)
+    w = select_workload(args.config, args.group, args.fp4, args.block_size)
     if args.fp4:
         args.row_scales = True
     log(f"workload {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} bs={w.bs} cache={w.cache_dtype} "

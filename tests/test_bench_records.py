@@ -12,17 +12,19 @@ import bench
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# (config, --row-scales, --fp4) of the bench lines with profiler records
+# (config, --row-scales, --fp4, --block-size) of the bench lines with profiler records
 LINES = [
-    ("llama8b", False, False),
-    ("llama70b", False, False),
-    ("heavy_tail", False, False),
-    ("shared_prefix", False, False),
-    ("spec_decode", False, False),
-    ("chunked_prefill", False, False),
-    ("heavy_tail", True, False),
-    ("llama8b", True, True),
-    ("heavy_tail", True, True),
+    ("llama8b", False, False, 0),
+    ("llama70b", False, False, 0),
+    ("heavy_tail", False, False, 0),
+    ("heavy_tail", False, False, 8),
+    ("heavy_tail", False, False, 32),
+    ("shared_prefix", False, False, 0),
+    ("spec_decode", False, False, 0),
+    ("chunked_prefill", False, False, 0),
+    ("heavy_tail", True, False, 0),
+    ("llama8b", True, True, 0),
+    ("heavy_tail", True, True, 0),
 ]
 
 
@@ -31,9 +33,9 @@ def _record():
         return json.load(f)
 
 
-@pytest.mark.parametrize("config,row_scales,fp4", LINES)
-def test_every_profiled_line_finds_its_record(config, row_scales, fp4):
-    w = bench.select_workload(config, 0, fp4)
+@pytest.mark.parametrize("config,row_scales,fp4,block_size", LINES)
+def test_every_profiled_line_finds_its_record(config, row_scales, fp4, block_size):
+    w = bench.select_workload(config, 0, fp4, block_size)
     key = bench.traffic_key(w.name, row_scales or fp4)
     rec = _record()["workloads"]
     assert key in rec, f"no recorded traffic under {key!r}"

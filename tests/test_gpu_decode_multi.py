@@ -138,3 +138,32 @@ def test_shared_chunk_kernel_equals_one_wave_kernel(cache, D, bs, G, mode, monke
     monkeypatch.setenv("PA_DECODE_MQ_SHARED", "0")
     one = g.decode_multi().cpu().numpy()
     assert np.array_equal(out.astype(np.float32), one)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_shared_chunk_kernels_on_random_shapes(seed, monkeypatch):
+    """Seeded random batches (group 1-16, head_dim 64/128, block size 8/16/32,
+    f16/bf16, empty sequences, sequences without queries, query counts up to
+    the length): both shared-chunk kernels equal the one-wave kernel bit for
+    bit, and the default one is within tolerance of the oracle."""
+    rng = np.random.default_rng(900 + seed)
+    G = [1, 2, 4, 8, 16, 4][seed]
+    D = [64, 128][seed % 2]
+    bs = int(rng.choice([8, 16, 32]))
+    cache = str(rng.choice(["f16", "bf16"]))
+    B = int(rng.integers(3, 12))
+    lens = [int(x) for x in rng.integers(0, 1500, size=B)]
+    lens[0] = max(lens[0], 160)  # at least one sequence with enough queries for the shared kernels
+    lens[-1] = 0  # an empty sequence
+    nqs = [int(rng.integers(0, min(L, 96) + 1)) for L in lens]
+    nqs[0] = max(nqs[0], min(lens[0], -(-128 // G)))
+    nqs[1] = 0  # a sequence without queries
+    w = W.multi_query(f"mq_rand{seed}_{cache}_D{D}_bs{bs}_g{G}", 910 + seed, lens, nqs, 2 * G, 2, D, bs, cache)
+    log(f"[random shapes seed={seed}] G={G} D={D} bs={bs} {cache} lens={lens} nqs={nqs}")
+    g, out = _check_multi(w, label=f"[random {seed}]")
+    res = {}
+    for mode in ("0", "1", "2"):
+        monkeypatch.setenv("PA_DECODE_MQ_SHARED", mode)
+        res[mode] = g.decode_multi().cpu().numpy()
+    assert np.array_equal(res["1"], res["0"]) and np.array_equal(res["2"], res["0"])
+    assert np.array_equal(out.astype(np.float32), res["2"])

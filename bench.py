@@ -507,7 +507,8 @@ def main():
             "frac": round(tflops / mfma_peak if mfma_bound else achieved / HBM_PEAK_GBS, 4),
             "traffic": None if args.identity_tables or args.unfused else
                        recorded_traffic(traffic_key(w.name, rs)),
-            "kernel": ("pa_decode_multi call: MFMA kernel, (query, head) columns + merge kernel" if multi else
+            "kernel": ("pa_decode_multi call: MFMA kernel over (query, head) columns (long query chunks: "
+                       "workgroups whose waves share K/V chunks through LDS) + merge kernel" if multi else
                        "pa_decode_scaled call: MFMA kernel with row scales + merge kernel" if rs else
                        "pa_decode call: decode kernel (balanced slices) + merge kernel" if args.unfused else
                        "pa_decode_append call: decode kernel (balanced slices, append fused for 16-bit caches; "

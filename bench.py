@@ -6,12 +6,15 @@ the batch's new token rows into their slots, then paged decode attention over
 every sequence's blocks.  By default the step is one pa_decode_append call
 (the decode kernel stores the new rows itself for 16-bit caches); with
 --unfused it is pa_reshape_and_cache followed by pa_decode.  The default
-workload is the Llama-3-8B-shaped decode layer: 64 sequences, 32 query / 8 KV
-heads, head_dim 128, bf16, block size 16, context lengths U{512..4096}.
+workload is the largest single-GPU batch, the 70B-class decode layer: 32
+sequences of 8,000 positions, 64 query / 8 KV heads, head_dim 128, fp16,
+block size 16 (500 shuffled blocks per sequence).
 
 Reported: KV GB/s (algorithmic K+V bytes of the batch per step time) and
-sequence-heads per second, the decode call's roofline fraction against the
-8 TB/s HBM peak, and the CPU oracle on a bounded sample of the same batch.
+sequence-heads per second; the attention kernel's roofline fraction against
+the 8 TB/s HBM peak, its duration taken live by events the library records
+around that kernel alone; and the CPU oracle on a bounded sample of the same
+batch.
 
     python bench.py [--steps K] [--warmup W] [--config llama8b|llama70b|...]
 """
@@ -275,7 +278,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="llama8b")
+    ap.add_argument("--config", default="llama70b")
     ap.add_argument("--no-flush", action="store_true", help="do not evict L2/MALL between steps")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0 = skip)")
     ap.add_argument("--identity-tables", action="store_true",
@@ -400,8 +403,10 @@ def main():
     log(f"warmup done ({args.warmup} steps)")
 
     # events on torch's current stream, the stream every call launches on;
-    # with two calls, a middle event separates the append from the attention call
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # with two calls, a middle event separates the append from the attention
+    # call; the library records ev[i][3] / ev[i][4] at the start and end of the
+    # call's attention kernel itself (the launch's own events)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -410,16 +415,20 @@ def main():
         if two_calls:
             append()
             ev[i][1].record()
+            pa.time_next_attention_kernel(ev[i][3], ev[i][4])
             second()
         else:
+            pa.time_next_attention_kernel(ev[i][3], ev[i][4])
             decode_append()
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = [e[0].elapsed_time(e[2]) for e in ev]
     dec_ms = [e[1].elapsed_time(e[2]) for e in ev] if two_calls else step_ms
+    kern_ms = [e[3].elapsed_time(e[4]) for e in ev]
     ms_step = float(np.mean(step_ms))
     ms_dec = float(np.mean(dec_ms))
+    ms_kern = float(np.mean(kern_ms))
 
     # the same step captured once in a HIP graph and replayed (the cache
     # eviction stays outside the graph and outside the events)
@@ -447,16 +456,17 @@ def main():
     if rs:  # each (position, kv head) row also carries a 4-byte K and V scale
         kv_bytes += int(w.context_lens.astype(np.int64).sum()) * w.Hkv * 4 * 2
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = kv_bytes / (ms_dec * 1e-3) / 1e9
+    achieved = kv_bytes / (ms_kern * 1e-3) / 1e9
     # algorithmic flops: 4 * D per (query head, position seen) -- QK and PV
     seen = (w.context_lens.astype(np.int64) if not multi else
             np.array([sum(int(L) - n + j + 1 for j in range(n)) for L, n in zip(w.context_lens, nqs)]))
     flops = 4 * w.D * w.Hq * int(seen.sum())
-    tflops = flops / (ms_dec * 1e-3) / 1e12
+    tflops = flops / (ms_kern * 1e-3) / 1e12
     mfma_peak = MFMA_PEAK_TFLOPS[w.cache_dtype]
     mfma_bound = tflops / mfma_peak > achieved / HBM_PEAK_GBS
     log(f"step {ms_step * 1e3:.1f} us (median {np.median(step_ms) * 1e3:.1f}), decode {ms_dec * 1e3:.1f} us "
-        f"(median {np.median(dec_ms) * 1e3:.1f}), wall/step incl. flush {wall / args.steps * 1e3:.3f} ms")
+        f"(median {np.median(dec_ms) * 1e3:.1f}), attention kernel {ms_kern * 1e3:.1f} us "
+        f"(median {np.median(kern_ms) * 1e3:.1f}), wall/step incl. flush {wall / args.steps * 1e3:.3f} ms")
 
     ceil = hbm_ceilings(dev)
     log(f"plain copy {ceil['copy_gbs']} GB/s (read + write), plain read {ceil['read_gbs']} GB/s")
@@ -496,6 +506,7 @@ def main():
         "attention_tflops": round(tflops, 2),
         "hbm_fraction": round(value / HBM_PEAK_GBS, 4),
         "decode_us": round(ms_dec * 1e3, 2),
+        "attention_kernel_us": round(ms_kern * 1e3, 2),
         "graph_replay_us_per_step": None if graph_ms is None else round(graph_ms * 1e3, 2),
         "hbm_copy": {**ceil, "frac_of_copy": round(value / ceil["copy_gbs"], 4),
                      "frac_of_read": round(value / ceil["read_gbs"], 4)},
@@ -507,12 +518,14 @@ def main():
             "frac": round(tflops / mfma_peak if mfma_bound else achieved / HBM_PEAK_GBS, 4),
             "traffic": None if args.identity_tables or args.unfused else
                        recorded_traffic(traffic_key(w.name, rs)),
-            "kernel": ("pa_decode_multi call: MFMA kernel over (query, head) columns (long query chunks: "
-                       "workgroups whose waves share K/V chunks through LDS) + merge kernel" if multi else
-                       "pa_decode_scaled call: MFMA kernel with row scales + merge kernel" if rs else
-                       "pa_decode call: decode kernel (balanced slices) + merge kernel" if args.unfused else
-                       "pa_decode_append call: decode kernel (balanced slices, append fused for 16-bit caches; "
-                       "fp8: append scatter first) + merge kernel"),
+            "kernel": ("attention kernel of pa_decode_multi: MFMA kernel over (query, head) columns (long query "
+                       "chunks: workgroups whose waves share K/V chunks through LDS)" if multi else
+                       "attention kernel of pa_decode_scaled: MFMA kernel with row scales" if rs else
+                       "attention kernel of pa_decode: decode kernel (balanced slices)" if args.unfused else
+                       "attention kernel of pa_decode_append: decode kernel (balanced slices, append fused for "
+                       "16-bit caches)"),
+            "timing": "achieved = algorithmic bytes / mean duration of that kernel alone over the timed steps, "
+                      "from start/stop events recorded by its launch on the call's stream",
         },
         "cpu_baseline": cpu,
         "block_manager": bm,

@@ -136,7 +136,13 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
 
 /*
  * Bytes of device workspace pa_decode needs for these sizes (split-K
- * partial results and the work list).  Depends only on its arguments.
+ * partial results and the work list).  A function of its arguments alone:
+ * it covers every kernel choice on any gfx950 device (the split is planned
+ * for at most 256 compute units and 8 waves on each), so a workspace sized
+ * once serves every device of the process.  max_context_len is the length
+ * bound the decode call plans with: for a call given max_context_len <= 0,
+ * pass max_blocks_per_seq * block_size here.  Returns 0 for B <= 0,
+ * max_context_len <= 0 or sizes the calls refuse.
  */
 size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_group,
                                 int32_t head_dim, int32_t block_size, int32_t max_context_len);
@@ -166,7 +172,8 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_gro
  *                  initialisation and are scratch after the call.
  * Environment: PA_DECODE_VARIANT=valu|mfma forces one of the two kernel
  * families (default: MFMA for every group size; the VALU/DPP kernel is built
- * for groups 1 and 2, and for group 4 at head_dim 128 and block size 16).
+ * for groups 1 and 2, and forcing it at another group gives
+ * PA_ERR_UNSUPPORTED).
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t B,
@@ -194,8 +201,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
  *   every other argument as for pa_decode; the caches are written.
  * For 16-bit caches the decode kernel stores the rows itself and reads them
  * from key/value, so the call launches no scatter; for FP8 caches a scatter
- * runs first.  Errors are those of pa_decode and pa_reshape_and_cache; a
- * call that fails has no effect.
+ * runs first.  Errors are those of pa_decode and pa_reshape_and_cache; every
+ * check that can refuse the call (arguments, workspace, kernel choice) runs
+ * before anything is enqueued, so such a call has no effect.  Only a launch
+ * the HIP runtime itself refuses (PA_ERR_HIP) can come after the FP8
+ * scatter was enqueued; the appended rows may then be written.
  */
 /*
  * FP8 or FP4 cache with one scale per (slot, kv head) row ("PagedAttention -
@@ -393,6 +403,19 @@ pa_status pa_bm_tables(const pa_block_manager* bm, const int64_t* seqs, int32_t 
 /* length of seq in tokens, -1 if unknown */
 int64_t pa_bm_length(const pa_block_manager* bm, int64_t seq);
 pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* out);
+
+/*
+ * Kernel timing, for benchmarks.  start_event and stop_event are hipEvent_t
+ * handles the caller created (either may be NULL).  The next pa_decode,
+ * pa_decode_append, pa_decode_scaled or pa_decode_multi call on this thread
+ * that launches its kernels records start_event when its first attention
+ * kernel begins and stop_event when its last attention kernel ends, on the
+ * call's stream (the start and stop events of hipExtLaunchKernel), and the
+ * pair is then forgotten.  The elapsed time between them is the attention
+ * kernel alone: the split merge and an FP8 append lie outside it unless a
+ * batch runs as several launches (more than 4,096 sequences).  Always PA_OK.
+ */
+pa_status pa_time_next_attention_kernel(void* start_event, void* stop_event);
 
 /* Static description of a status code. */
 const char* pa_status_string(pa_status s);

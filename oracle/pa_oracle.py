@@ -48,7 +48,6 @@ elements is D / 2 bytes).
 """
 from __future__ import annotations
 
-import math
 from typing import Optional
 
 import numpy as np
@@ -211,6 +210,10 @@ def e2m1_unpack(packed) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def widen(x, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Storage values -> float64, exactly.  f16 is IEEE binary16; bf16 is the
+    upper half of an IEEE binary32 (1 sign, 8 exponent, 7 fraction bits), so
+    its bit pattern shifted left by 16 is that binary32; fp8 goes through the
+    E4M3FN code table times the scale."""
     if dtype == "f16":
         return np.asarray(x, np.float16).astype(np.float64)
     if dtype == "bf16":
@@ -440,11 +443,3 @@ def decode_contiguous(q, keys, values, scale: float, group: int, cache_dtype: st
                widen(values[s], cache_dtype, v_scale), scale, group)
         for s in range(len(keys))
     ])
-
-
-def relative_l2(a, b) -> float:
-    a = np.asarray(a, np.float64)
-    b = np.asarray(b, np.float64)
-    den = math.sqrt(float((b * b).sum()))
-    num = math.sqrt(float(((a - b) ** 2).sum()))
-    return num / den if den else num

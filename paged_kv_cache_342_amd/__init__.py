@@ -101,6 +101,8 @@ def _load(path: str) -> ctypes.CDLL:
     lib.pa_last_error_message.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
     lib.pa_version.restype = ctypes.c_char_p
+    lib.pa_time_next_attention_kernel.argtypes = [p, p]
+    lib.pa_time_next_attention_kernel.restype = ctypes.c_int
     lib.pa_is_checked_build.argtypes = []
     lib.pa_is_checked_build.restype = ctypes.c_int32
     lib.pa_bm_create.argtypes = [i64, i32]
@@ -154,6 +156,23 @@ def _require(t: torch.Tensor, name: str, dtype=None):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
 
 
+def _out(out: Optional[torch.Tensor], shape, out_dtype, like: torch.Tensor) -> torch.Tensor:
+    """The caller's output tensor after checking that it has the call's shape
+    (a wrong shape would make the kernels write outside it), or a new one."""
+    if out is None:
+        return torch.empty(shape, dtype=out_dtype or like.dtype, device=like.device)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out must have shape {tuple(shape)}, got {tuple(out.shape)}")
+    _require(out, "out", (torch.float32, torch.float16, torch.bfloat16))
+    return out
+
+
+def _max_context(max_context_len: Optional[int], M: int, bs: int) -> int:
+    """The host-side length bound a call plans with: None or <= 0 means every
+    table entry, M * block_size (as the C calls read <= 0)."""
+    return M * bs if max_context_len is None or int(max_context_len) <= 0 else int(max_context_len)
+
+
 def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       slot_mapping: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """Write key/value rows [T, Hkv, D] into the slots slot_mapping[T] (int64, negative = skip)
@@ -193,11 +212,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [B, M] and context_lens [B]")
     M = block_tables.shape[1]
-    mcl = M * bs if max_context_len is None else int(max_context_len)
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
-    else:
-        _require(out, "out")
+    mcl = _max_context(max_context_len, M, bs)
+    out = _out(out, (B, Hq, D), out_dtype, q)
     need = decode_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl) if B else 0
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -230,11 +246,8 @@ def decode_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [B, M] and context_lens [B]")
     M = block_tables.shape[1]
-    mcl = M * bs if max_context_len is None else int(max_context_len)
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
-    else:
-        _require(out, "out")
+    mcl = _max_context(max_context_len, M, bs)
+    out = _out(out, (B, Hq, D), out_dtype, q)
     need = decode_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl) if B else 0
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -295,11 +308,8 @@ def decode_scaled(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [B, M] and context_lens [B]")
     M = block_tables.shape[1]
-    mcl = M * bs if max_context_len is None else int(max_context_len)
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
-    else:
-        _require(out, "out")
+    mcl = _max_context(max_context_len, M, bs)
+    out = _out(out, (B, Hq, D), out_dtype, q)
     need = decode_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl) if B else 0
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -339,11 +349,8 @@ def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start.shape != (B + 1,):
         raise ValueError("block_tables must be [B, M], context_lens [B] and query_start [B + 1]")
     M = block_tables.shape[1]
-    mcl = M * bs if max_context_len is None else int(max_context_len)
-    if out is None:
-        out = torch.empty((T, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
-    else:
-        _require(out, "out")
+    mcl = _max_context(max_context_len, M, bs)
+    out = _out(out, (T, Hq, D), out_dtype, q)
     need = decode_multi_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl, max_queries) if B else 0
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -356,12 +363,20 @@ def decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
     return out
 
 
+def _pairs_shape(block_mapping: torch.Tensor) -> None:
+    if block_mapping.numel() and (block_mapping.dim() != 2 or block_mapping.shape[1] != 2):
+        raise ValueError(f"block_mapping must be [N, 2], got {tuple(block_mapping.shape)}")
+
+
 def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, block_mapping: torch.Tensor) -> None:
     """Copy-on-write: k_cache[dst] = k_cache[src] (and V) for each (src, dst) row of block_mapping [N, 2] int64."""
     _require(k_cache, "k_cache")
     _require(v_cache, "v_cache")
     _require(block_mapping, "block_mapping", torch.int64)
+    _pairs_shape(block_mapping)
     nb, Hkv, bs, _ = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes do not agree")
     N = block_mapping.shape[0] if block_mapping.numel() else 0
     _check(library().pa_copy_blocks(
         _ptr(k_cache), _ptr(v_cache), _ptr(block_mapping) if N else None, N, Hkv, _head_dim(k_cache), bs, nb,
@@ -376,6 +391,7 @@ def copy_blocks_scaled(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: t
     _require(k_scales, "k_scales", torch.float32)
     _require(v_scales, "v_scales", torch.float32)
     _require(block_mapping, "block_mapping", torch.int64)
+    _pairs_shape(block_mapping)
     _scaled_cache(k_cache, v_cache)
     nb, Hkv, bs, _ = k_cache.shape
     if v_cache.shape != k_cache.shape or k_scales.shape != (nb, Hkv, bs) or v_scales.shape != k_scales.shape:
@@ -384,6 +400,17 @@ def copy_blocks_scaled(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scales: t
     _check(library().pa_copy_blocks_scaled(
         _ptr(k_cache), _ptr(v_cache), _ptr(k_scales), _ptr(v_scales), _ptr(block_mapping) if N else None, N, Hkv,
         _head_dim(k_cache), bs, nb, _TORCH_CODE[k_cache.dtype], _stream(k_cache)))
+
+
+def time_next_attention_kernel(start: torch.cuda.Event, stop: torch.cuda.Event) -> None:
+    """Have the next decode call on this thread record `start` when its first
+    attention kernel begins and `stop` when its last one ends, on the call's
+    stream (timing events, enable_timing=True); start.elapsed_time(stop) is
+    then the attention kernel alone, without the split merge."""
+    for ev in (start, stop):
+        if not ev.cuda_event:  # torch creates the underlying event on its first record
+            ev.record()
+    _check(library().pa_time_next_attention_kernel(start.cuda_event, stop.cuda_event))
 
 
 def version() -> str:

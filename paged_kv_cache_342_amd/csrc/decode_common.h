@@ -30,9 +30,23 @@
 // read once into LDS), so no separate planning kernel runs before it.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "pa_device.h"
+#include "pa_internal.h"
 
 namespace pa {
+
+// Launch a kernel with the given events (hipExtLaunchKernel's start and
+// stop), or as a plain launch when there are none.
+template <class K, class... Args>
+inline void launch_with_events(K kernel, dim3 grid, dim3 block, hipStream_t stream, const LaunchEvents& ev,
+                               Args... args) {
+  if (ev.start != nullptr || ev.stop != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+}
 
 constexpr int kChunk = 32;        // positions per chunk, the unit of the split
 constexpr int kScanMax = 4096;    // sequences one launch scans in LDS

@@ -11,9 +11,11 @@
 namespace pa {
 
 bool launch_decode_mfma(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, bool multi_query,
-                        int tiles_per_wave, int waves_per_group, dim3 grid, hipStream_t stream);
+                        int tiles_per_wave, int waves_per_group, dim3 grid, hipStream_t stream,
+                        const LaunchEvents& ev);
+bool mfma_kernel_built(int ct, int qt, int head_dim, int bs, bool multi_query, bool row_scales);
 bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, int group,
-                        dim3 grid, hipStream_t stream);
+                        dim3 grid, hipStream_t stream, const LaunchEvents& ev);
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
 
 // Workgroups per (KV head, sequence) -- one for decode, more when its
@@ -93,10 +95,13 @@ int device_cu_count() {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   if (dev < 64 && cache[dev] > 0) return cache[dev];
   int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = kPlanMaxCUs;
   if (dev < 64) cache[dev] = n;
   return n;
 }
+
+// compute units a launch plans with: the device's, at most kPlanMaxCUs
+static int plan_cus() { return std::min(device_cu_count(), kPlanMaxCUs); }
 
 // virtual chunks a sequence is charged on the line for its fixed costs
 static int segment_cost() {
@@ -106,18 +111,18 @@ static int segment_cost() {
 }
 
 // waves the grid gives each CU: one per SIMD, or two for the kernels that
-// run two per SIMD
+// run two per SIMD (PA_DECODE_WAVES_PER_CU overrides it, within
+// [1, kMaxWavesPerCU])
 static int waves_per_cu(bool two_waves) {
   const char* v = std::getenv("PA_DECODE_WAVES_PER_CU");
   const int n = v ? std::atoi(v) : 0;
-  return n >= 1 && n <= 32 ? n : (two_waves ? 8 : 4);
+  return n >= 1 && n <= kMaxWavesPerCU ? n : (two_waves ? 8 : 4);
 }
 
-DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq,
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int64_t waves, int nq,
                        bool multi_query, bool two_waves) {
   (void)bs;
   DecodePlan p{};
-  const int64_t waves = (int64_t)waves_per_cu(two_waves) * num_cu;
   const int64_t per = (int64_t)Hkv * head_tiles;
   p.nslices = (int)std::max<int64_t>(1, (waves + per - 1) / per);
   p.min_slice = 4;
@@ -135,10 +140,23 @@ DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int he
   return p;
 }
 
+// The bound plans the most slices any launch can have (kMaxWavesPerCU waves
+// on each of kPlanMaxCUs CUs, one head tile per KV head) at both
+// occupancies, so it depends on the arguments alone, not on the device.
 size_t decode_workspace_bound(int B, int Hkv, int G, int D, int bs, int max_ctx, int nq, bool multi_query) {
-  const int cu = device_cu_count();
-  return std::max(plan_decode(B, Hkv, G, D, bs, max_ctx, 1, cu, nq, multi_query, false).bytes,
-                  plan_decode(B, Hkv, G, D, bs, max_ctx, 1, cu, nq, multi_query, true).bytes);
+  const int64_t waves = (int64_t)kMaxWavesPerCU * kPlanMaxCUs;
+  return std::max(plan_decode(B, Hkv, G, D, bs, max_ctx, 1, waves, nq, multi_query, false).bytes,
+                  plan_decode(B, Hkv, G, D, bs, max_ctx, 1, waves, nq, multi_query, true).bytes);
+}
+
+// Events the next decode call records around its attention kernels
+// (pa_time_next_attention_kernel); one pair per thread.
+static thread_local hipEvent_t g_time_start = nullptr;
+static thread_local hipEvent_t g_time_stop = nullptr;
+
+void set_timing_events(hipEvent_t start, hipEvent_t stop) {
+  g_time_start = start;
+  g_time_stop = stop;
 }
 
 // Long query chunks on a 16-bit cache: 2 = workgroups of kSharedWaves1 waves
@@ -197,8 +215,8 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const bool shared = shared1 || (shared_mode >= 1 && tw == 2 && tiles >= kSharedWaves);
   const int group_waves = shared1 ? kSharedWaves1 : (shared ? kSharedWaves : 1);
   const int group_tiles = (tiles + group_waves - 1) / group_waves;  // workgroups per (slice, KV head)
-  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles, device_cu_count(), nq, mq,
-                                      two_waves);
+  const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles,
+                                      (int64_t)waves_per_cu(two_waves) * plan_cus(), nq, mq, two_waves);
   if (r.workspace_bytes < plan.bytes) {
     set_error("pa_decode: workspace of %zu bytes needed, %zu given", plan.bytes, r.workspace_bytes);
     return PA_ERR_WORKSPACE;
@@ -210,6 +228,13 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const int64_t grid_waves = (int64_t)plan.nslices * r.Hkv * tiles;
   if (grid_waves >= ((int64_t)1 << 31)) {
     set_error("pa_decode: %lld waves exceed the grid limit", (long long)grid_waves);
+    return PA_ERR_UNSUPPORTED;
+  }
+  // Every choice that can refuse the call is made before anything is
+  // enqueued (the fp8 append below writes the cache).
+  if (!valu && !mfma_kernel_built(r.cache_dtype, r.q_dtype, r.D, r.bs, mq, rs)) {
+    set_error("pa_decode: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d", r.cache_dtype,
+              r.q_dtype, r.D, r.bs);
     return PA_ERR_UNSUPPORTED;
   }
   const int Hq = r.Hkv * r.G;
@@ -251,9 +276,14 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const int ct = r.cache_dtype, qt = r.q_dtype;
   const size_t out_row = (size_t)Hq * r.D * elem_size(r.out_dtype);
   const size_t q_row = (size_t)Hq * r.D * 2;
+  // timing events of this call, if the caller asked for them: start on the
+  // first attention kernel, stop on the last
+  const hipEvent_t t_start = g_time_start, t_stop = g_time_stop;
+  g_time_start = g_time_stop = nullptr;
   // batches beyond one launch's scan capacity run as consecutive launches;
   // they share the workspace, which stream order makes safe
   for (int s0 = 0; s0 < r.B; s0 += plan.sub_batch) {
+    const LaunchEvents ev{s0 == 0 ? t_start : nullptr, s0 + plan.sub_batch >= r.B ? t_stop : nullptr};
     a.B = std::min(plan.sub_batch, r.B - s0);
     // decode rows follow the sequences; query rows are named by q_start
     a.out = reinterpret_cast<uint8_t*>(r.out) + (mq ? 0 : (size_t)s0 * out_row);
@@ -265,8 +295,8 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     a.new_k = fused_append ? reinterpret_cast<const uint8_t*>(r.new_k) + (size_t)s0 * new_row : nullptr;
     a.new_v = fused_append ? reinterpret_cast<const uint8_t*>(r.new_v) + (size_t)s0 * new_row : nullptr;
     const dim3 grid((unsigned)((int64_t)plan.nslices * r.Hkv * group_tiles));
-    const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream)
-                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, tw, group_waves, grid, stream);
+    const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream, ev)
+                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, tw, group_waves, grid, stream, ev);
     if (!ok) {
       set_error("pa_decode: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d, group %d (%s)",
                 ct, qt, r.D, r.bs, r.G, valu ? "valu" : "mfma");

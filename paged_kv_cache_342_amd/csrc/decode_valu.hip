@@ -319,7 +319,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
 
 #define PA_VALU_CASE(CT, QT, D, BS, G)                                                            \
   if (ct == CT::code && qt == QT::code && head_dim == D && bs == BS && group == G) {              \
-    hipLaunchKernelGGL((decode_valu_kernel<CT, QT, D, BS, G>), grid, dim3(64), 0, stream, a);    \
+    launch_with_events(decode_valu_kernel<CT, QT, D, BS, G>, grid, dim3(64), stream, ev, a);      \
     return true;                                                                                  \
   }
 
@@ -332,12 +332,8 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
   PA_VALU_G(CT, QT, D, 16)    \
   PA_VALU_G(CT, QT, D, 32)
 
-// group 4 is built only for the block size and head_dim of the measured
-// grouped-query workloads, to compare against the MFMA kernel
-#define PA_VALU_G4(CT, QT) PA_VALU_CASE(CT, QT, 128, 16, 4)
-
 bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, int group,
-                        dim3 grid, hipStream_t stream) {
+                        dim3 grid, hipStream_t stream, const LaunchEvents& ev) {
   PA_VALU_BS(F16, F16, 64)
   PA_VALU_BS(F16, F16, 128)
   PA_VALU_BS(BF16, BF16, 64)
@@ -346,15 +342,12 @@ bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int b
   PA_VALU_BS(FP8, F16, 128)
   PA_VALU_BS(FP8, BF16, 64)
   PA_VALU_BS(FP8, BF16, 128)
-  PA_VALU_G4(F16, F16)
-  PA_VALU_G4(BF16, BF16)
-  PA_VALU_G4(FP8, BF16)
   return false;
 }
 
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group) {
-  if (group == 1 || group == 2) return true;
-  return group == 4 && head_dim == 128 && bs == 16 && (ct == qt || ct == FP8::code);
+  (void)ct, (void)qt, (void)head_dim, (void)bs;
+  return group == 1 || group == 2;
 }
 
 }  // namespace pa

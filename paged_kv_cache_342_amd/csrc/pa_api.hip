@@ -101,6 +101,12 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
                         num_blocks, src_dtype, cache_dtype, k_scale, v_scale, reinterpret_cast<hipStream_t>(stream));
 }
 
+pa_status pa_time_next_attention_kernel(void* start_event, void* stop_event) {
+  g_error[0] = 0;
+  set_timing_events(reinterpret_cast<hipEvent_t>(start_event), reinterpret_cast<hipEvent_t>(stop_event));
+  return PA_OK;
+}
+
 size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                                 int32_t block_size, int32_t max_context_len) {
   if (B <= 0 || num_kv_heads <= 0 || gqa_group <= 0 || max_context_len <= 0) return 0;
@@ -114,7 +120,7 @@ size_t pa_decode_workspace_size(int32_t B, int32_t num_kv_heads, int32_t gqa_gro
 namespace pa {
 
 // Checks shared by pa_decode and pa_decode_append; fills r on success.
-static pa_status decode_request(const char* fn, void* out, const void* q, const void* k_cache,
+pa_status decode_request(const char* fn, void* out, const void* q, const void* k_cache,
                                 const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                                 int32_t B, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                                 int32_t block_size, int64_t num_blocks, int32_t max_blocks_per_seq,

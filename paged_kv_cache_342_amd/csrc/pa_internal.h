@@ -22,19 +22,36 @@ struct DecodePlan {
 
 // most queries per sequence pa_decode_multi takes
 constexpr int kMaxQueries = 1024;
+// A launch plans for at most this many compute units (every gfx950 part has
+// 256; a device with more would use 256 of them for the split) and at most
+// kMaxWavesPerCU waves on each, so that workspace sizes are a function of the
+// call's arguments alone.
+constexpr int kPlanMaxCUs = 256;
+constexpr int kMaxWavesPerCU = 8;
 
 // compute units of the current device (cached per device)
 int device_cu_count();
 
+// waves: slices are planned for this many waves in the grid.
 // nq: queries per sequence at most (1 for decode); partial rows scale with it.
 // multi_query: the launch uses the several-queries kernel (fewer sequences per launch).
 // two_waves: the kernel runs two waves per SIMD (twice the slices, half the
 // sequences per launch: mfma_two_waves()).
-DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int num_cu, int nq,
+DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int64_t waves, int nq,
                        bool multi_query, bool two_waves);
-// Workspace bytes that cover every kernel choice for these sizes (one tile
-// per KV head, either occupancy).
+// Workspace bytes that cover every kernel choice and device for these sizes
+// (the most slices a launch can have, either occupancy).
 size_t decode_workspace_bound(int B, int Hkv, int G, int D, int bs, int max_ctx, int nq, bool multi_query);
+
+// Events an attention-kernel launch records (hipExtLaunchKernel's start and
+// stop events; null = not recorded).
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+// The pair the next decode call on this thread records around its attention
+// kernels (pa_time_next_attention_kernel).
+void set_timing_events(hipEvent_t start, hipEvent_t stop);
 
 struct DecodeRequest {
   void* out;

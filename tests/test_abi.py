@@ -132,6 +132,22 @@ def test_decode_workspace_checks():
     assert pa.decode_workspace_size(0, 4, 1, 64, 16, 100) == 0
 
 
+def test_workspace_size_depends_on_the_arguments_alone():
+    """The size covers every kernel choice and device: a process whose
+    occupancy override differs gets the same sizes."""
+    import subprocess
+    import sys
+
+    cases = [(64, 8, 4, 128, 16, 4096), (32, 8, 8, 128, 16, 8000), (256, 8, 4, 128, 8, 32768), (3, 2, 1, 64, 32, 100)]
+    here = [pa.decode_workspace_size(*c) for c in cases]
+    code = ("import sys; sys.path.insert(0, %r); import paged_kv_cache_342_amd as pa; "
+            "print([pa.decode_workspace_size(*c) for c in %r])" % (ROOT, cases))
+    for waves in ("1", "8", "32"):
+        env = dict(os.environ, PA_DECODE_WAVES_PER_CU=waves)
+        got = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True)
+        assert eval(got.stdout.strip()) == here
+
+
 def test_empty_calls_are_no_ops():
     lib = pa.library()
     assert _decode(B=0, out=None, q=None, bt=None, cl=None) == pa.OK

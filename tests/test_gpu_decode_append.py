@@ -60,9 +60,8 @@ def test_decode_append_tiny():
         _check_append(W.tiny(), variant=v)
 
 
-@pytest.mark.parametrize("variant", [None, "valu"])
-def test_decode_append_llama8b_reduced(variant):
-    _check_append(W.llama8b(B=6), variant=variant, label="[B=6]")
+def test_decode_append_llama8b_reduced():
+    _check_append(W.llama8b(B=6), label="[B=6]")
 
 
 def test_decode_append_llama8b_full_size_sampled():
@@ -82,6 +81,17 @@ def test_decode_append_shared_prefix_reduced():
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_decode_append_heavy_tail_reduced(bs):
     _check_append(W.heavy_tail(bs=bs, B=24), label="[B=24]")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_decode_append_heavy_tail_full_size_sampled(bs):
+    """One decode step of the whole heavy-tailed batch (256 sequences, fp8
+    cache, the append a scatter by table) at each block size the bench sweeps:
+    the two longest, the shortest and the median sequence."""
+    w = W.heavy_tail(bs=bs)
+    order = np.argsort(w.context_lens)
+    seqs = sorted({int(order[-1]), int(order[-2]), int(order[0]), int(order[len(order) // 2])})
+    _check_append(w, seqs=seqs, label=f"[full, sampled, bs={bs}]")
 
 
 @pytest.mark.parametrize("cache,q", [("f16", "f16"), ("bf16", "bf16"), ("fp8", "bf16")])

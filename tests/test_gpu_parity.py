@@ -122,9 +122,36 @@ def test_decode_tiny():
         _check_decode(W.tiny(), variant=v)
 
 
-@pytest.mark.parametrize("variant", [None, "valu"])
-def test_decode_llama8b_reduced(variant):
-    _check_decode(W.llama8b(B=6), variant=variant, label="[B=6]")
+def test_max_context_len_zero_plans_with_every_table_entry():
+    """max_context_len <= 0 means max_blocks_per_seq * block_size, in the C
+    call and in the binding (which sizes the workspace with it): the result
+    equals the call given the true bound, bit for bit."""
+    w = W.llama8b(B=3)
+    g = GpuBatch(w)
+    base = g.decode().cpu()
+    for mcl in (0, -1):
+        assert torch.equal(g.decode(max_context_len=mcl).cpu().view(torch.int32), base.view(torch.int32))
+
+
+def test_workspace_size_is_the_same_with_no_device_visible():
+    """The workspace size is a function of the arguments: this process (one
+    MI355X visible) and a process that sees no device get the same sizes."""
+    import subprocess
+    import sys
+
+    cases = [(64, 8, 4, 128, 16, 4096), (32, 8, 8, 128, 16, 8000), (256, 8, 4, 128, 8, 32768)]
+    here = [pa.decode_workspace_size(*c) for c in cases]
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r); import paged_kv_cache_342_amd as pa; "
+            "print([pa.decode_workspace_size(*c) for c in %r])" % (root, cases))
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    got = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert got.returncode == 0, got.stderr[-2000:]
+    assert eval(got.stdout.strip().splitlines()[-1]) == here
+
+
+def test_decode_llama8b_reduced():
+    _check_decode(W.llama8b(B=6), label="[B=6]")
 
 
 def test_decode_llama8b_full_size_sampled():
@@ -157,8 +184,11 @@ def test_decode_heavy_tail_reduced(bs):
     _check_decode(W.heavy_tail(bs=bs, B=24), label=f"[B=24]")
 
 
-def test_decode_heavy_tail_full_size_sampled():
-    w = W.heavy_tail(bs=16)
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_decode_heavy_tail_full_size_sampled(bs):
+    """The whole 256-sequence heavy-tailed batch at each block size the bench
+    sweeps, checked on its two longest, its shortest and its median sequence."""
+    w = W.heavy_tail(bs=bs)
     order = np.argsort(w.context_lens)
     seqs = sorted({int(order[-1]), int(order[-2]), int(order[0]), int(order[len(order) // 2])})
     _check_decode(w, seqs=seqs, label="[full, sampled]")
@@ -188,8 +218,18 @@ def test_decode_many_heads_per_kv_head(G):
     _check_decode(w)
 
 
-def test_decode_forced_valu_group4():
-    _check_decode(W.llama8b(B=4), variant="valu", label="[valu g4]")
+def test_decode_forced_valu_is_built_for_groups_1_and_2_only():
+    """The VALU/DPP kernel is kept for groups 1 and 2; forcing it at group 4
+    is refused on the host before any launch."""
+    w = W.llama8b(B=4)
+    g = GpuBatch(w)
+    set_variant("valu")
+    try:
+        with pytest.raises(pa.PagedAttentionError) as e:
+            g.decode()
+        assert e.value.status == pa.ERR_UNSUPPORTED
+    finally:
+        set_variant(None)
 
 
 def test_decode_empty_context_rows_are_zero():

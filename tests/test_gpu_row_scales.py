@@ -2,12 +2,26 @@
 for bit (codes and scales), the block copy bit for bit, and the decode
 against the oracle.
 
-Decode bound: rows of unit magnitude meet the FP8 gate (max-abs 3e-2,
-relative L2 1e-3).  Rows spread over six decades are checked against a bound
-taken from the arithmetic: the kernel weights V by the probability times the
-row's scale rounded to fp16 (a relative error of 2^-11 per weight, fp32
-sums), so the absolute error may reach 2^-11 of the largest |V| on top of
-the gate; relative L2 stays at 1e-3."""
+Decode bound, from the kernel's arithmetic (fp32 output against the fp64
+oracle over the same codes and scales):
+  |out - ref| <= 3e-2 + (pv + 2 * (D + 8) * 2^-24 * A) * max|V|
+* pv: PV takes each weight w = p * v_scale as two bf16 terms hi + lo with
+  hi = RNE(w) and lo = RNE(w - hi), which hold w to 2^-18 relative; the
+  products with the (exactly widened) codes are exact in fp32, and the
+  accumulator rounds at most L/8 + 16 times (two MFMAs per 16 positions,
+  rescales, the merge), 2^-24 each; 2^-21 covers the exp2 approximation of
+  p, which the denominator shares only in part.  pv = 2^-17 + 2^-21 +
+  (L_max / 8 + 16) * 2^-24, about 2^-16 at L_max = 1031.
+* scores: q . k sums D exact products in fp32 and is then scaled twice;
+  each of at most D + 8 roundings is within 2^-24 of A = max over heads and
+  positions of scale * sum_d |q_d| |k_d| (K dequantised), so a score is off
+  by at most (D + 8) 2^-24 A, and the normalised weights by twice that,
+  relative.
+Rows of unit magnitude meet the FP8 gate (max-abs 3e-2, relative L2 1e-3).
+Rows whose K and V both spread over six decades have scores of ~1e4, where
+the score term dominates; rows whose V alone spreads, with the query scaled
+by 2^-4, leave the PV term alone, so a coarser PV (fp16 weights, 2^-11)
+would fail there."""
 import numpy as np
 import pytest
 import torch
@@ -20,19 +34,22 @@ from tests.gpu_util import errors, log, storage_to_torch
 pytestmark = pytest.mark.gpu
 
 
-def _rows(w, spread, seed):
+def _rows(w, spread, seed, k_spread=None):
     """Every sequence's K/V rows (bf16 storage), each (token, head) row scaled
-    by 10^U(-spread, spread) so rows differ in magnitude; and their slots."""
+    by 10^U(-spread, spread) so rows differ in magnitude (K by
+    10^U(-k_spread, k_spread) when given); and their slots."""
     rng = np.random.default_rng(seed)
     ks, vs, slots = [], [], []
+    k_spread = spread if k_spread is None else k_spread
     for s in range(w.B):
         L = int(w.context_lens[s])
         if L == 0:
             continue
         k, v = w.seq_kv(s)
-        f = 10.0 ** rng.uniform(-spread, spread, size=(2, L, w.Hkv, 1))
-        ks.append(W.to_storage(W.storage_to_f32(k, "bf16") * f[0].astype(np.float32), "bf16"))
-        vs.append(W.to_storage(W.storage_to_f32(v, "bf16") * f[1].astype(np.float32), "bf16"))
+        u = rng.uniform(-1.0, 1.0, size=(2, L, w.Hkv, 1))
+        fk, fv = 10.0 ** (k_spread * u[0]), 10.0 ** (spread * u[1])
+        ks.append(W.to_storage(W.storage_to_f32(k, "bf16") * fk.astype(np.float32), "bf16"))
+        vs.append(W.to_storage(W.storage_to_f32(v, "bf16") * fv.astype(np.float32), "bf16"))
         slots.append(O.slots_for(w.block_tables[s], 0, L, w.bs))
     return np.concatenate(ks), np.concatenate(vs), np.concatenate(slots).astype(np.int64)
 
@@ -92,11 +109,29 @@ def test_scatter_with_row_scales_is_bit_exact(cd):
         assert np.array_equal(kc[0, 0, 0].cpu().view(torch.uint8).numpy(), want)
 
 
-def _bound(ovc, ovs, spread, cd="fp8"):
-    if spread == 0:
-        return 3e-2
-    vmax = np.nanmax(np.abs(O.widen_rows(ovc, ovs, cd)))
-    return 3e-2 + 2.0 ** -10 * vmax
+def _bound(w, q, okc, oks, ovc, ovs, seqs=None):
+    """The decode bound of the module docstring for these pools and queries
+    (q in storage form), over the sequences `seqs` (default: all)."""
+    cd, D = w.cache_dtype, w.D
+    seqs = range(w.B) if seqs is None else seqs
+    vmax = float(np.nanmax(np.abs(O.widen_rows(ovc, ovs, cd))))
+    A, lmax = 0.0, 0
+    for s in seqs:
+        L = int(w.context_lens[s])
+        if L == 0:
+            continue
+        lmax = max(lmax, L)
+        k = O.widen_rows(O.gather_kv(okc, w.block_tables[s], L),
+                         O.gather_kv(oks[..., None], w.block_tables[s], L)[..., 0], cd)  # [L, Hkv, D]
+        qa = np.abs(O.widen(q[s], w.q_dtype)).reshape(w.Hkv, w.group, D)
+        A = max(A, float(np.einsum("hgd,lhd->hgl", qa, np.abs(k)).max()) * abs(w.scale))
+    pv = 2.0 ** -17 + 2.0 ** -21 + (lmax / 8 + 16) * 2.0 ** -24
+    return 3e-2 + (pv + 2 * (D + 8) * 2.0 ** -24 * A) * vmax
+
+
+def _scaled_query(w, factor):
+    """The workload's queries times a power of two, in their storage dtype."""
+    return W.to_storage(W.storage_to_f32(w.query(), w.q_dtype) * np.float32(factor), w.q_dtype)
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -117,9 +152,34 @@ def test_decode_with_row_scales(D, bs, q, spread, cd):
         ref = O.decode_scaled(w.query(), okc, ovc, oks, ovs, w.block_tables, w.context_lens, w.scale, g, q,
                               cache_dtype=cd)
         ma, rel = errors(out, ref)
-        bound = _bound(ovc, ovs, spread, cd)
+        bound = _bound(w, w.query(), okc, oks, ovc, ovs)
         log(f"[row scales {cd} D={D} bs={bs} q={q} g={g} spread={spread}] max_abs={ma:.2e} (bound {bound:.2e}) "
             f"rel_l2={rel:.2e}")
+        assert np.isfinite(out).all() and ma <= bound and rel <= 1e-3
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("q", ["f16", "bf16"])
+@pytest.mark.parametrize("cd", ["fp8", "fp4"])
+def test_decode_with_row_scales_pv_precision(D, q, cd):
+    """V rows spread over six decades, K rows of unit magnitude and the query
+    scaled by 2^-4: scores stay small, so the bound is about (2^-16 + 2^-19)
+    max|V| and measures PV's precision."""
+    lens = [1, 7, 33, 129, 517, 1031]
+    for g in (1, 4, 8):
+        w = W.custom(f"rs_pv_{cd}_D{D}_{q}_g{g}", 74 + g, lens, 2 * g, 2, D, 16, cd, q)
+        k, v, slots = _rows(w, 3.0, 84 + g, k_spread=0.0)
+        (kc, vc, kss, vss), (okc, ovc, oks, ovs) = _pools(w, k, v, slots)
+        qs = _scaled_query(w, 2.0 ** -4)
+        out = pa.decode_scaled(storage_to_torch(qs, q).cuda(), kc, vc, kss, vss,
+                               torch.from_numpy(w.block_tables).cuda(), torch.from_numpy(w.context_lens).cuda(),
+                               w.scale, out_dtype=torch.float32).cpu().numpy().astype(np.float64)
+        ref = O.decode_scaled(qs, okc, ovc, oks, ovs, w.block_tables, w.context_lens, w.scale, g, q, cache_dtype=cd)
+        ma, rel = errors(out, ref)
+        bound = _bound(w, qs, okc, oks, ovc, ovs)
+        vmax = float(np.nanmax(np.abs(O.widen_rows(ovc, ovs, cd))))
+        log(f"[row scales PV {cd} D={D} q={q} g={g}] max_abs={ma:.2e} = {ma / vmax:.2e} max|V| "
+            f"(bound {bound:.2e} = {bound / vmax:.2e} max|V|) rel_l2={rel:.2e}")
         assert np.isfinite(out).all() and ma <= bound and rel <= 1e-3
 
 
@@ -141,7 +201,7 @@ def test_decode_with_row_scales_heavy_tail_full_size_sampled(cd):
     ref = O.decode_scaled(w.query(), okc, ovc, oks, ovs, w.block_tables, w.context_lens, w.scale, w.group,
                           w.q_dtype, seqs=seqs, cache_dtype=cd)
     ma, rel = errors(out[seqs], ref)
-    bound = _bound(ovc, ovs, 3.0, cd)
+    bound = _bound(w, w.query(), okc, oks, ovc, ovs, seqs)
     log(f"[row scales heavy tail {cd}] max_abs={ma:.2e} (bound {bound:.2e}) rel_l2={rel:.2e}")
     assert np.isfinite(out).all() and ma <= bound and rel <= 1e-3
 
@@ -236,4 +296,4 @@ def test_fp4_batch_across_launches():
                           cache_dtype="fp4")
     ma, rel = errors(out, ref)
     log(f"[fp4, 2100 sequences in two launches] max_abs={ma:.2e} rel_l2={rel:.2e}")
-    assert np.isfinite(out).all() and ma <= _bound(ovc, ovs, 1.0, "fp4") and rel <= 1e-3
+    assert np.isfinite(out).all() and ma <= _bound(w, w.query(), okc, oks, ovc, ovs) and rel <= 1e-3

@@ -365,6 +365,73 @@ def test_round_to_bf16_matches_torch():
     assert np.array_equal(ours, ref)
 
 
+# ---------------------------------------------------------------- widening of 16-bit storage
+
+def _binary_format_value(bits, exp_bits, frac_bits):
+    """Value of every bit pattern of an IEEE-style binary format, from its
+    definition: (-1)^s 2^(e - bias) (1 + f / 2^frac_bits) for normal
+    exponents, (-1)^s 2^(1 - bias) f / 2^frac_bits for e = 0, infinity or NaN
+    for the all-ones exponent (Python integers and ldexp, no float casts)."""
+    bias = (1 << (exp_bits - 1)) - 1
+    out = []
+    for b in bits.tolist():
+        s = -1.0 if b >> (exp_bits + frac_bits) else 1.0
+        e = (b >> frac_bits) & ((1 << exp_bits) - 1)
+        f = b & ((1 << frac_bits) - 1)
+        if e == (1 << exp_bits) - 1:
+            out.append(s * math.inf if f == 0 else math.nan)
+        elif e == 0:
+            out.append(s * math.ldexp(f, 1 - bias - frac_bits))
+        else:
+            out.append(s * math.ldexp((1 << frac_bits) + f, e - bias - frac_bits))
+    return np.array(out, np.float64)
+
+
+def _same_values(a, b):
+    """Equal as float64, NaN positions equal, and zeros of the same sign."""
+    nan = np.isnan(a)
+    if not np.array_equal(nan, np.isnan(b)):
+        return False
+    a, b = a[~nan], b[~nan]
+    return np.array_equal(a, b) and np.array_equal(np.signbit(a), np.signbit(b))
+
+
+ALL16 = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+
+
+def test_widen_bf16_every_bit_pattern():
+    """bf16 -> fp64 over all 65,536 patterns against the format's definition
+    (8 exponent bits, bias 127, 7 fraction bits) and against torch's
+    bfloat16 -> float64 conversion."""
+    ours = O.widen(ALL16, "bf16")
+    assert _same_values(ours, _binary_format_value(ALL16, 8, 7))
+    ref = torch.from_numpy(ALL16.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert _same_values(ours, ref)
+
+
+def test_widen_f16_every_bit_pattern():
+    """f16 -> fp64 over all 65,536 patterns against IEEE binary16 (5 exponent
+    bits, bias 15, 10 fraction bits) and against torch's conversion."""
+    ours = O.widen(ALL16.view(np.float16), "f16")
+    assert _same_values(ours, _binary_format_value(ALL16, 5, 10))
+    ref = torch.from_numpy(ALL16.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    assert _same_values(ours, ref)
+
+
+@pytest.mark.parametrize("mistake", ["shift15", "as_f16", "byteswap", "low_half"])
+def test_widen_pins_catch_planted_mistakes(mistake):
+    bits = ALL16.astype(np.uint32)
+    if mistake == "shift15":
+        bad = (bits << 15).view(np.float32).astype(np.float64)
+    elif mistake == "as_f16":
+        bad = ALL16.view(np.float16).astype(np.float64)
+    elif mistake == "byteswap":
+        bad = (ALL16.byteswap().astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:  # the pattern in the low half of the binary32
+        bad = bits.view(np.float32).astype(np.float64)
+    assert not _same_values(bad, _binary_format_value(ALL16, 8, 7))
+
+
 # ---------------------------------------------------------------- planted mistakes
 
 def _pins_pass(attend):

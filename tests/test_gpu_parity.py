@@ -234,13 +234,15 @@ def test_decode_forced_valu_is_built_for_groups_1_and_2_only():
 
 def test_decode_empty_context_rows_are_zero():
     lens = [0, 5, 0, 300]
-    w = W.custom("empty", 3, lens, 8, 2, 128, 16, "bf16")
-    for v in ("valu", "mfma"):
+    # the VALU/DPP kernel is built for groups 1 and 2, the MFMA kernel for all
+    for g, v in ((2, "valu"), (2, "mfma"), (4, "mfma")):
+        w = W.custom(f"empty_g{g}", 3, lens, 2 * g, 2, 128, 16, "bf16")
         set_variant(v)
         out = GpuBatch(w).decode().cpu()
         assert torch.equal(out[0], torch.zeros_like(out[0])) and torch.equal(out[2], torch.zeros_like(out[2]))
         assert torch.isfinite(out).all()
-    _check_decode(w)
+        _check_decode(w, variant=v)
+    set_variant(None)
 
 
 # ------------------------------------------------------------------ output dtypes

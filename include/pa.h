@@ -295,6 +295,32 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
                            void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * pa_decode_append for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that never call hipMalloc,
+ * harnesses that forbid allocation.  It takes no workspace: the split-K
+ * partials live in a scratch array the library holds in device memory,
+ * 64 MiB on each device it runs on (set aside when the library's code is
+ * loaded there, kept until the process ends; its address is looked up once
+ * per device, on the first call there).  The call itself allocates and
+ * frees nothing.  Sizes whose pa_decode_workspace_size(B, num_kv_heads,
+ * gqa_group, head_dim, block_size, max_context_len) exceeds 64 MiB (with
+ * max_context_len <= 0 read as max_blocks_per_seq * block_size) return
+ * PA_ERR_WORKSPACE before anything is enqueued.  Every call on one device
+ * shares that device's array: calls whose work may overlap on one device
+ * (streams with no ordering between them) race and give unspecified
+ * results; calls ordered on one stream, or by events, do not.  The array
+ * needs no clearing: each call writes every part of it that it reads.
+ * Otherwise, arguments, results and errors are those of pa_decode_append.
+ */
+pa_status pa_decode_append_noalloc(void* out, const void* q, void* k_cache, void* v_cache, const void* key,
+                                   const void* value, pa_dtype src_dtype, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t B, int32_t num_kv_heads, int32_t gqa_group,
+                                   int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                   int32_t max_blocks_per_seq, int32_t max_context_len, float scale, float k_scale,
+                                   float v_scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                                   pa_stream_t stream);
+
+/*
  * Copy-on-write: for each n < N with (src, dst) = block_mapping[n],
  *   k_cache[dst] = k_cache[src] and v_cache[dst] = v_cache[src]
  * byte for byte (whole [num_kv_heads, block_size, head_dim] chunks; an

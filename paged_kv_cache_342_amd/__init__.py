@@ -101,6 +101,9 @@ def _load(path: str) -> ctypes.CDLL:
     lib.pa_last_error_message.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
     lib.pa_version.restype = ctypes.c_char_p
+    lib.pa_decode_append_noalloc.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i64, i32, i32,
+                                             f32, f32, f32, i32, i32, i32, p]
+    lib.pa_decode_append_noalloc.restype = ctypes.c_int
     lib.pa_time_next_attention_kernel.argtypes = [p, p]
     lib.pa_time_next_attention_kernel.restype = ctypes.c_int
     lib.pa_is_checked_build.argtypes = []
@@ -257,6 +260,37 @@ def decode_append(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _ptr(block_tables), _ptr(context_lens), B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
         _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
         _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def decode_append_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, key: torch.Tensor,
+                          value: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                          out: torch.Tensor, max_context_len: Optional[int] = None, k_scale: float = 1.0,
+                          v_scale: float = 1.0) -> torch.Tensor:
+    """decode_append() through pa_decode_append_noalloc, which allocates
+    nothing: the split partials live in the library's own per-device scratch
+    array (64 MiB).  The caller passes every tensor, `out` included; sizes
+    whose partials do not fit raise PagedAttentionError(ERR_WORKSPACE).
+    Calls that overlap on one device share that array and race."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (key, "key"), (value, "value")):
+        _require(t, n)
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or Hq % Hkv:
+        raise ValueError("q, k_cache and v_cache shapes do not agree")
+    if key.shape != (B, Hkv, D) or value.shape != key.shape:
+        raise ValueError("key and value must be [B, num_kv_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, M] and context_lens [B]")
+    M = block_tables.shape[1]
+    out = _out(out, (B, Hq, D), None, q)
+    _check(library().pa_decode_append_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(key), _ptr(value), _TORCH_CODE.get(key.dtype, -9),
+        _ptr(block_tables), _ptr(context_lens), B, Hkv, Hq // Hkv, D, bs, nb, M, _max_context(max_context_len, M, bs),
+        scale, k_scale, v_scale, _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9),
+        _TORCH_CODE.get(out.dtype, -9), _stream(q)))
     return out
 
 

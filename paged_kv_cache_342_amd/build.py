@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 LIB_CHECKED = os.path.join(PKG, "libpa_checked.so")
 
-SOURCES = ["pa_api.hip", "decode_core.hip", "decode_mfma.hip", "decode_valu.hip", "cache_ops.hip"]
+SOURCES = ["pa_api.hip", "pa_noalloc.hip", "decode_core.hip", "decode_mfma.hip", "decode_valu.hip", "cache_ops.hip"]
 HOST_SOURCES = ["block_manager.cpp"]  # host-only C++, built with the host compiler
 CHECKED_SOURCES = ["pa_api.hip", "contract_check.hip"]  # compiled again with PA_CHECKED
 

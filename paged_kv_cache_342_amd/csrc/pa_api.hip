@@ -193,6 +193,18 @@ pa_status decode_request(const char* fn, void* out, const void* q, const void* k
   return PA_OK;
 }
 
+// The checks pa_decode_append adds to pa_decode's: the new rows' dtype and pointers.
+pa_status append_rows_check(const char* fn, pa_dtype src_dtype, pa_dtype cache_dtype, const void* key,
+                            const void* value, int32_t B) {
+  if (!known_dtype(src_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (cache_dtype == PA_FP8_E4M3 ? (src_dtype != PA_F16 && src_dtype != PA_BF16) : src_dtype != cache_dtype)
+    return fail(PA_ERR_UNSUPPORTED, "%s: new rows must have the cache dtype (f16 or bf16 for an fp8 cache)", fn);
+  if (B == 0) return PA_OK;
+  if (!key || !value) return fail(PA_ERR_INVALID_ARG, "%s: null key/value", fn);
+  if (!aligned(key, 16) || !aligned(value, 16)) return fail(PA_ERR_INVALID_ARG, "%s: misaligned key/value", fn);
+  return PA_OK;
+}
+
 }  // namespace pa
 
 extern "C" {
@@ -230,12 +242,8 @@ pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cach
                                       max_context_len, scale, k_scale, v_scale, q_dtype, cache_dtype, out_dtype,
                                       workspace, workspace_bytes, 1, false, false, r);
   if (st != PA_OK) return st;
-  if (!known_dtype(src_dtype)) return fail(PA_ERR_INVALID_ARG, "%s: unknown dtype", fn);
-  if (cache_dtype == PA_FP8_E4M3 ? (src_dtype != PA_F16 && src_dtype != PA_BF16) : src_dtype != cache_dtype)
-    return fail(PA_ERR_UNSUPPORTED, "%s: new rows must have the cache dtype (f16 or bf16 for an fp8 cache)", fn);
-  if (B == 0) return PA_OK;
-  if (!key || !value) return fail(PA_ERR_INVALID_ARG, "%s: null key/value", fn);
-  if (!aligned(key, 16) || !aligned(value, 16)) return fail(PA_ERR_INVALID_ARG, "%s: misaligned key/value", fn);
+  const pa_status sa = append_rows_check(fn, src_dtype, cache_dtype, key, value, B);
+  if (sa != PA_OK || B == 0) return sa;
   r.new_k = key;
   r.new_v = value;
   r.src_dtype = src_dtype;

@@ -90,6 +90,19 @@ bool decode_uses_valu(int variant, int G);
 
 pa_status decode_launch(const DecodeRequest& r, hipStream_t stream);
 
+// Host checks of the decode calls (pa_api.hip): decode_request validates
+// everything pa_decode takes and fills r, the workspace last (so a call with
+// no workspace that passes every other check gives PA_ERR_WORKSPACE);
+// append_rows_check adds pa_decode_append's checks of the new rows.
+pa_status decode_request(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t num_kv_heads,
+                         int32_t gqa_group, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                         int32_t max_blocks_per_seq, int32_t max_context_len, float scale, float k_scale,
+                         float v_scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
+                         size_t workspace_bytes, int nq, bool multi_query, bool row_scales, DecodeRequest& r);
+pa_status append_rows_check(const char* fn, pa_dtype src_dtype, pa_dtype cache_dtype, const void* key,
+                            const void* value, int32_t B);
+
 pa_status scatter_launch(const void* key, const void* value, void* k_cache, void* v_cache,
                          const int64_t* slots, int T, int Hkv, int D, int bs, int64_t num_blocks,
                          int src_dtype, int cache_dtype, float k_scale, float v_scale,

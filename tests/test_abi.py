@@ -148,6 +148,27 @@ def test_workspace_size_depends_on_the_arguments_alone():
         assert eval(got.stdout.strip()) == here
 
 
+def test_noalloc_refuses_sizes_beyond_its_scratch_on_the_host():
+    """pa_decode_append_noalloc checks the partials against its 64 MiB scratch
+    array before anything else, so an oversized batch is refused here, with
+    no GPU; a batch that fits proceeds to the usual argument checks."""
+    lib = pa.library()
+    big = dict(B=4000, Hkv=8, G=8, D=128, bs=16, M=2, mcl=32)
+    assert pa.decode_workspace_size(big["B"], big["Hkv"], big["G"], big["D"], big["bs"], big["mcl"]) > 64 << 20
+
+    def call(B, Hkv, G, D, bs, M, mcl, key=FAKE):
+        return lib.pa_decode_append_noalloc(FAKE, FAKE, FAKE, FAKE, key, key, pa.BF16, FAKE, FAKE, B, Hkv, G, D, bs,
+                                            1000, M, mcl, 0.1, 1.0, 1.0, pa.BF16, pa.BF16, pa.F32, None)
+
+    assert call(**big) == pa.ERR_WORKSPACE
+    assert b"scratch" in lib.pa_last_error_message()
+    assert call(**dict(big, mcl=0)) == pa.ERR_WORKSPACE  # <= 0 reads as M * bs
+    # fits: the ordinary checks run next (a null key is refused before any launch)
+    assert call(**dict(big, B=4), key=None) == pa.ERR_INVALID_ARG
+    assert call(**dict(big, D=96)) == pa.ERR_UNSUPPORTED
+    assert call(**dict(big, B=0)) == pa.OK
+
+
 def test_empty_calls_are_no_ops():
     lib = pa.library()
     assert _decode(B=0, out=None, q=None, bt=None, cl=None) == pa.OK

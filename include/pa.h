@@ -55,7 +55,9 @@
  *     need the device data): block ids in block tables and copy pairs lie in
  *     [0, num_blocks); slots are unique within one call; copy pairs have
  *     distinct destinations and no destination is also a source in the same
- *     call; 0 <= context_lens[s] <= max_context_len.  The kernels never read
+ *     call; 0 <= context_lens[s] <= max_context_len; for pa_decode_append,
+ *     the block that receives a sequence's new row (its block of position
+ *     L - 1) is read by no other table entry of the call.  The kernels never read
  *     or write outside the buffers when these are violated (out-of-range ids
  *     and slots are skipped, lengths are clamped), but results are then
  *     unspecified.
@@ -109,6 +111,8 @@ typedef enum {
 #define PA_VIOLATION_COPY_DST_REPEATED 0x20u /* two copy pairs with one destination */
 #define PA_VIOLATION_COPY_DST_IS_SRC 0x40u   /* a copy destination that is another pair's source */
 #define PA_VIOLATION_QUERY_START 0x80u       /* query_start not as pa_decode_multi requires */
+#define PA_VIOLATION_APPEND_BLOCK_SHARED 0x100u /* pa_decode_append: a sequence's block of position L - 1
+                                                   is also read by another table entry of the call */
 
 /* 1 in libpa_checked.so, 0 in libpa.so. */
 int32_t pa_is_checked_build(void);

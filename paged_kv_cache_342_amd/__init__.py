@@ -26,6 +26,7 @@ F32, F16, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NO_BLOCKS, ERR_CONTRACT = 0, -1, -2, -3, -4, -5, -6
 VIOLATION_BLOCK_ID, VIOLATION_CONTEXT_LEN, VIOLATION_SLOT, VIOLATION_SLOT_REPEATED = 0x01, 0x02, 0x04, 0x08
 VIOLATION_COPY_ID, VIOLATION_COPY_DST_REPEATED, VIOLATION_COPY_DST_IS_SRC, VIOLATION_QUERY_START = 0x10, 0x20, 0x40, 0x80
+VIOLATION_APPEND_BLOCK_SHARED = 0x100
 
 # an FP4 cache holds two E2M1 codes per byte: torch.float4_e2m1fn_x2, last dim head_dim / 2
 _TORCH_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3,

@@ -63,6 +63,44 @@ __global__ __launch_bounds__(64) void check_tables_kernel(const int32_t* tables,
 
 constexpr int kTile = 256;
 
+// pa_decode_append: the block that receives a sequence's new row (its block
+// of position L - 1) must be read by no other sequence of the call, nor
+// twice by its own table, since the decode kernel stores the row while
+// other waves of the launch read.  One wave per sequence s compares every
+// table entry s reads with the tail block of every sequence t, 64 tails at a
+// time from LDS; the entry that is t's own tail (t == s, at its index) is
+// the one allowed match.
+__global__ __launch_bounds__(64) void check_append_kernel(const int32_t* tables, const int32_t* lens, int B, int M,
+                                                          int bs, int max_ctx, uint32_t* word) {
+  __shared__ int tail_id[64];
+  __shared__ int tail_j[64];
+  const int s = blockIdx.x;
+  const int lane = threadIdx.x;
+  if (s >= B) return;
+  auto blocks_of = [&](int t) {
+    const int L = lens[t];
+    const int Lc = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+    return (Lc + bs - 1) / bs;  // <= M, since max_ctx <= M * bs
+  };
+  const int nblk = blocks_of(s);
+  bool shared = false;
+  for (int t0 = 0; t0 < B; t0 += 64) {
+    __syncthreads();
+    const int t = t0 + lane;
+    const int nb = t < B ? blocks_of(t) : 0;
+    tail_j[lane] = nb - 1;
+    tail_id[lane] = nb > 0 ? tables[(int64_t)t * M + nb - 1] : -1;
+    __syncthreads();
+    const int n = B - t0 < 64 ? B - t0 : 64;
+    for (int j = lane; j < nblk; j += 64) {
+      const int id = tables[(int64_t)s * M + j];
+      for (int u = 0; u < n; ++u)
+        if (tail_j[u] >= 0 && tail_id[u] == id && !(t0 + u == s && j == tail_j[u])) shared = true;
+    }
+  }
+  if (shared) flag(word, PA_VIOLATION_APPEND_BLOCK_SHARED);
+}
+
 // Slots: each non-negative slot lies below num_slots and appears once.  Thread
 // i compares its slot with every later one, a tile of 256 at a time from LDS.
 __global__ __launch_bounds__(kTile) void check_slots_kernel(const int64_t* slots, int T, int64_t num_slots,
@@ -127,6 +165,7 @@ static void describe(uint32_t bits, char* buf, size_t n) {
       {PA_VIOLATION_COPY_DST_REPEATED, "a copy destination given twice"},
       {PA_VIOLATION_COPY_DST_IS_SRC, "a copy destination that is another pair's source"},
       {PA_VIOLATION_QUERY_START, "a query range outside the contract"},
+      {PA_VIOLATION_APPEND_BLOCK_SHARED, "a block receiving a new row that another table entry of the call reads"},
   };
   size_t used = 0;
   buf[0] = 0;
@@ -177,6 +216,9 @@ pa_status check_decode_contract(const char* fn, const DecodeRequest& r, hipStrea
   }
   hipLaunchKernelGGL(check_tables_kernel, dim3((unsigned)r.B), dim3(64), 0, stream, r.block_tables, r.context_lens,
                      r.q_start, r.B, r.M, r.bs, r.max_ctx, r.num_blocks, r.q_start ? r.nq : 1, r.q_rows, word);
+  if (r.new_k != nullptr)
+    hipLaunchKernelGGL(check_append_kernel, dim3((unsigned)r.B), dim3(64), 0, stream, r.block_tables, r.context_lens,
+                       r.B, r.M, r.bs, r.max_ctx, word);
   const pa_status st = launched(fn);
   return st != PA_OK ? st : collect(fn, word, stream);
 }

@@ -105,6 +105,45 @@ def test_block_id_and_length_violations_are_rejected():
     pa.decode(b.q, b.kc, b.vc, b.tables, b.lens, w.scale, max_context_len=w.max_context_len)
 
 
+def test_append_into_a_block_another_entry_reads_is_rejected():
+    """pa_decode_append writes each sequence's new row into its block of
+    position L - 1, which must be read by no other table entry of the call.
+    Parallel samples after copy-on-write (private tails over a shared prefix)
+    pass; a table that also reads another sequence's tail block, or its own
+    tail block twice, is rejected, and plain decode over it is not."""
+    w = W.shared_prefix(prompts=2, samples=4, prefix=256, max_tail=100)
+    log(f"[checked build, append into shared blocks, {w.name}]")
+    b = GpuBatch(w, skip_last_append=True)
+    k_new, v_new = b.last_rows()
+    kc0, vc0 = b.kc.clone(), b.vc.clone()
+    out_c = b.decode_append(k_new, v_new)
+    kc1 = b.kc.clone()
+    b.kc.copy_(kc0)
+    b.vc.copy_(vc0)
+    assert torch.equal(out_c, _release(lambda: b.decode_append(k_new, v_new)))
+    assert torch.equal(kc1.view(torch.int16), b.kc.view(torch.int16))
+    b.kc.copy_(kc0)
+    b.vc.copy_(vc0)
+
+    w = W.tiny()  # lengths 37 and 100: 3 and 7 blocks
+    b = GpuBatch(w, skip_last_append=True)
+    k_new, v_new = b.last_rows()
+    kc0, vc0 = torch_to_bytes(b.kc), torch_to_bytes(b.vc)
+    tail0 = int(w.block_tables[0, 2])
+    other = b.tables.clone()
+    other[1, 4] = tail0  # sequence 1 also reads sequence 0's tail block
+    twice = b.tables.clone()
+    twice[1, 0] = int(w.block_tables[1, 6])  # sequence 1 reads its own tail block twice
+    for tables in (other, twice):
+        out = _sentinel_out(b)
+        _rejected(pa.VIOLATION_APPEND_BLOCK_SHARED,
+                  lambda: pa.decode_append(b.q, b.kc, b.vc, k_new, v_new, tables, b.lens, w.scale, out=out,
+                                           max_context_len=w.max_context_len))
+        assert bool((out == 7.0).all())
+        assert np.array_equal(kc0, torch_to_bytes(b.kc)) and np.array_equal(vc0, torch_to_bytes(b.vc))
+        pa.decode(b.q, b.kc, b.vc, tables, b.lens, w.scale, max_context_len=w.max_context_len)  # reads only
+
+
 def test_slot_violations_are_rejected():
     w = W.tiny()
     log(f"[checked build, slots, {w.name}]")

@@ -406,6 +406,35 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, group:
     return np.stack(out) if out else np.zeros((0,) + q.shape[1:])
 
 
+def window_positions(L: int, sink_tokens: int, window_tokens: int) -> np.ndarray:
+    """Positions a query at the end of a sequence of L positions attends to
+    under attention sinks plus a sliding window ("Paged Attention and Memory
+    Efficiency in Production LLM Serving", section "Eviction, compression,
+    and the challenge of fitting more KV cache into less memory": the first
+    few tokens stay as attention sinks next to a window of the most recent
+    ones): t < sink_tokens or t >= L - window_tokens, in order."""
+    t = np.arange(L)
+    return t[(t < sink_tokens) | (t >= L - window_tokens)]
+
+
+def decode_window(q, k_cache, v_cache, block_tables, context_lens, scale: float, group: int, sink_tokens: int,
+                  window_tokens: int, cache_dtype: str, q_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0,
+                  seqs=None) -> np.ndarray:
+    """Decode attention over each sequence's sink and window positions only
+    (window_positions), gathered through the block table like decode():
+    fp64 [B, Hq, D] (or the rows of ``seqs``)."""
+    q = np.asarray(q)
+    seqs = range(q.shape[0]) if seqs is None else seqs
+    out = []
+    for s in seqs:
+        L = int(context_lens[s])
+        keep = window_positions(L, sink_tokens, window_tokens)
+        k = widen(gather_kv(k_cache, block_tables[s], L), cache_dtype, k_scale)[keep]
+        v = widen(gather_kv(v_cache, block_tables[s], L), cache_dtype, v_scale)[keep]
+        out.append(attend(widen(q[s], q_dtype), k, v, scale, group))
+    return np.stack(out) if out else np.zeros((0,) + q.shape[1:])
+
+
 def decode_multi(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float, group: int,
                  cache_dtype: str, q_dtype: str, k_scale: float = 1.0, v_scale: float = 1.0,
                  seqs=None) -> np.ndarray:

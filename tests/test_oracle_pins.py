@@ -827,3 +827,138 @@ def test_fp4_pins_catch_planted_mistakes(mistake):
     bound_ok = np.all(np.abs(back - x) <= half_gap * (1 + 1e-6))
     top_ok = codes[np.argmax(np.abs(x))] & 7 == 7
     assert not (brute_ok and bound_ok and top_ok)
+
+
+# ---------------------------------------------------------------- attention sinks + sliding window
+
+def test_window_positions_closed_forms():
+    """Sink 4 and window 10 over 30 positions keep 0..3 and 20..29; a window
+    (or sink) that covers the sequence keeps everything; window 1 keeps the
+    newest position alone; overlapping ranges count each position once."""
+    assert O.window_positions(30, 4, 10).tolist() == [0, 1, 2, 3] + list(range(20, 30))
+    assert O.window_positions(30, 0, 30).tolist() == list(range(30))
+    assert O.window_positions(30, 31, 1).tolist() == list(range(30))
+    assert O.window_positions(30, 0, 1).tolist() == [29]
+    assert O.window_positions(30, 12, 25).tolist() == list(range(30))
+    for L in range(0, 40):
+        for sink in (0, 1, 4, 17):
+            for window in (1, 3, 16, 33):
+                brute = sorted({t for t in range(L) if t < sink} | {t for t in range(L) if t >= L - window})
+                assert O.window_positions(L, sink, window).tolist() == brute
+
+
+def _window_case(seed, lens, group=2, Hkv=2, D=16, bs=4):
+    """A permuted pool holding each sequence's rows (f16), tables and a query."""
+    rng = np.random.default_rng(seed)
+    nb = int(sum((L + bs - 1) // bs for L in lens)) + 2
+    perm = rng.permutation(nb)
+    M = max((L + bs - 1) // bs for L in lens)
+    tables = np.full((len(lens), M), -1, np.int64)
+    kc = O.new_pool(nb, Hkv, bs, D, "f16")
+    vc = O.new_pool(nb, Hkv, bs, D, "f16")
+    off = 0
+    for s, L in enumerate(lens):
+        n = (L + bs - 1) // bs
+        tables[s, :n] = perm[off:off + n]
+        off += n
+        k = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        v = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        O.reshape_and_cache(k, v, kc, vc, O.slots_for(tables[s], 0, L, bs), bs, "f16")
+    q = rng.standard_normal((len(lens), Hkv * group, D)).astype(np.float16)
+    return kc, vc, tables, np.array(lens), q
+
+
+def test_window_decode_covering_everything_is_decode():
+    kc, vc, tables, lens, q = _window_case(11, [1, 9, 30, 57])
+    full = O.decode(q, kc, vc, tables, lens, 0.25, 2, "f16", "f16")
+    for sink, window in ((0, 57), (57, 1), (3, 1000)):
+        assert np.array_equal(O.decode_window(q, kc, vc, tables, lens, 0.25, 2, sink, window, "f16", "f16"), full)
+
+
+def test_window_of_one_without_sink_is_the_newest_value_row():
+    kc, vc, tables, lens, q = _window_case(12, [1, 9, 30, 57])
+    out = O.decode_window(q, kc, vc, tables, lens, 0.25, 2, 0, 1, "f16", "f16")
+    for s, L in enumerate(lens):
+        v_last = O.widen(O.gather_kv(vc, tables[s], int(L)), "f16")[L - 1]  # [Hkv, D]
+        assert np.array_equal(out[s], np.repeat(v_last, 2, axis=0))
+
+
+def _masked_sdpa(q, k, v, keep, scale, group):
+    """torch float64 scaled_dot_product_attention over the whole sequence with
+    a boolean mask that admits only the kept positions."""
+    L = k.shape[0]
+    mask = torch.zeros((1, L), dtype=torch.bool)
+    mask[0, torch.from_numpy(keep)] = True
+    qt = torch.from_numpy(q)[:, None, :]  # [Hq, 1, D]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)[:, 0].numpy()
+
+
+@pytest.mark.parametrize("sink,window", [(4, 10), (0, 7), (1, 1), (9, 3), (20, 20)])
+def test_window_decode_matches_masked_torch_attention(sink, window):
+    kc, vc, tables, lens, q = _window_case(13, [5, 23, 41, 64])
+    out = O.decode_window(q, kc, vc, tables, lens, 0.25, 2, sink, window, "f16", "f16")
+    for s, L in enumerate(lens):
+        k = O.widen(O.gather_kv(kc, tables[s], int(L)), "f16")
+        v = O.widen(O.gather_kv(vc, tables[s], int(L)), "f16")
+        ref = _masked_sdpa(O.widen(q[s], "f16"), k, v, O.window_positions(int(L), sink, window), 0.25, 2)
+        assert np.max(np.abs(out[s] - ref)) <= 1e-12
+
+
+def test_window_decode_matches_brute_force():
+    kc, vc, tables, lens, q = _window_case(14, [6, 19])
+    out = O.decode_window(q, kc, vc, tables, lens, 0.25, 2, 2, 5, "f16", "f16")
+    for s, L in enumerate(lens):
+        keep = [t for t in range(int(L)) if t < 2 or t >= L - 5]
+        for i in range(q.shape[1]):
+            h = i // 2
+            qi = [float(x) for x in q[s, i]]
+            rows = [(int(tables[s][t // 4]), t % 4) for t in keep]
+            sc = [0.25 * math.fsum(qi[d] * float(kc[b, h, r, d]) for d in range(16)) for b, r in rows]
+            mx = max(sc)
+            e = [math.exp(x - mx) for x in sc]
+            den = math.fsum(e)
+            for d in range(16):
+                want = math.fsum(e[u] * float(vc[b, h, r, d]) for u, (b, r) in enumerate(rows)) / den
+                assert abs(out[s, i, d] - want) <= 1e-13
+
+
+def test_window_decode_after_block_eviction_is_unchanged():
+    """Whole-block eviction of what neither the sink nor the window holds,
+    then the windowed decode over the shortened table, attends to the same
+    rows in the same order as the windowed decode over the full table: the
+    kept blocks keep the first positions, and the last positions stay last."""
+    from oracle.block_manager import BlockManager
+
+    rng = np.random.default_rng(15)
+    bs, Hkv, D, group = 4, 2, 16, 2
+    for L, sink, window in ((30, 4, 10), (57, 3, 9), (64, 0, 5), (13, 5, 20), (40, 9, 1)):
+        bm = BlockManager(40, bs)
+        bm.add(0)
+        slots, _ = bm.append(0, L)
+        kc, vc = O.new_pool(40, Hkv, bs, D, "f16"), O.new_pool(40, Hkv, bs, D, "f16")
+        k = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        v = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        O.reshape_and_cache(k, v, kc, vc, np.array(slots), bs, "f16")
+        q = rng.standard_normal((1, Hkv * group, D)).astype(np.float16)
+        before = O.decode_window(q, kc, vc, np.array([bm.table(0)]), [L], 0.25, group, sink, window, "f16", "f16")
+        bm.evict(0, sink, window)
+        after = O.decode_window(q, kc, vc, np.array([bm.table(0)]), [bm.length(0)], 0.25, group, sink, window,
+                                "f16", "f16")
+        assert np.array_equal(before, after)
+
+
+@pytest.mark.parametrize("mistake", ["window_one_short", "sink_inclusive", "window_after_sink"])
+def test_window_pins_catch_planted_mistakes(mistake, monkeypatch):
+    def bad(L, sink, window):
+        t = np.arange(L)
+        if mistake == "window_one_short":
+            return t[(t < sink) | (t > L - window)]
+        if mistake == "sink_inclusive":
+            return t[(t <= sink) | (t >= L - window)]
+        return t[t < sink + window]  # the window read as the positions right after the sink
+
+    monkeypatch.setattr(O, "window_positions", bad)
+    with pytest.raises(AssertionError):
+        test_window_positions_closed_forms()

@@ -46,7 +46,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, budget_s: float, row_scales: bool = False):
+def cpu_baseline(w, budget_s: float, row_scales: bool = False, window=None):
     """The fp64 oracle over whole sequences of the same batch, until the time budget is spent."""
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -79,6 +79,9 @@ def cpu_baseline(w, budget_s: float, row_scales: bool = False):
             if row_scales:
                 O.decode_scaled(q, kc, vc, ks, vs, w.block_tables, w.context_lens, w.scale, w.group, w.q_dtype,
                                 seqs=[s], cache_dtype=cd)
+            elif window is not None:
+                O.decode_window(q, kc, vc, w.block_tables, w.context_lens, w.scale, w.group, window[0], window[1],
+                                w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale, seqs=[s])
             elif w.query_start is None:
                 O.decode_one(q[s], kc, vc, w.block_tables[s], int(w.context_lens[s]), w.scale, w.group,
                              w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale)
@@ -87,7 +90,9 @@ def cpu_baseline(w, budget_s: float, row_scales: bool = False):
                                w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale, seqs=[s])
             t_total += time.perf_counter() - t0
             done_seqs += 1
-            kv += int(w.context_lens[s]) * w.Hkv * w.D * 2 * {"fp8": 8, "fp4": 4}.get(w.cache_dtype, 16) // 8
+            L = int(w.context_lens[s])
+            n_att = L if window is None else min(L, window[0] + window[1])
+            kv += n_att * w.Hkv * w.D * 2 * {"fp8": 8, "fp4": 4}.get(w.cache_dtype, 16) // 8
             if t_total >= budget_s:
                 break
         passes += 1
@@ -295,6 +300,9 @@ def main():
                          "(fresh seeded values; implies --row-scales)")
     ap.add_argument("--block-size", type=int, default=0, choices=[0, 8, 16, 32],
                     help="heavy_tail: the same lengths and values in blocks of 8, 16 (its default) or 32 positions")
+    ap.add_argument("--window", default="",
+                    help="SINK,WINDOW: attention sinks plus a sliding window (pa_reshape_and_cache + "
+                         "pa_decode_window); the bytes counted are those of the attended positions")
     ap.add_argument("--unfused", action="store_true",
                     help="time the step as two calls, pa_reshape_and_cache then pa_decode")
     ap.add_argument("--no-graph", action="store_true", help="skip timing the step replayed from a HIP graph")
@@ -326,6 +334,13 @@ def main():
     if args.row_scales and w.cache_dtype not in ("fp8", "fp4"):
         raise SystemExit("--row-scales applies to FP8 (and FP4) workloads")
     rs = args.row_scales
+    win = None
+    if args.window:
+        win = tuple(int(x) for x in args.window.split(","))
+        if len(win) != 2 or win[0] < 0 or win[1] < 1:
+            raise SystemExit("--window takes SINK,WINDOW with SINK >= 0 and WINDOW >= 1")
+        if multi or rs:
+            raise SystemExit("--window applies to the decode workloads with a scale per tensor")
     batch = DeviceBatch(w, device=dev, skip_last_append=not multi, row_scales=rs)
     if multi:  # the step re-appends the query tokens' own rows, then attends
         nqs = np.diff(w.query_start).astype(np.int64)
@@ -369,7 +384,11 @@ def main():
             pa.reshape_and_cache(k_new, v_new, batch.kc, batch.vc, slots_new, w.k_scale, w.v_scale)
 
     def decode():
-        if rs:
+        if win:
+            pa.decode_window(batch.q, batch.kc, batch.vc, batch.tables, batch.lens, w.scale, win[0], win[1],
+                             max_context_len=w.max_context_len, k_scale=w.k_scale, v_scale=w.v_scale, out=out,
+                             workspace=ws)
+        elif rs:
             pa.decode_scaled(batch.q, batch.kc, batch.vc, batch.kss, batch.vss, batch.tables, batch.lens, w.scale,
                              max_context_len=w.max_context_len, out=out, workspace=ws)
         else:
@@ -386,7 +405,7 @@ def main():
                         max_context_len=w.max_context_len, k_scale=w.k_scale, v_scale=w.v_scale, out=out,
                         workspace=ws)
 
-    two_calls = args.unfused or multi or rs
+    two_calls = args.unfused or multi or rs or win is not None
     second = decode_multi if multi else decode
 
     def step():
@@ -459,13 +478,17 @@ def main():
             log(f"graph replay: {graph_ms * 1e3:.1f} us per step")
         except RuntimeError as e:  # the eager figures stand without it
             log(f"graph replay not timed: {e}")
-    kv_bytes = w.kv_bytes()
+    # positions each sequence attends to: all, or the sink's and the window's
+    attended = (w.context_lens.astype(np.int64) if win is None else
+                np.minimum(w.context_lens.astype(np.int64), win[0] + win[1]))
+    bits = {"fp8": 8, "fp4": 4}.get(w.cache_dtype, 16)
+    kv_bytes = int(attended.sum()) * w.Hkv * w.D * 2 * bits // 8
     if rs:  # each (position, kv head) row also carries a 4-byte K and V scale
         kv_bytes += int(w.context_lens.astype(np.int64).sum()) * w.Hkv * 4 * 2
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (ms_kern * 1e-3) / 1e9
     # algorithmic flops: 4 * D per (query head, position seen) -- QK and PV
-    seen = (w.context_lens.astype(np.int64) if not multi else
+    seen = (attended if not multi else
             np.array([sum(int(L) - n + j + 1 for j in range(n)) for L, n in zip(w.context_lens, nqs)]))
     flops = 4 * w.D * w.Hq * int(seen.sum())
     tflops = flops / (ms_kern * 1e-3) / 1e12
@@ -483,7 +506,7 @@ def main():
 
     cpu = None
     if args.cpu_budget > 0:
-        cpu = cpu_baseline(w, args.cpu_budget, rs)
+        cpu = cpu_baseline(w, args.cpu_budget, rs, win)
 
     res = {
         "metric": METRIC,
@@ -504,7 +527,10 @@ def main():
             "sum_context_len": int(w.context_lens.sum()), "kv_bytes": kv_bytes, "parallelism": "single-gpu",
             "l2_mall_flush_between_steps": flush is not None, "identity_tables": args.identity_tables,
             "row_scales": rs,
+            **({"sink_tokens": win[0], "window_tokens": win[1], "sum_attended_positions": int(attended.sum())}
+               if win else {}),
             "step": ("pa_reshape_and_cache + pa_decode_multi" if multi else
+                     "pa_reshape_and_cache + pa_decode_window" if win else
                      "pa_reshape_and_cache_scaled + pa_decode_scaled" if rs else
                      "pa_reshape_and_cache + pa_decode" if args.unfused else "pa_decode_append"),
             **({"queries_per_seq": w.max_queries, "total_queries": int(w.query_start[-1])} if multi else {}),
@@ -525,10 +551,12 @@ def main():
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": round(tflops / mfma_peak if mfma_bound else achieved / HBM_PEAK_GBS, 4),
             "traffic": None if args.identity_tables or args.unfused else
-                       recorded_traffic(traffic_key(w.name, rs)),
+                       recorded_traffic(traffic_key(w.name, rs) + (f"+window{win[0]},{win[1]}" if win else "")),
             "kernel": ("attention kernel of pa_decode_multi: MFMA kernel over (query, head) columns (long query "
                        "chunks: workgroups whose waves share K/V chunks through LDS)" if multi else
                        "attention kernel of pa_decode_scaled: MFMA kernel with row scales" if rs else
+                       "attention kernel of pa_decode_window: decode kernel over the sink and window chunks" if win
+                       else
                        "attention kernel of pa_decode: decode kernel (balanced slices)" if args.unfused else
                        "attention kernel of pa_decode_append: decode kernel (balanced slices, append fused for "
                        "16-bit caches)"),

@@ -188,6 +188,33 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     size_t workspace_bytes, pa_stream_t stream);
 
 /*
+ * Attention sinks plus a sliding window, token-exact ("Paged Attention and
+ * Memory Efficiency ...", section "Eviction, compression, and the challenge
+ * of fitting more KV cache into less memory": StreamingLLM keeps the first
+ * few tokens as attention sinks next to a window of recent ones).  pa_decode
+ * where sequence s (L = context_lens[s], clamped as pa_decode clamps it)
+ * attends only to its positions t < sink_tokens and t >= L - window_tokens:
+ *   out[s, i, :] = sum over those t of softmax(score)[t] * V[t, h, :]
+ * The kernel reads only the blocks of the chunks of 32 positions that hold
+ * such positions (the sink's and the window's), so a long sequence costs
+ * about (sink + window) positions of K/V traffic, not L.  Over a table that
+ * pa_bm_evict shortened with the same sink and window (whole blocks gone,
+ * positions renumbered), the result is the same attention: the kept blocks
+ * hold the first positions first and the last positions last.
+ *   sink_tokens >= 0, window_tokens >= 1 (the newest position is always
+ *   seen, so no row is empty for L > 0); L == 0 gives an all-zero row.
+ * Every other argument, the workspace (pa_decode_workspace_size) and the
+ * errors are those of pa_decode; the kernel is the MFMA one.
+ */
+pa_status pa_decode_window(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                           int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int32_t sink_tokens, int32_t window_tokens, float scale, float k_scale, float v_scale,
+                           pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
+                           size_t workspace_bytes, pa_stream_t stream);
+
+/*
  * One decode step in one call: each sequence's new token row is appended
  * and the sequence then attends over all of its positions, the new one
  * included (the cache grows by one row per generated token: "Paged Attention

@@ -79,6 +79,9 @@ def _load(path: str) -> ctypes.CDLL:
     lib.pa_decode.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32, f32, f32,
                               i32, i32, i32, p, sz, p]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_window.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i32, i32, i32, i32, f32, f32,
+                                     f32, i32, i32, i32, p, sz, p]
+    lib.pa_decode_window.restype = ctypes.c_int
     lib.pa_decode_append.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32,
                                      f32, f32, i32, i32, i32, p, sz, p]
     lib.pa_decode_append.restype = ctypes.c_int
@@ -225,6 +228,39 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
     _check(library().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
+        _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
+        _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def decode_window(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, scale: float, sink_tokens: int, window_tokens: int,
+                  max_context_len: Optional[int] = None, k_scale: float = 1.0, v_scale: float = 1.0,
+                  out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode() over each sequence's attention sinks and sliding window only:
+    positions t < sink_tokens and t >= L - window_tokens (window_tokens >= 1)."""
+    _require(q, "q")
+    _require(k_cache, "k_cache")
+    _require(v_cache, "v_cache")
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or Hq % Hkv:
+        raise ValueError("q, k_cache and v_cache shapes do not agree")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, M] and context_lens [B]")
+    M = block_tables.shape[1]
+    mcl = _max_context(max_context_len, M, bs)
+    out = _out(out, (B, Hq, D), out_dtype, q)
+    need = decode_workspace_size(B, Hkv, Hq // Hkv, D, bs, mcl) if B else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_decode_window(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, int(sink_tokens), int(window_tokens), scale, k_scale, v_scale,
         _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
         _ptr(workspace), ws_bytes, _stream(q)))
     return out

@@ -119,7 +119,31 @@ struct DecodeArgs {
   // fp32 each (row-scale kernels only; the per-tensor scales are then 1)
   const float* k_row_scale;
   const float* v_row_scale;
+  // Attention sinks plus a sliding window (window > 0; window kernels
+  // only): a sequence of L positions attends to t < sink and t >= L - window.
+  // Its walk visits the chunks that hold such positions: the sink chunks
+  // [0, ceil(sink / kChunk)), then the chunks from the one holding L - window
+  // on.  Chunk-aligned positions of that walk ("visited" positions) equal
+  // real ones in the sink chunks and are window_shift() below them after.
+  int32_t sink;
+  int32_t window;
 };
+
+// Positions the walk of a windowed sequence skips between its sink chunks
+// and its window chunks (a multiple of kChunk; 0 when they meet, and without
+// a window).
+__host__ __device__ __forceinline__ int window_shift(int L, int sink, int window) {
+  if (window <= 0) return 0;
+  const int sink_chunks = (sink + kChunk - 1) / kChunk;
+  const int lo = L - window;
+  const int win_chunk = lo > 0 ? lo / kChunk : 0;
+  return win_chunk > sink_chunks ? (win_chunk - sink_chunks) * kChunk : 0;
+}
+
+// Positions the walk of a sequence of L positions visits.
+__device__ __forceinline__ int visit_len(const DecodeArgs& a, int L) {
+  return L - window_shift(L, a.sink, a.window);
+}
 
 // Queries of sequence s under MQ (qs = q_start, in memory or in LDS): first
 // row and count, clamped to at most nq, at most the sequence's length and to
@@ -170,7 +194,7 @@ __device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int* 
       L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
       lens[s] = L;
       if (qrow != nullptr) qrow[s] = a.q_start[s];
-      n = L > 0 ? (L + kChunk - 1) / kChunk + a.seg_cost : 0;
+      n = L > 0 ? (visit_len(a, L) + kChunk - 1) / kChunk + a.seg_cost : 0;
     }
     const int inc = wave_inclusive_sum(n);
     if (s < a.B) cum[s + 1] = carry + inc;
@@ -215,35 +239,40 @@ __device__ __forceinline__ bool past_slice(const Slice& sl, int cs, int ce) {
 }
 
 // The piece of one sequence a slice covers (wave-uniform values); s == -1
-// means none.
+// means none.  Positions are those the walk visits (visit_len): they are the
+// real ones, except past the sink chunks of a windowed sequence, where the
+// real position is the visited one plus `shift`.
 struct Segment {
   int s;
   int cs, ce;        // the range of the sequence's chunks on the line (after its charge)
-  int tok0, tok_end; // positions of the piece
+  int tok0, tok_end; // visited positions of the piece
   int nchunks;
+  int shift;         // window_shift of the sequence (0 without a window)
 };
 
 // First sequence at or after s_from that is not empty and has chunks in the slice.
-__device__ __forceinline__ Segment next_segment(const Slice& sl, const int* cum, const int* lens, int B,
-                                                int s_from) {
+__device__ __forceinline__ Segment next_segment(const DecodeArgs& a, const Slice& sl, const int* cum,
+                                                const int* lens, int s_from) {
   Segment g;
   g.s = -1;
-  g.cs = g.ce = g.tok0 = g.tok_end = g.nchunks = 0;
-  for (int s = s_from; s < B; ++s) {
+  g.cs = g.ce = g.tok0 = g.tok_end = g.nchunks = g.shift = 0;
+  for (int s = s_from; s < a.B; ++s) {
     const int L = lens[s];
     const int ce = cum[s + 1];
     if (L == 0) {
       if (past_slice(sl, cum[s], ce)) break;
       continue;
     }
-    const int cs = ce - (L + kChunk - 1) / kChunk;  // the charge lies before cs
+    const int Lv = visit_len(a, L);
+    const int cs = ce - (Lv + kChunk - 1) / kChunk;  // the charge lies before cs
     if (cs >= sl.c1) break;
     g.s = uniform(s);
     g.cs = uniform(cs);
     g.ce = uniform(ce);
     g.tok0 = (max(sl.c0, cs) - cs) * kChunk;
-    g.tok_end = min((min(sl.c1, ce) - cs) * kChunk, L);
+    g.tok_end = min((min(sl.c1, ce) - cs) * kChunk, Lv);
     g.nchunks = (g.tok_end - g.tok0 + kChunk - 1) / kChunk;
+    g.shift = uniform(L - Lv);
     break;
   }
   return g;
@@ -261,28 +290,40 @@ __device__ __forceinline__ bool whole_sequence(const Slice& sl, int cs, int ce) 
 // part re-read a valid entry), and a request is merged two steps after it
 // was issued, so a merge never waits on a table read newer than the chunk
 // loads it is followed by.
-template <int BS>
+//
+// Windowed sequences (WIN): the segment's blocks are those of its visited
+// positions, and block j of the segment is table entry j, or j + gap from
+// block `split` of the segment on (the window chunks after the sink chunks).
+template <int BS, bool WIN = false>
 struct IdRing {
   static constexpr int NB = kChunk / BS;  // blocks per chunk
   static_assert((kIdAhead + 3) * NB <= 64, "ring too small for the lookahead");
   const int32_t* row;  // block table row of the sequence, from the segment's first block
   int nblk;            // blocks in the segment
+  int split, gap;      // WIN: segment blocks from `split` on are `gap` entries further on
   int ids;             // the ring
   int pending0;        // ids of chunk `next`, not merged yet
   int pending1;        // ids of chunk `next + 1`
   int next;
 
+  __device__ __forceinline__ int entry(int j) const {
+    if constexpr (WIN) return row[j + (j >= split ? gap : 0)];
+    return row[j];
+  }
   __device__ __forceinline__ int fetch(int chunk) const {
     const int lane = __lane_id();
     const int slot0 = (chunk * NB) & 63;
     const int j = chunk * NB + ((lane - slot0) & 63);
-    return row[j < nblk ? j : nblk - 1];
+    return entry(j < nblk ? j : nblk - 1);
   }
-  __device__ __forceinline__ void start(const int32_t* table_row, int blocks) {
+  __device__ __forceinline__ void start(const int32_t* table_row, int blocks, int split_block = 0,
+                                        int gap_blocks = 0) {
     row = table_row;
     nblk = blocks;
+    split = split_block;
+    gap = gap_blocks;
     const int lane = __lane_id();
-    ids = row[lane < nblk ? lane : nblk - 1];  // chunks 0 .. 64/NB - 1
+    ids = entry(lane < nblk ? lane : nblk - 1);  // chunks 0 .. 64/NB - 1
     next = kIdAhead + 1;
     pending0 = fetch(next);
     pending1 = fetch(next + 1);

@@ -27,8 +27,10 @@ bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
 // of the group (and, with several queries per sequence, all its queries) are
 // merged at once, and the loads of up to kMergeUnroll pieces are issued
 // before any of them is used.  Sequences that are whole in one slice were
-// written by the decode kernel and are skipped here.  Under MQ a piece whose
-// positions all lie past what a query sees holds m = -inf and is skipped.
+// written by the decode kernel and are skipped here.  A piece that saw no
+// position holds m = -inf and is skipped: under MQ one whose positions all
+// lie past what a query sees, with a window one that lies in the gap between
+// the sink and the window.  Lengths on the chunk line are visited lengths.
 constexpr int kMergeUnroll = 8;
 
 template <int D, bool MQ>
@@ -42,7 +44,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   int L = a.context_lens[s];
   L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
   if (L == 0) return;
-  const int cs = ce - (L + kChunk - 1) / kChunk;  // the sequence's chunks, after its charge
+  const int cs = ce - (visit_len(a, L) + kChunk - 1) / kChunk;  // the sequence's chunks, after its charge
   const int kf = cs / S;
   const int kl = min((ce - 1) / S, neff - 1);
   if (kl <= kf) return;
@@ -69,7 +71,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
-        if (p0 + u < np && (!MQ || ml[u][0] > -INFINITY)) {
+        if (p0 + u < np && ml[u][0] > -INFINITY) {
           const float Mn = fmaxf(M, ml[u][0]);
           const float ca = fast_exp2(M - Mn);
           const float cb = fast_exp2(ml[u][0] - Mn);
@@ -195,7 +197,8 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const bool mq = r.q_start != nullptr;  // several queries per sequence: MFMA kernel only
   const bool rs = r.k_row_scale != nullptr;  // a scale per row: MFMA kernel only
   const int nq = mq ? r.nq : 1;
-  const bool valu = !mq && !rs && decode_uses_valu(decode_variant_override(), r.G);
+  const bool win = r.window > 0;  // sinks plus a window: MFMA kernel only
+  const bool valu = !mq && !rs && !win && decode_uses_valu(decode_variant_override(), r.G);
   if (valu && !valu_supports(r.cache_dtype, r.q_dtype, r.D, r.bs, r.G)) {
     set_error("pa_decode: the VALU kernel is not built for group %d, head_dim %d, block size %d",
               r.G, r.D, r.bs);
@@ -271,6 +274,8 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   a.v_scale = fp8 && !rs ? r.v_scale : 1.f;
   a.k_row_scale = r.k_row_scale;
   a.v_row_scale = r.v_row_scale;
+  a.sink = win ? r.sink : 0;
+  a.window = win ? r.window : 0;
   a.nq = nq;
   a.q_rows = mq ? r.q_rows : r.B;
   const int ct = r.cache_dtype, qt = r.q_dtype;

@@ -130,9 +130,18 @@ struct MfmaWaves {
 // same segments and chunks, so every barrier is reached by all of them; a
 // wave whose tiles hold no query of the sequence loads and waits but does
 // not compute.
-template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW, int NW = 1>
+//
+// WIN (one query per sequence, no row scales): attention sinks plus a
+// sliding window.  The walk visits the sink chunks and the window chunks of
+// each sequence (visit_len), the id ring skips the table entries in between,
+// and a position is masked unless it is below the sink or at or past
+// L - window; since a segment can then see no position at all, p and the
+// rescale are guarded as under MQ.
+template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW, int NW = 1, bool WIN = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MfmaWaves<CT, RS, TW, NW>::value)))
 void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(!WIN || (!MQ && !RS && NW == 1), "windows: one query per sequence, a scale per tensor");
+  constexpr bool kMasked = MQ || WIN;  // a column may see no position of a chunk or a segment
   constexpr int RB = D * CT::bits / 8;  // bytes per cache row
   constexpr int KK = D / 32;   // MFMAs per QK tile
   constexpr int W = D / 16;    // V values per lane per position (one output d-run)
@@ -223,7 +232,7 @@ void decode_mfma_kernel(DecodeArgs a) {
   // is read again), so segment changes cost no table or query round trips.
   struct Header {
     i32x4 qop[TW][KK];
-    IdRing<BS> ring;
+    IdRing<BS, WIN> ring;
     const uint8_t* last_k;  // row of the last position
     const uint8_t* last_v;
     int lim;                // positions from lim on read last_k / last_v
@@ -265,8 +274,18 @@ void decode_mfma_kernel(DecodeArgs a) {
     if constexpr (!kQueryLate) load_query(g, hd);
     const int32_t* trow = a.block_tables + (int64_t)g.s * a.M;
     const int blk0 = g.tok0 / BS;
-    hd.ring.start(trow + blk0, (g.tok_end + BS - 1) / BS - blk0);
-    int id = uniform(trow[(g.tok_end - 1) / BS]);
+    int last_blk = (g.tok_end - 1) / BS;  // visited block of the last position
+    if constexpr (WIN) {
+      // visited blocks from the end of the sink chunks on lie g.shift / BS
+      // table entries further on
+      const int sink_blocks = (a.sink + kChunk - 1) / kChunk * NB;
+      const int gap = g.shift / BS;
+      hd.ring.start(trow + blk0, (g.tok_end + BS - 1) / BS - blk0, sink_blocks - blk0, gap);
+      if (last_blk >= sink_blocks) last_blk += gap;
+    } else {
+      hd.ring.start(trow + blk0, (g.tok_end + BS - 1) / BS - blk0);
+    }
+    int id = uniform(trow[last_blk]);
     const bool id_ok = id >= 0 && (int64_t)id < a.num_blocks;
     if (!id_ok) id = 0;
     const int64_t off = (int64_t)id * blk_stride + (int64_t)((g.tok_end - 1) % BS) * RB;
@@ -278,20 +297,24 @@ void decode_mfma_kernel(DecodeArgs a) {
     hd.tail_off = app && id_ok && ht == 0 ? off : -1;
   };
 
-  Segment cur = next_segment(sl, cum, lens, a.B, sl.s_first);
+  Segment cur = next_segment(a, sl, cum, lens,sl.s_first);
   if (cur.s < 0) return;
   Header hc, hn;
   load_header(cur, hc);
   if constexpr (kQueryLate) load_query(cur, hc);
-  Segment nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
+  Segment nxt = next_segment(a, sl, cum, lens,cur.s + 1);
   load_header(nxt.s >= 0 ? nxt : cur, hn);
 
   while (true) {
     const int s = cur.s;
     const int cs = cur.cs, ce = cur.ce;
     const int tok0 = cur.tok0, tok_end = cur.tok_end, nchunks = cur.nchunks;
-    IdRing<BS>& ring = hc.ring;
+    IdRing<BS, WIN>& ring = hc.ring;
     const int lim = hc.lim;
+    // WIN: a visited position p is seen if p < sink or p + shift >= L - window
+    // (in the sink chunks p + shift stays below L - window whenever shift > 0)
+    const int win_shift = WIN ? cur.shift : 0;
+    const int win_lo = WIN ? lens[s] - a.window : 0;
     bool live[TW];
     int qlim[TW];  // last position each column's query sees (MQ)
 #pragma unroll
@@ -411,7 +434,8 @@ void decode_mfma_kernel(DecodeArgs a) {
           float raw_s = (j < 4 ? s0[t][j & 3] : s1[t][j & 3]) * a.qk_scale_log2;
           if constexpr (RS) raw_s *= scl.k[j >> 2][j & 3];
           const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
-          const bool seen = ctok + tc < tok_end && (!MQ || ctok + tc <= qlim[t]);
+          const bool seen = ctok + tc < tok_end && (!MQ || ctok + tc <= qlim[t]) &&
+                            (!WIN || ctok + tc < a.sink || ctok + tc + win_shift >= win_lo);
           sc[j] = seen ? raw_s : -INFINITY;
           mx = fmaxf(mx, sc[j]);
         }
@@ -419,8 +443,8 @@ void decode_mfma_kernel(DecodeArgs a) {
           mx = fmaxf(mx, shfl_xor(mx, 16));
           mx = fmaxf(mx, shfl_xor(mx, 32));
           const float mn = fmaxf(m[t], mx);
-          // under MQ a column may have seen no position yet (mn = -inf)
-          const float alpha = (MQ && mn == -INFINITY) ? 1.f : fast_exp2(m[t] - mn);
+          // under MQ or a window a column may have seen no position yet (mn = -inf)
+          const float alpha = (kMasked && mn == -INFINITY) ? 1.f : fast_exp2(m[t] - mn);
 #pragma unroll
           for (int i = 0; i < W; ++i) acc[t][i] *= alpha;
           l[t] *= alpha;
@@ -429,7 +453,7 @@ void decode_mfma_kernel(DecodeArgs a) {
         float p[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          p[j] = (MQ && sc[j] == -INFINITY) ? 0.f : fast_exp2(sc[j] - m[t]);
+          p[j] = (kMasked && sc[j] == -INFINITY) ? 0.f : fast_exp2(sc[j] - m[t]);
           l[t] += p[j];
         }
         // ---- P as the B operand of PV (weighted by the V rows' scales under
@@ -632,7 +656,7 @@ void decode_mfma_kernel(DecodeArgs a) {
     cur = nxt;
     hc = hn;
     if constexpr (kQueryLate) load_query(cur, hc);
-    nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
+    nxt = next_segment(a, sl, cum, lens,cur.s + 1);
     load_header(nxt.s >= 0 ? nxt : cur, hn);
   }
 }
@@ -641,7 +665,10 @@ template <class CT, class QT, int D, int BS>
 void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, int waves_per_group, dim3 grid,
                  hipStream_t stream, const LaunchEvents& ev) {
   if (!multi_query) {
-    launch_with_events(decode_mfma_kernel<CT, QT, D, BS, false, false, 1>, grid, dim3(64), stream, ev, a);
+    if (a.window > 0)
+      launch_with_events(decode_mfma_kernel<CT, QT, D, BS, false, false, 1, 1, true>, grid, dim3(64), stream, ev, a);
+    else
+      launch_with_events(decode_mfma_kernel<CT, QT, D, BS, false, false, 1>, grid, dim3(64), stream, ev, a);
     return;
   }
   if constexpr (CT::bits == 16) {
@@ -686,8 +713,9 @@ void launch_mfma(const DecodeArgs& a, bool multi_query, int tiles_per_wave, int 
 
 // Whether launch_decode_mfma has a kernel for these types and sizes (the
 // instantiations below): 16-bit caches read with a query of their own dtype,
-// FP8 caches with either query dtype, FP8 and FP4 caches with row scales
-// (one query per sequence); head_dim 64 or 128; block size 8, 16 or 32.
+// FP8 caches with either query dtype (one query per sequence also with sinks
+// plus a window), FP8 and FP4 caches with row scales (one query per
+// sequence); head_dim 64 or 128; block size 8, 16 or 32.
 bool mfma_kernel_built(int ct, int qt, int head_dim, int bs, bool multi_query, bool row_scales) {
   if ((head_dim != 64 && head_dim != 128) || (bs != 8 && bs != 16 && bs != 32)) return false;
   if (qt != F16::code && qt != BF16::code) return false;

@@ -153,11 +153,11 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     hd.tail_off = app && id_ok ? off : -1;
   };
 
-  Segment cur = next_segment(sl, cum, lens, a.B, sl.s_first);
+  Segment cur = next_segment(a, sl, cum, lens,sl.s_first);
   if (cur.s < 0) return;
   Header hc, hn;
   load_header(cur, hc);
-  Segment nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
+  Segment nxt = next_segment(a, sl, cum, lens,cur.s + 1);
   load_header(nxt.s >= 0 ? nxt : cur, hn);
 
   while (true) {
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(DecodeArgs a) {
     if (nxt.s < 0) break;
     cur = nxt;
     hc = hn;
-    nxt = next_segment(sl, cum, lens, a.B, cur.s + 1);
+    nxt = next_segment(a, sl, cum, lens,cur.s + 1);
     load_header(nxt.s >= 0 ? nxt : cur, hn);
   }
 }

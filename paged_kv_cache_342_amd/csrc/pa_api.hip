@@ -227,6 +227,32 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
 
+pa_status pa_decode_window(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                           int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int32_t sink_tokens, int32_t window_tokens, float scale, float k_scale, float v_scale,
+                           pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
+                           size_t workspace_bytes, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_decode_window";
+  if (sink_tokens < 0) return fail(PA_ERR_INVALID_ARG, "%s: sink_tokens must be >= 0 (got %d)", fn, sink_tokens);
+  if (window_tokens < 1)
+    return fail(PA_ERR_INVALID_ARG, "%s: window_tokens must be >= 1 (got %d)", fn, window_tokens);
+  DecodeRequest r;
+  const pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads,
+                                      gqa_group, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                                      max_context_len, scale, k_scale, v_scale, q_dtype, cache_dtype, out_dtype,
+                                      workspace, workspace_bytes, 1, false, false, r);
+  if (st != PA_OK || B == 0) return st;
+  // lengths are at most 2^30 (max_blocks_per_seq * block_size), so larger
+  // counts mean the same and are clamped to keep the index math in range
+  r.sink = sink_tokens > (1 << 30) ? (1 << 30) : sink_tokens;
+  r.window = window_tokens > (1 << 30) ? (1 << 30) : window_tokens;
+  PA_CONTRACT(check_decode_contract(fn, r, reinterpret_cast<hipStream_t>(stream)));
+  return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
+}
+
 pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, const void* key,
                            const void* value, pa_dtype src_dtype, const int32_t* block_tables,
                            const int32_t* context_lens, int32_t B, int32_t num_kv_heads, int32_t gqa_group,

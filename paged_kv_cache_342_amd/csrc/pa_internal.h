@@ -82,6 +82,10 @@ struct DecodeRequest {
   // fp32 each); null = one scale per tensor
   const float* k_row_scale;
   const float* v_row_scale;
+  // attention sinks plus a sliding window (pa_decode_window): each sequence
+  // attends to t < sink and t >= L - window; window == 0 = every position
+  int sink;
+  int window;
 };
 
 // 0 = default choice, 1 = VALU/DPP kernel, 2 = MFMA kernel

@@ -1,0 +1,123 @@
+"""pa_decode_window (attention sinks plus a sliding window, token-exact)
+against the oracle's decode_window over the same pools.
+
+Cases: lengths on both sides of chunk and block boundaries with sinks and
+windows that meet, overlap, cover everything or leave a long gap; every
+cache dtype, head_dim, block size and several group sizes; the full-size
+8B-, 70B-shaped and heavy-tailed batches on sampled sequences; a window that
+covers every sequence, which must equal pa_decode bit for bit (the walk is
+then the decode walk); and tables shortened by whole-block eviction of the
+same sink and window, which must give the same attention."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_342_amd as pa
+import workloads as W
+from oracle import harness as OH
+from oracle import pa_oracle as O
+from tests.gpu_util import GpuBatch, errors, log, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, sink, window, batch=None, seqs=None, tables=None, lens=None, label=""):
+    """GPU decode_window (over `tables` / `lens` when given, else the
+    workload's) against the oracle's decode_window over the workload's own
+    tables and lengths."""
+    b = batch or GpuBatch(w)
+    t = b.tables if tables is None else tables
+    n = b.lens if lens is None else lens
+    out = pa.decode_window(b.q, b.kc, b.vc, t, n, w.scale, sink, window, max_context_len=w.max_context_len,
+                           k_scale=w.k_scale, v_scale=w.v_scale, out_dtype=torch.float32)
+    got = out.cpu().numpy().astype(np.float64)
+    kc, vc = OH.build_pools(w, seqs=seqs)
+    ref = O.decode_window(w.query(), kc, vc, w.block_tables, w.context_lens, w.scale, w.group, sink, window,
+                          w.cache_dtype, w.q_dtype, w.k_scale, w.v_scale, seqs=seqs)
+    got = got if seqs is None else got[list(seqs)]
+    ma, rel = errors(got, ref)
+    tol_abs, tol_rel = tolerance(w.cache_dtype)
+    log(f"[window {w.name}{label} sink={sink} window={window}] max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert np.isfinite(got).all()
+    assert ma <= tol_abs
+    if tol_rel is not None:
+        assert rel <= tol_rel
+    return b
+
+
+LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 127, 129, 255, 257, 511, 777, 1031]
+WINDOWS = [(0, 1), (4, 16), (4, 100), (31, 33), (32, 64), (1, 2000), (100, 1), (64, 32)]
+
+
+@pytest.mark.parametrize("cache,q", [("f16", "f16"), ("bf16", "bf16"), ("fp8", "bf16"), ("fp8", "f16")])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_window_sweep(cache, q, D, bs):
+    for g in (1, 4, 8):
+        w = W.custom(f"win_{cache}_{q}_D{D}_bs{bs}_g{g}", 400 + g, LENS, 2 * g, 2, D, bs, cache, q)
+        b = GpuBatch(w)
+        for sink, window in WINDOWS:
+            _check(w, sink, window, batch=b)
+
+
+@pytest.mark.parametrize("make,sink,window", [
+    (lambda: W.llama8b(), 4, 512),
+    (lambda: W.llama70b(), 4, 1024),
+    (lambda: W.llama70b(), 64, 2000),
+    (lambda: W.heavy_tail(bs=16), 8, 256),
+    (lambda: W.heavy_tail(bs=8), 0, 100),
+], ids=["llama8b_4_512", "llama70b_4_1024", "llama70b_64_2000", "heavy_tail_8_256", "heavy_tail_bs8_0_100"])
+def test_window_full_size_sampled(make, sink, window):
+    w = make()
+    order = np.argsort(w.context_lens)
+    seqs = sorted({int(order[-1]), int(order[-2]), int(order[0]), int(order[len(order) // 2])})
+    _check(w, sink, window, seqs=seqs, label="[full, sampled]")
+
+
+@pytest.mark.parametrize("make", [lambda: W.llama8b(B=8), lambda: W.heavy_tail(bs=8, B=40), lambda: W.tiny()],
+                         ids=["bf16", "fp8", "f16"])
+def test_covering_window_is_decode_bit_for_bit(make):
+    w = make()
+    b = GpuBatch(w)
+    base = b.decode()
+    for sink, window in ((0, 1 << 20), (1 << 20, 1)):
+        got = pa.decode_window(b.q, b.kc, b.vc, b.tables, b.lens, w.scale, sink, window,
+                               max_context_len=w.max_context_len, k_scale=w.k_scale, v_scale=w.v_scale,
+                               out_dtype=torch.float32)
+        assert torch.equal(got.view(torch.int32), base.view(torch.int32))
+
+
+def _evicted(w, sink, window):
+    """Tables and lengths after whole-block eviction of what neither the sink
+    nor the window holds (the newest block always stays), as pa_bm_evict does."""
+    bs = w.bs
+    tables = np.full_like(w.block_tables, -1)
+    lens = np.zeros_like(w.context_lens)
+    for s in range(w.B):
+        L = int(w.context_lens[s])
+        nblk = (L + bs - 1) // bs
+        keep = [j for j in range(nblk)
+                if j * bs < sink or min(L, (j + 1) * bs) - 1 >= L - window or j == nblk - 1]
+        tables[s, :len(keep)] = w.block_tables[s, keep]
+        lens[s] = L - (nblk - len(keep)) * bs
+    return tables, lens
+
+
+@pytest.mark.parametrize("sink,window", [(4, 100), (16, 48), (0, 1), (7, 300)])
+def test_window_over_block_evicted_tables(sink, window):
+    """The StreamingLLM flow: evict whole blocks, then attend token-exactly
+    over the shortened tables; the oracle attends over the full tables."""
+    w = W.custom("win_evicted", 431, [1, 40, 129, 500, 1031, 2048, 3000], 32, 8, 128, 16, "bf16")
+    b = GpuBatch(w)
+    tables, lens = _evicted(w, sink, window)
+    _check(w, sink, window, batch=b, tables=torch.from_numpy(tables).cuda(), lens=torch.from_numpy(lens).cuda(),
+           label="[evicted tables]")
+
+
+def test_window_rejects_bad_counts():
+    w = W.tiny()
+    b = GpuBatch(w)
+    for sink, window in ((-1, 10), (0, 0), (3, -2)):
+        with pytest.raises(pa.PagedAttentionError) as e:
+            pa.decode_window(b.q, b.kc, b.vc, b.tables, b.lens, w.scale, sink, window)
+        assert e.value.status == pa.ERR_INVALID_ARG

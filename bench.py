@@ -37,7 +37,8 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "fp8": 2500.0, "fp4": 2500.0}
 CSRC = os.path.join(ROOT, "paged_kv_cache_342_amd", "csrc")
 # sources of the kernels a pa_decode call runs; profiler traffic recorded for
 # other sources is stale and is not reported
-DECODE_SOURCES = ("pa_device.h", "decode_common.h", "decode_core.hip", "decode_mfma.hip", "decode_valu.hip",
+DECODE_SOURCES = ("pa_device.h", "decode_common.h", "decode_core.hip", "decode_mfma_kernel.h", "decode_mfma.hip",
+                  "decode_cascade.hip", "decode_valu.hip",
                   "cache_ops.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
@@ -300,6 +301,9 @@ def main():
                          "(fresh seeded values; implies --row-scales)")
     ap.add_argument("--block-size", type=int, default=0, choices=[0, 8, 16, 32],
                     help="heavy_tail: the same lengths and values in blocks of 8, 16 (its default) or 32 positions")
+    ap.add_argument("--cascade", action="store_true",
+                    help="shared_prefix: pa_reshape_and_cache + pa_decode_shared_prefix, each prompt's shared prefix "
+                         "read once for its samples (the roofline counts those unique bytes)")
     ap.add_argument("--window", default="",
                     help="SINK,WINDOW: attention sinks plus a sliding window (pa_reshape_and_cache + "
                          "pa_decode_window); the bytes counted are those of the attended positions")
@@ -335,6 +339,9 @@ def main():
         raise SystemExit("--row-scales applies to FP8 (and FP4) workloads")
     rs = args.row_scales
     win = None
+    if args.cascade and w.name != "shared_prefix":
+        raise SystemExit("--cascade applies to the shared_prefix workload")
+    cascade = args.cascade
     if args.window:
         win = tuple(int(x) for x in args.window.split(","))
         if len(win) != 2 or win[0] < 0 or win[1] < 1:
@@ -383,8 +390,18 @@ def main():
         else:
             pa.reshape_and_cache(k_new, v_new, batch.kc, batch.vc, slots_new, w.k_scale, w.v_scale)
 
+    if cascade:
+        samples, plen = w.meta["samples"], w.meta["shared_len"].astype(np.int64)
+        group_start = torch.tensor(np.arange(len(plen) + 1) * samples, dtype=torch.int32, device=dev)
+        prefix_lens = torch.tensor(plen, dtype=torch.int32, device=dev)
+        cws = torch.empty(pa.decode_shared_prefix_workspace_size(w.B, len(plen), samples, w.Hkv, w.group, w.D, w.bs,
+                                                                  w.max_context_len), dtype=torch.uint8, device=dev)
+
     def decode():
-        if win:
+        if cascade:
+            pa.decode_shared_prefix(batch.q, batch.kc, batch.vc, batch.tables, batch.lens, group_start, prefix_lens,
+                                    samples, w.scale, max_context_len=w.max_context_len, out=out, workspace=cws)
+        elif win:
             pa.decode_window(batch.q, batch.kc, batch.vc, batch.tables, batch.lens, w.scale, win[0], win[1],
                              max_context_len=w.max_context_len, k_scale=w.k_scale, v_scale=w.v_scale, out=out,
                              workspace=ws)
@@ -405,7 +422,7 @@ def main():
                         max_context_len=w.max_context_len, k_scale=w.k_scale, v_scale=w.v_scale, out=out,
                         workspace=ws)
 
-    two_calls = args.unfused or multi or rs or win is not None
+    two_calls = args.unfused or multi or rs or win is not None or cascade
     second = decode_multi if multi else decode
 
     def step():
@@ -485,8 +502,14 @@ def main():
     kv_bytes = int(attended.sum()) * w.Hkv * w.D * 2 * bits // 8
     if rs:  # each (position, kv head) row also carries a 4-byte K and V scale
         kv_bytes += int(w.context_lens.astype(np.int64).sum()) * w.Hkv * 4 * 2
+    # the cascade reads each prompt's prefix once per KV head: those are the
+    # bytes its kernels must move (the metric's value keeps every sequence's own)
+    kern_bytes = kv_bytes
+    if cascade:
+        shared = int((plen * (samples - 1)).sum())
+        kern_bytes = (int(attended.sum()) - shared) * w.Hkv * w.D * 2 * bits // 8
     value = kv_bytes / (ms_step * 1e-3) / 1e9
-    achieved = kv_bytes / (ms_kern * 1e-3) / 1e9
+    achieved = kern_bytes / (ms_kern * 1e-3) / 1e9
     # algorithmic flops: 4 * D per (query head, position seen) -- QK and PV
     seen = (attended if not multi else
             np.array([sum(int(L) - n + j + 1 for j in range(n)) for L, n in zip(w.context_lens, nqs)]))
@@ -525,12 +548,14 @@ def main():
             "workload": w.name, "decode_kernel": os.environ.get("PA_DECODE_VARIANT", "default"), "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
             "block_size": w.bs, "cache_dtype": w.cache_dtype, "q_dtype": w.q_dtype, "seed": w.seed,
             "sum_context_len": int(w.context_lens.sum()), "kv_bytes": kv_bytes, "parallelism": "single-gpu",
+            **({"kernel_bytes_unique": kern_bytes} if cascade else {}),
             "l2_mall_flush_between_steps": flush is not None, "identity_tables": args.identity_tables,
             "row_scales": rs,
             **({"sink_tokens": win[0], "window_tokens": win[1], "sum_attended_positions": int(attended.sum())}
                if win else {}),
             "step": ("pa_reshape_and_cache + pa_decode_multi" if multi else
                      "pa_reshape_and_cache + pa_decode_window" if win else
+                     "pa_reshape_and_cache + pa_decode_shared_prefix" if cascade else
                      "pa_reshape_and_cache_scaled + pa_decode_scaled" if rs else
                      "pa_reshape_and_cache + pa_decode" if args.unfused else "pa_decode_append"),
             **({"queries_per_seq": w.max_queries, "total_queries": int(w.query_start[-1])} if multi else {}),
@@ -551,10 +576,14 @@ def main():
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": round(tflops / mfma_peak if mfma_bound else achieved / HBM_PEAK_GBS, 4),
             "traffic": None if args.identity_tables or args.unfused else
-                       recorded_traffic(traffic_key(w.name, rs) + (f"+window{win[0]},{win[1]}" if win else "")),
+                       recorded_traffic(traffic_key(w.name, rs) + (f"+window{win[0]},{win[1]}" if win else "")
+                                        + ("+cascade" if cascade else "")),
             "kernel": ("attention kernel of pa_decode_multi: MFMA kernel over (query, head) columns (long query "
                        "chunks: workgroups whose waves share K/V chunks through LDS)" if multi else
                        "attention kernel of pa_decode_scaled: MFMA kernel with row scales" if rs else
+                       "attention kernels of pa_decode_shared_prefix, from the start of the prefix pass to the end "
+                       "of the suffix pass (the prefix state merge between them included); achieved counts each "
+                       "prompt's prefix once" if cascade else
                        "attention kernel of pa_decode_window: decode kernel over the sink and window chunks" if win
                        else
                        "attention kernel of pa_decode: decode kernel (balanced slices)" if args.unfused else

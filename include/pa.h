@@ -113,6 +113,8 @@ typedef enum {
 #define PA_VIOLATION_QUERY_START 0x80u       /* query_start not as pa_decode_multi requires */
 #define PA_VIOLATION_APPEND_BLOCK_SHARED 0x100u /* pa_decode_append: a sequence's block of position L - 1
                                                    is also read by another table entry of the call */
+#define PA_VIOLATION_PREFIX_GROUP 0x200u        /* pa_decode_shared_prefix: group_start or prefix_lens
+                                                   not as the call requires */
 
 /* 1 in libpa_checked.so, 0 in libpa.so. */
 int32_t pa_is_checked_build(void);
@@ -186,6 +188,46 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     float scale, float k_scale, float v_scale, pa_dtype q_dtype,
                     pa_dtype cache_dtype, pa_dtype out_dtype, void* workspace,
                     size_t workspace_bytes, pa_stream_t stream);
+
+/*
+ * Decode over shared prefixes, each read once per group ("Paged Attention
+ * and Memory Efficiency ...", section "How PagedAttention borrows OS paging
+ * ...": requests that share a prefix point at the same physical blocks;
+ * "PagedAttention - The KV Cache Problem", section "Why This Matters for
+ * Production": parallel sampling and beam search).  The result is pa_decode's
+ * for the same arguments; only the reading differs.  Group p is sequences
+ * group_start[p] .. group_start[p + 1] - 1, which share their first
+ * prefix_lens[p] positions: each member's K/V rows at those positions equal
+ * the group's first member's (the same blocks, or copy-on-write copies of
+ * them).  The call attends the members' queries over that prefix together,
+ * reading it once per group through the first member's block table, then
+ * attends each sequence over its own positions from prefix_lens[p] on and
+ * combines the two, exactly as softmax over all positions.
+ *   group_start    [num_groups + 1] int32, device: non-decreasing from 0 to B
+ *   prefix_lens    [num_groups] int32, device: 0 <= prefix_lens[p] <=
+ *                  L_s - 1 for every member s (the newest position is its own)
+ *   num_groups     1 .. B; max_group_size: host bound of members per group,
+ *                  1 .. 1024; B <= 3072 (one launch per pass)
+ *   workspace      at least pa_decode_shared_prefix_workspace_size(B,
+ *                  num_groups, max_group_size, num_kv_heads, gqa_group,
+ *                  head_dim, block_size, max_context_len) bytes (with
+ *                  max_context_len <= 0 read as max_blocks_per_seq * block_size)
+ * Caches: 16-bit with a query of the same dtype, or FP8 with a scale per
+ * tensor.  group_start and prefix_lens outside these rules are part of the
+ * device-side contract (PA_VIOLATION_PREFIX_GROUP in the checked build).
+ * Every other argument and error is pa_decode's.
+ */
+size_t pa_decode_shared_prefix_workspace_size(int32_t B, int32_t num_groups, int32_t max_group_size,
+                                              int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                                              int32_t block_size, int32_t max_context_len);
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens, int32_t B,
+                                  int32_t num_groups, int32_t max_group_size, int32_t num_kv_heads,
+                                  int32_t gqa_group, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, float scale, float k_scale,
+                                  float v_scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                                  void* workspace, size_t workspace_bytes, pa_stream_t stream);
 
 /*
  * Attention sinks plus a sliding window, token-exact ("Paged Attention and

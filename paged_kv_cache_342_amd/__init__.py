@@ -26,7 +26,7 @@ F32, F16, BF16, FP8_E4M3, FP4_E2M1 = 0, 1, 2, 3, 4
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NO_BLOCKS, ERR_CONTRACT = 0, -1, -2, -3, -4, -5, -6
 VIOLATION_BLOCK_ID, VIOLATION_CONTEXT_LEN, VIOLATION_SLOT, VIOLATION_SLOT_REPEATED = 0x01, 0x02, 0x04, 0x08
 VIOLATION_COPY_ID, VIOLATION_COPY_DST_REPEATED, VIOLATION_COPY_DST_IS_SRC, VIOLATION_QUERY_START = 0x10, 0x20, 0x40, 0x80
-VIOLATION_APPEND_BLOCK_SHARED = 0x100
+VIOLATION_APPEND_BLOCK_SHARED, VIOLATION_PREFIX_GROUP = 0x100, 0x200
 
 # an FP4 cache holds two E2M1 codes per byte: torch.float4_e2m1fn_x2, last dim head_dim / 2
 _TORCH_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3,
@@ -82,6 +82,11 @@ def _load(path: str) -> ctypes.CDLL:
     lib.pa_decode_window.argtypes = [p, p, p, p, p, p, i32, i32, i32, i32, i32, i64, i32, i32, i32, i32, f32, f32,
                                      f32, i32, i32, i32, p, sz, p]
     lib.pa_decode_window.restype = ctypes.c_int
+    lib.pa_decode_shared_prefix_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.pa_decode_shared_prefix_workspace_size.restype = sz
+    lib.pa_decode_shared_prefix.argtypes = [p, p, p, p, p, p, p, p, i32, i32, i32, i32, i32, i32, i32, i64, i32, i32,
+                                            f32, f32, f32, i32, i32, i32, p, sz, p]
+    lib.pa_decode_shared_prefix.restype = ctypes.c_int
     lib.pa_decode_append.argtypes = [p, p, p, p, p, p, i32, p, p, i32, i32, i32, i32, i32, i64, i32, i32, f32,
                                      f32, f32, i32, i32, i32, p, sz, p]
     lib.pa_decode_append.restype = ctypes.c_int
@@ -228,6 +233,53 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_
     _check(library().pa_decode(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
         B, Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
+        _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
+        _ptr(workspace), ws_bytes, _stream(q)))
+    return out
+
+
+def decode_shared_prefix_workspace_size(B: int, num_groups: int, max_group_size: int, num_kv_heads: int, group: int,
+                                        head_dim: int, block_size: int, max_context_len: int) -> int:
+    return int(library().pa_decode_shared_prefix_workspace_size(B, num_groups, max_group_size, num_kv_heads, group,
+                                                                head_dim, block_size, max_context_len))
+
+
+def decode_shared_prefix(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                         context_lens: torch.Tensor, group_start: torch.Tensor, prefix_lens: torch.Tensor,
+                         max_group_size: int, scale: float, max_context_len: Optional[int] = None,
+                         k_scale: float = 1.0, v_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+                         out_dtype: Optional[torch.dtype] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """decode() over sequences grouped by a shared prefix: group p is sequences
+    group_start[p] .. group_start[p+1]-1 (int32 [P+1] on the device), which share
+    their first prefix_lens[p] positions (int32 [P]); each prefix is read once
+    per group.  max_group_size: host bound of members per group."""
+    _require(q, "q")
+    _require(k_cache, "k_cache")
+    _require(v_cache, "v_cache")
+    _require(block_tables, "block_tables", torch.int32)
+    _require(context_lens, "context_lens", torch.int32)
+    _require(group_start, "group_start", torch.int32)
+    _require(prefix_lens, "prefix_lens", torch.int32)
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or Hq % Hkv:
+        raise ValueError("q, k_cache and v_cache shapes do not agree")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, M] and context_lens [B]")
+    P = prefix_lens.shape[0] if prefix_lens.dim() == 1 else -1
+    if P < 1 or group_start.shape != (P + 1,):
+        raise ValueError("prefix_lens must be [P] and group_start [P + 1]")
+    M = block_tables.shape[1]
+    mcl = _max_context(max_context_len, M, bs)
+    out = _out(out, (B, Hq, D), out_dtype, q)
+    need = decode_shared_prefix_workspace_size(B, P, max_group_size, Hkv, Hq // Hkv, D, bs, mcl) if B else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().pa_decode_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens), _ptr(group_start),
+        _ptr(prefix_lens), B, P, int(max_group_size), Hkv, Hq // Hkv, D, bs, nb, M, mcl, scale, k_scale, v_scale,
         _TORCH_CODE.get(q.dtype, -9), _TORCH_CODE.get(k_cache.dtype, -9), _TORCH_CODE.get(out.dtype, -9),
         _ptr(workspace), ws_bytes, _stream(q)))
     return out

@@ -101,6 +101,25 @@ __global__ __launch_bounds__(64) void check_append_kernel(const int32_t* tables,
   if (shared) flag(word, PA_VIOLATION_APPEND_BLOCK_SHARED);
 }
 
+// pa_decode_shared_prefix: group_start rises from 0 to B, each group has at
+// most max_group members, and its prefix length is at least 0 and below the
+// (clamped) length of each member.  One thread per group.
+__global__ __launch_bounds__(kTile) void check_groups_kernel(const int32_t* group_start, const int32_t* prefix_lens,
+                                                             const int32_t* lens, int P, int B, int max_group,
+                                                             int max_ctx, uint32_t* word) {
+  const int p = blockIdx.x * kTile + threadIdx.x;
+  if (p >= P) return;
+  const int a = group_start[p], b = group_start[p + 1], pl = prefix_lens[p];
+  bool bad = b < a || b - a > max_group || a < 0 || b > B || pl < 0;
+  if ((p == 0 && a != 0) || (p == P - 1 && b != B)) bad = true;
+  for (int s = a < 0 ? 0 : a; !bad && s < (b > B ? B : b); ++s) {
+    const int L = lens[s];
+    const int Lc = L < 0 ? 0 : (L > max_ctx ? max_ctx : L);
+    if (pl > Lc - 1) bad = true;
+  }
+  if (bad) flag(word, PA_VIOLATION_PREFIX_GROUP);
+}
+
 // Slots: each non-negative slot lies below num_slots and appears once.  Thread
 // i compares its slot with every later one, a tile of 256 at a time from LDS.
 __global__ __launch_bounds__(kTile) void check_slots_kernel(const int64_t* slots, int T, int64_t num_slots,
@@ -166,6 +185,7 @@ static void describe(uint32_t bits, char* buf, size_t n) {
       {PA_VIOLATION_COPY_DST_IS_SRC, "a copy destination that is another pair's source"},
       {PA_VIOLATION_QUERY_START, "a query range outside the contract"},
       {PA_VIOLATION_APPEND_BLOCK_SHARED, "a block receiving a new row that another table entry of the call reads"},
+      {PA_VIOLATION_PREFIX_GROUP, "a prefix group or prefix length outside the contract"},
   };
   size_t used = 0;
   buf[0] = 0;
@@ -219,6 +239,9 @@ pa_status check_decode_contract(const char* fn, const DecodeRequest& r, hipStrea
   if (r.new_k != nullptr)
     hipLaunchKernelGGL(check_append_kernel, dim3((unsigned)r.B), dim3(64), 0, stream, r.block_tables, r.context_lens,
                        r.B, r.M, r.bs, r.max_ctx, word);
+  if (r.group_start != nullptr)
+    hipLaunchKernelGGL(check_groups_kernel, dim3((unsigned)((r.n_groups + kTile - 1) / kTile)), dim3(kTile), 0, stream,
+                       r.group_start, r.prefix_lens, r.context_lens, r.n_groups, r.B, r.nq, r.max_ctx, word);
   const pa_status st = launched(fn);
   return st != PA_OK ? st : collect(fn, word, stream);
 }

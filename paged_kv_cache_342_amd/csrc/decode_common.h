@@ -127,30 +127,53 @@ struct DecodeArgs {
   // real ones in the sink chunks and are window_shift() below them after.
   int32_t sink;
   int32_t window;
+  // Shared prefixes (pa_decode_shared_prefix): group p is sequences
+  // group_start[p] .. group_start[p + 1] - 1, which share their first
+  // prefix_lens[p] positions.  The prefix pass is a several-queries launch
+  // over the groups (q_start = group_start, context_lens = prefix_lens, every
+  // member sees the whole prefix, the table row of the group's first member);
+  // it leaves each member's unnormalised state (m, l, acc) in state_ml /
+  // state_acc ([B, Hq, 2] and [B, Hq, D], by sequence).  The suffix pass is a
+  // decode launch whose sequences attend from their group's prefix_lens on
+  // (a window with no sink and a first position of its own) and start from
+  // that state.
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int32_t n_groups;
+  float* state_ml;
+  float* state_acc;
 };
 
-// Positions the walk of a windowed sequence skips between its sink chunks
-// and its window chunks (a multiple of kChunk; 0 when they meet, and without
-// a window).
-__host__ __device__ __forceinline__ int window_shift(int L, int sink, int window) {
-  if (window <= 0) return 0;
+// Positions the walk of a sequence skips between its first chunks (those
+// holding positions below `sink`) and the chunks from the one holding `lo`
+// on (a multiple of kChunk; 0 when they meet).
+__host__ __device__ __forceinline__ int visit_shift(int sink, int lo) {
   const int sink_chunks = (sink + kChunk - 1) / kChunk;
-  const int lo = L - window;
   const int win_chunk = lo > 0 ? lo / kChunk : 0;
   return win_chunk > sink_chunks ? (win_chunk - sink_chunks) * kChunk : 0;
 }
 
+// What a sequence of L positions attends to, besides t < L: t < sink or
+// t >= lo.  With a window, sink and L - window; in the suffix pass of
+// shared prefixes, no sink and its own first position `start`; otherwise
+// every position (lo = 0).
+__device__ __forceinline__ int attend_sink(const DecodeArgs& a) { return a.window > 0 ? a.sink : 0; }
+__device__ __forceinline__ int attend_lo(const DecodeArgs& a, int L, int start) {
+  return a.window > 0 ? L - a.window : start;
+}
+
 // Positions the walk of a sequence of L positions visits.
-__device__ __forceinline__ int visit_len(const DecodeArgs& a, int L) {
-  return L - window_shift(L, a.sink, a.window);
+__device__ __forceinline__ int visit_len(const DecodeArgs& a, int L, int start) {
+  return L - visit_shift(attend_sink(a), attend_lo(a, L, start));
 }
 
 // Queries of sequence s under MQ (qs = q_start, in memory or in LDS): first
-// row and count, clamped to at most nq, at most the sequence's length and to
-// rows that exist.
-__device__ __forceinline__ void query_range(const DecodeArgs& a, const int* qs, int s, int L, int& row0, int& n) {
+// row and count, clamped to at most nq, at most the sequence's length
+// (causal: query j of n sees up to L - n + j) and to rows that exist.
+__device__ __forceinline__ void query_range(const DecodeArgs& a, const int* qs, int s, int L, int& row0, int& n,
+                                            bool causal = true) {
   row0 = qs[s];
-  n = max(0, min(qs[s + 1] - row0, min(a.nq, L)));
+  n = max(0, min(qs[s + 1] - row0, causal ? min(a.nq, L) : a.nq));
   if (row0 < 0 || row0 > a.q_rows - n) n = 0, row0 = 0;
 }
 
@@ -178,14 +201,27 @@ struct Slice {
   int s_first;  // first sequence it visits
 };
 
-// Fills cum[], lens[] (clamped context lengths), qrow[] (q_start, when
-// several queries per sequence; null otherwise) and sl; returns false when
-// the slice holds nothing.  Wave 0 also publishes S, the slice count and
+// Fills cum[], lens[] (clamped context lengths), qrow[] and sl; returns false
+// when the slice holds nothing.  qrow (null if the kernel has none) gets
+// q_start with several queries per sequence, or, in the suffix pass of
+// shared prefixes (no q_start), each sequence's first attended position
+// (its group's prefix length).  Wave 0 also publishes S, the slice count and
 // cum[] for the merge kernel.
 __device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int* lens, int* qrow, int k, Slice& sl) {
   const int lane = __lane_id();
   int carry = 0;
-  if (qrow != nullptr && lane == 0) qrow[a.B] = a.q_start[a.B];
+  const bool starts = qrow != nullptr && a.q_start == nullptr;
+  if (qrow != nullptr && lane == 0) qrow[a.B] = starts ? 0 : a.q_start[a.B];
+  if (starts) {
+    for (int s = lane; s < a.B; s += 64) qrow[s] = 0;
+    __syncthreads();
+    for (int p = lane; p < a.n_groups; p += 64) {
+      const int lo = max(a.group_start[p], 0), hi = min(a.group_start[p + 1], a.B);
+      const int pl = max(a.prefix_lens[p], 0);
+      for (int s = lo; s < hi; ++s) qrow[s] = pl;
+    }
+    __syncthreads();
+  }
   for (int base = 0; base < a.B; base += 64) {
     const int s = base + lane;
     int n = 0;
@@ -193,8 +229,8 @@ __device__ __forceinline__ bool slice_setup(const DecodeArgs& a, int* cum, int* 
       int L = a.context_lens[s];
       L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
       lens[s] = L;
-      if (qrow != nullptr) qrow[s] = a.q_start[s];
-      n = L > 0 ? (visit_len(a, L) + kChunk - 1) / kChunk + a.seg_cost : 0;
+      if (qrow != nullptr && !starts) qrow[s] = a.q_start[s];
+      n = L > 0 ? (visit_len(a, L, starts ? min(qrow[s], L) : 0) + kChunk - 1) / kChunk + a.seg_cost : 0;
     }
     const int inc = wave_inclusive_sum(n);
     if (s < a.B) cum[s + 1] = carry + inc;
@@ -247,12 +283,14 @@ struct Segment {
   int cs, ce;        // the range of the sequence's chunks on the line (after its charge)
   int tok0, tok_end; // visited positions of the piece
   int nchunks;
-  int shift;         // window_shift of the sequence (0 without a window)
+  int shift;         // visit_shift of the sequence (0 when its walk skips nothing)
 };
 
-// First sequence at or after s_from that is not empty and has chunks in the slice.
+// First sequence at or after s_from that is not empty and has chunks in the
+// slice.  starts: each sequence's first attended position (the suffix pass of
+// shared prefixes), or null.
 __device__ __forceinline__ Segment next_segment(const DecodeArgs& a, const Slice& sl, const int* cum,
-                                                const int* lens, int s_from) {
+                                                const int* lens, int s_from, const int* starts = nullptr) {
   Segment g;
   g.s = -1;
   g.cs = g.ce = g.tok0 = g.tok_end = g.nchunks = g.shift = 0;
@@ -263,7 +301,7 @@ __device__ __forceinline__ Segment next_segment(const DecodeArgs& a, const Slice
       if (past_slice(sl, cum[s], ce)) break;
       continue;
     }
-    const int Lv = visit_len(a, L);
+    const int Lv = visit_len(a, L, starts != nullptr ? min(starts[s], L) : 0);
     const int cs = ce - (Lv + kChunk - 1) / kChunk;  // the charge lies before cs
     if (cs >= sl.c1) break;
     g.s = uniform(s);

@@ -30,11 +30,17 @@ bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
 // written by the decode kernel and are skipped here.  A piece that saw no
 // position holds m = -inf and is skipped: under MQ one whose positions all
 // lie past what a query sees, with a window one that lies in the gap between
-// the sink and the window.  Lengths on the chunk line are visited lengths.
+// the sink and the window.  A sequence's chunks on the line start seg_cost
+// after its place in the scan (meta), whatever its walk visits.
+//
+// STATE (the prefix pass of shared prefixes): every member of a group sees
+// the whole prefix, and the merged (M, den) and num are written unnormalised
+// to the member's state rows, where the suffix pass starts from them.
 constexpr int kMergeUnroll = 8;
 
-template <int D, bool MQ>
+template <int D, bool MQ, bool STATE = false>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
+  static_assert(!STATE || MQ, "the prefix pass is a several-queries launch");
   constexpr int LPH = D / 4;  // threads per head
   const int h = blockIdx.x;
   const int s = blockIdx.y;
@@ -44,13 +50,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
   int L = a.context_lens[s];
   L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
   if (L == 0) return;
-  const int cs = ce - (visit_len(a, L) + kChunk - 1) / kChunk;  // the sequence's chunks, after its charge
+  const int cs = a.meta[2 + s] + a.seg_cost;  // the sequence's chunks, after its charge
   const int kf = cs / S;
   const int kl = min((ce - 1) / S, neff - 1);
   if (kl <= kf) return;
   const int np = kl - kf + 1;
   int qrow0 = s, nqs = 1;
-  if constexpr (MQ) query_range(a, a.q_start, s, L, qrow0, nqs);
+  if constexpr (MQ) query_range(a, a.q_start, s, L, qrow0, nqs, !STATE);
   for (int idx = blockIdx.z * blockDim.x + threadIdx.x; idx < nqs * a.G * LPH; idx += gridDim.z * blockDim.x) {
     const int jq = MQ ? idx / (a.G * LPH) : 0;
     const int rem = idx - jq * a.G * LPH;
@@ -81,9 +87,15 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
         }
       }
     }
-    const float f = a.v_scale / den;
-    const float v[4] = {num[0] * f, num[1] * f, num[2] * f, num[3] * f};
-    store_out(a, qrow0 + jq, head, D, d, v, 4);
+    if constexpr (STATE) {
+      const int64_t row = (int64_t)(qrow0 + jq) * a.Hkv * a.G + head;
+      *reinterpret_cast<f32x4*>(a.state_acc + row * D + d) = num;
+      if (d == 0) *reinterpret_cast<f32x2*>(a.state_ml + 2 * row) = f32x2{M, den};
+    } else {
+      const float f = a.v_scale / den;
+      const float v[4] = {num[0] * f, num[1] * f, num[2] * f, num[3] * f};
+      store_out(a, qrow0 + jq, head, D, d, v, 4);
+    }
   }
 }
 
@@ -325,6 +337,150 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
       set_error("pa_decode: launch failed: %s", hipGetErrorString(err));
       return PA_ERR_HIP;
     }
+  }
+  return PA_OK;
+}
+
+// ------------------------------------------------- shared prefixes (cascade)
+
+bool launch_cascade_pass(bool prefix, const DecodeArgs& a, int ct, int qt, int head_dim, int bs, dim3 grid,
+                         hipStream_t stream, const LaunchEvents& ev);
+
+// 16-column tiles of a group's (member, head) columns; a prefix-pass wave
+// computes two
+static int prefix_tiles(int max_group, int G) {
+  const int64_t col_tiles = ((int64_t)max_group * G + 15) / 16;
+  return (int)((col_tiles + 1) / 2);
+}
+
+// Workspace of one cascade call: [prefix plan][suffix plan][state m, l][state acc]
+struct CascadeLayout {
+  DecodePlan pre, suf;
+  size_t suf_off, state_ml_off, state_acc_off, bytes;
+};
+
+static CascadeLayout cascade_layout(int B, int P, int max_group, int Hkv, int G, int D, int bs, int max_ctx,
+                                    int64_t waves, int pre_tiles) {
+  CascadeLayout c{};
+  c.pre = plan_decode(P, Hkv, G, D, bs, max_ctx, pre_tiles, waves, max_group, true, false);
+  // the suffix pass keeps first positions in LDS: the several-queries scan capacity
+  c.suf = plan_decode(B, Hkv, G, D, bs, max_ctx, 1, waves, 1, true, false);
+  const size_t Hq = (size_t)Hkv * G;
+  c.suf_off = align256(c.pre.bytes);
+  c.state_ml_off = c.suf_off + align256(c.suf.bytes);
+  c.state_acc_off = c.state_ml_off + align256(sizeof(float) * 2 * (size_t)B * Hq);
+  c.bytes = c.state_acc_off + align256(sizeof(float) * (size_t)D * B * Hq);
+  return c;
+}
+
+size_t cascade_workspace_bound(int B, int n_groups, int max_group, int Hkv, int G, int D, int bs, int max_ctx) {
+  return cascade_layout(B, n_groups, max_group, Hkv, G, D, bs, max_ctx, (int64_t)kMaxWavesPerCU * kPlanMaxCUs, 1)
+      .bytes;
+}
+
+int cascade_max_sequences() { return scan_capacity(true, false); }
+
+template <bool STATE>
+static void launch_merge(const DecodeArgs& a, int D, int nq, hipStream_t stream) {
+  const int64_t threads = (int64_t)nq * a.G * (D / 4);
+  const dim3 mgrid(a.Hkv, a.B, (unsigned)std::min<int64_t>(65535, (threads + 255) / 256));
+  const dim3 mblock(threads >= 256 ? 256 : (unsigned)(((threads + 63) / 64) * 64));
+  if (D == 64)
+    hipLaunchKernelGGL((decode_merge_kernel<64, STATE, STATE>), mgrid, mblock, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<128, STATE, STATE>), mgrid, mblock, 0, stream, a);
+}
+
+pa_status cascade_launch(const DecodeRequest& r, hipStream_t stream) {
+  const int P = r.n_groups, nq = r.nq;
+  const int tiles = prefix_tiles(nq, r.G);
+  const CascadeLayout c = cascade_layout(r.B, P, nq, r.Hkv, r.G, r.D, r.bs, r.plan_ctx,
+                                         (int64_t)waves_per_cu(false) * plan_cus(), tiles);
+  if (r.workspace_bytes < c.bytes) {
+    set_error("pa_decode_shared_prefix: workspace of %zu bytes needed, %zu given", c.bytes, r.workspace_bytes);
+    return PA_ERR_WORKSPACE;
+  }
+  if (P > c.pre.sub_batch || r.B > c.suf.sub_batch) {
+    set_error("pa_decode_shared_prefix: %d sequences in %d groups exceed one launch (%d, %d)", r.B, P,
+              c.suf.sub_batch, c.pre.sub_batch);
+    return PA_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)std::max(c.pre.nslices * tiles, c.suf.nslices) * r.Hkv >= ((int64_t)1 << 31)) {
+    set_error("pa_decode_shared_prefix: the grid is too large");
+    return PA_ERR_UNSUPPORTED;
+  }
+  uint8_t* ws = reinterpret_cast<uint8_t*>(r.workspace);
+  const bool fp8 = r.cache_dtype == PA_FP8_E4M3;
+  DecodeArgs a{};
+  a.k_cache = reinterpret_cast<const uint8_t*>(r.k_cache);
+  a.v_cache = reinterpret_cast<const uint8_t*>(r.v_cache);
+  a.num_blocks = r.num_blocks;
+  a.Hkv = r.Hkv;
+  a.G = r.G;
+  a.M = r.M;
+  a.max_ctx = r.max_ctx;
+  a.out_dtype = r.out_dtype == PA_F32 ? 0 : (r.out_dtype == PA_F16 ? 1 : 2);
+  a.qk_scale_log2 = r.scale * (fp8 ? r.k_scale : 1.f) * 1.4426950408889634f;
+  a.v_scale = fp8 ? r.v_scale : 1.f;
+  a.out = r.out;
+  a.q = r.q;
+  a.block_tables = r.block_tables;
+  a.group_start = r.group_start;
+  a.prefix_lens = r.prefix_lens;
+  a.n_groups = P;
+  a.state_ml = reinterpret_cast<float*>(ws + c.state_ml_off);
+  a.state_acc = reinterpret_cast<float*>(ws + c.state_acc_off);
+  const hipEvent_t t_start = g_time_start, t_stop = g_time_stop;
+  g_time_start = g_time_stop = nullptr;
+
+  // prefix pass: the groups, their members as the queries, each member seeing
+  // the whole prefix; whole prefixes leave states, cut ones partials merged
+  // into states
+  DecodeArgs pre = a;
+  pre.meta = reinterpret_cast<int32_t*>(ws + c.pre.meta_off);
+  pre.part_ml = reinterpret_cast<float*>(ws + c.pre.ml_off);
+  pre.part_acc = reinterpret_cast<float*>(ws + c.pre.acc_off);
+  pre.B = P;
+  pre.context_lens = r.prefix_lens;
+  pre.q_start = r.group_start;
+  pre.nq = nq;
+  pre.q_rows = r.B;
+  pre.nslices = c.pre.nslices;
+  pre.min_slice = c.pre.min_slice;
+  pre.seg_cost = c.pre.seg_cost;
+  pre.head_tiles = tiles;
+  if (!launch_cascade_pass(true, pre, r.cache_dtype, r.q_dtype, r.D, r.bs,
+                           dim3((unsigned)((int64_t)c.pre.nslices * r.Hkv * tiles)), stream,
+                           LaunchEvents{t_start, nullptr})) {
+    set_error("pa_decode_shared_prefix: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d",
+              r.cache_dtype, r.q_dtype, r.D, r.bs);
+    return PA_ERR_UNSUPPORTED;
+  }
+  if (c.pre.nslices > 1) launch_merge<true>(pre, r.D, nq, stream);
+
+  // suffix pass: every sequence from its group's prefix length on, starting
+  // from its state
+  DecodeArgs suf = a;
+  const uint8_t* sw = ws + c.suf_off;
+  suf.meta = reinterpret_cast<int32_t*>(const_cast<uint8_t*>(sw) + c.suf.meta_off);
+  suf.part_ml = reinterpret_cast<float*>(const_cast<uint8_t*>(sw) + c.suf.ml_off);
+  suf.part_acc = reinterpret_cast<float*>(const_cast<uint8_t*>(sw) + c.suf.acc_off);
+  suf.B = r.B;
+  suf.context_lens = r.context_lens;
+  suf.q_start = nullptr;
+  suf.nq = 1;
+  suf.q_rows = r.B;
+  suf.nslices = c.suf.nslices;
+  suf.min_slice = c.suf.min_slice;
+  suf.seg_cost = c.suf.seg_cost;
+  suf.head_tiles = 1;
+  launch_cascade_pass(false, suf, r.cache_dtype, r.q_dtype, r.D, r.bs, dim3((unsigned)((int64_t)c.suf.nslices * r.Hkv)),
+                      stream, LaunchEvents{nullptr, t_stop});
+  if (c.suf.nslices > 1) launch_merge<false>(suf, r.D, 1, stream);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) {
+    set_error("pa_decode_shared_prefix: launch failed: %s", hipGetErrorString(err));
+    return PA_ERR_HIP;
   }
   return PA_OK;
 }

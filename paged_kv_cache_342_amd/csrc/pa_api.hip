@@ -162,12 +162,6 @@ pa_status decode_request(const char* fn, void* out, const void* q, const void* k
     return fail(PA_ERR_INVALID_ARG, "%s: misaligned pointer argument", fn);
   const int full = max_blocks_per_seq * block_size;
   const int plan_ctx = max_context_len > 0 ? max_context_len : full;
-  const size_t need = decode_workspace_bound(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx, nq,
-                                             multi_query);
-  if (!workspace || workspace_bytes < need)
-    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   r.out = out;
   r.q = q;
   r.k_cache = k_cache;
@@ -190,6 +184,14 @@ pa_status decode_request(const char* fn, void* out, const void* q, const void* k
   r.out_dtype = out_dtype;
   r.workspace = workspace;
   r.workspace_bytes = workspace_bytes;
+  // last: a call whose every other argument is valid gets PA_ERR_WORKSPACE
+  // with r filled (the shared-prefix call sizes its own workspace from it)
+  const size_t need = decode_workspace_bound(B, num_kv_heads, gqa_group, head_dim, block_size, plan_ctx, nq,
+                                             multi_query);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
   return PA_OK;
 }
 
@@ -251,6 +253,58 @@ pa_status pa_decode_window(void* out, const void* q, const void* k_cache, const 
   r.window = window_tokens > (1 << 30) ? (1 << 30) : window_tokens;
   PA_CONTRACT(check_decode_contract(fn, r, reinterpret_cast<hipStream_t>(stream)));
   return decode_launch(r, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t pa_decode_shared_prefix_workspace_size(int32_t B, int32_t num_groups, int32_t max_group_size,
+                                              int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                                              int32_t block_size, int32_t max_context_len) {
+  if (B <= 0 || num_groups <= 0 || num_groups > B || max_group_size <= 0 || num_kv_heads <= 0 || gqa_group <= 0 ||
+      max_context_len <= 0)
+    return 0;
+  if ((head_dim != 64 && head_dim != 128) || (block_size != 8 && block_size != 16 && block_size != 32)) return 0;
+  if (max_group_size > kMaxQueries || B > cascade_max_sequences()) return 0;
+  return cascade_workspace_bound(B, num_groups, max_group_size, num_kv_heads, gqa_group, head_dim, block_size,
+                                 max_context_len);
+}
+
+pa_status pa_decode_shared_prefix(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens, int32_t B,
+                                  int32_t num_groups, int32_t max_group_size, int32_t num_kv_heads,
+                                  int32_t gqa_group, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                  int32_t max_blocks_per_seq, int32_t max_context_len, float scale, float k_scale,
+                                  float v_scale, pa_dtype q_dtype, pa_dtype cache_dtype, pa_dtype out_dtype,
+                                  void* workspace, size_t workspace_bytes, pa_stream_t stream) {
+  g_error[0] = 0;
+  const char* fn = "pa_decode_shared_prefix";
+  if (max_group_size < 1 || max_group_size > kMaxQueries)
+    return fail(PA_ERR_UNSUPPORTED, "%s: max_group_size must be in [1, %d] (got %d)", fn, kMaxQueries, max_group_size);
+  DecodeRequest r;
+  // every check of pa_decode but the workspace, which is this call's own
+  pa_status st = decode_request(fn, out, q, k_cache, v_cache, block_tables, context_lens, B, num_kv_heads, gqa_group,
+                                head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len, scale, k_scale,
+                                v_scale, q_dtype, cache_dtype, out_dtype, nullptr, 0, 1, false, false, r);
+  if (st != PA_ERR_WORKSPACE) return st;  // an invalid argument, or OK for B == 0
+  if (num_groups < 1 || num_groups > B)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_groups must be in [1, B] (got %d)", fn, num_groups);
+  if (B > cascade_max_sequences())
+    return fail(PA_ERR_UNSUPPORTED, "%s: at most %d sequences per call", fn, cascade_max_sequences());
+  if (!group_start || !prefix_lens || !aligned(group_start, 4) || !aligned(prefix_lens, 4))
+    return fail(PA_ERR_INVALID_ARG, "%s: null or misaligned group_start / prefix_lens", fn);
+  const size_t need = cascade_workspace_bound(B, num_groups, max_group_size, num_kv_heads, gqa_group, head_dim,
+                                              block_size, r.plan_ctx);
+  if (!workspace || workspace_bytes < need)
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(PA_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+  r.workspace = workspace;
+  r.workspace_bytes = workspace_bytes;
+  r.group_start = group_start;
+  r.prefix_lens = prefix_lens;
+  r.n_groups = num_groups;
+  r.nq = max_group_size;
+  PA_CONTRACT(check_decode_contract(fn, r, reinterpret_cast<hipStream_t>(stream)));
+  return cascade_launch(r, reinterpret_cast<hipStream_t>(stream));
 }
 
 pa_status pa_decode_append(void* out, const void* q, void* k_cache, void* v_cache, const void* key,

@@ -86,7 +86,23 @@ struct DecodeRequest {
   // attends to t < sink and t >= L - window; window == 0 = every position
   int sink;
   int window;
+  // shared prefixes (pa_decode_shared_prefix): group p is sequences
+  // group_start[p] .. group_start[p + 1] - 1 (device, [n_groups + 1]), which
+  // share their first prefix_lens[p] positions (device, [n_groups]); nq is
+  // then the largest group
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int n_groups;
 };
+
+// Workspace bytes of pa_decode_shared_prefix: the prefix pass's plan over
+// the groups, the suffix pass's plan over the sequences and the members'
+// states, for any device (as decode_workspace_bound).
+size_t cascade_workspace_bound(int B, int n_groups, int max_group, int Hkv, int G, int D, int bs, int max_ctx);
+// Most sequences (and groups) one pa_decode_shared_prefix call takes: each
+// pass runs as a single launch.
+int cascade_max_sequences();
+pa_status cascade_launch(const DecodeRequest& r, hipStream_t stream);
 
 // 0 = default choice, 1 = VALU/DPP kernel, 2 = MFMA kernel
 int decode_variant_override();

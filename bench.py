@@ -38,8 +38,7 @@ CSRC = os.path.join(ROOT, "paged_kv_cache_342_amd", "csrc")
 # sources of the kernels a pa_decode call runs; profiler traffic recorded for
 # other sources is stale and is not reported
 DECODE_SOURCES = ("pa_device.h", "decode_common.h", "decode_core.hip", "decode_mfma_kernel.h", "decode_mfma.hip",
-                  "decode_cascade.hip", "decode_valu.hip",
-                  "cache_ops.hip")
+                  "decode_cascade.hip", "decode_prefill.hip", "decode_valu.hip", "cache_ops.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
 

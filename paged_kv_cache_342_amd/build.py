@@ -25,8 +25,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 LIB_CHECKED = os.path.join(PKG, "libpa_checked.so")
 
-SOURCES = ["pa_api.hip", "pa_noalloc.hip", "decode_core.hip", "decode_mfma.hip", "decode_cascade.hip", "decode_valu.hip",
-           "cache_ops.hip"]
+SOURCES = ["pa_api.hip", "pa_noalloc.hip", "decode_core.hip", "decode_mfma.hip", "decode_cascade.hip",
+           "decode_prefill.hip", "decode_valu.hip", "cache_ops.hip"]
 HOST_SOURCES = ["block_manager.cpp"]  # host-only C++, built with the host compiler
 CHECKED_SOURCES = ["pa_api.hip", "contract_check.hip"]  # compiled again with PA_CHECKED
 
@@ -86,7 +86,7 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     # the slowest source first, so it never waits for a free worker
     jobs = [(s, False) for s in SOURCES + HOST_SOURCES] + [(s, True) for s in CHECKED_SOURCES]
-    jobs.sort(key=lambda j: j[0] not in ("decode_mfma.hip", "decode_cascade.hip"))
+    jobs.sort(key=lambda j: j[0] not in ("decode_mfma.hip", "decode_cascade.hip", "decode_prefill.hip"))
     workers = min(len(jobs), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with ThreadPoolExecutor(workers) as ex:
         objs = dict(zip(jobs, ex.map(_compile, jobs)))

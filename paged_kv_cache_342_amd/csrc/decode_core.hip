@@ -17,6 +17,10 @@ bool mfma_kernel_built(int ct, int qt, int head_dim, int bs, bool multi_query, b
 bool launch_decode_valu(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, int group,
                         dim3 grid, hipStream_t stream, const LaunchEvents& ev);
 bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
+bool launch_prefill(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, dim3 grid, hipStream_t stream,
+                    const LaunchEvents& ev);
+// waves per workgroup of the prefill kernel (decode_prefill.hip): 256 columns
+constexpr int kPrefillWavesHost = 8;
 
 // Workgroups per (KV head, sequence) -- one for decode, more when its
 // queries hold more outputs than a workgroup has threads: merge the slices'
@@ -173,17 +177,20 @@ void set_timing_events(hipEvent_t start, hipEvent_t stop) {
   g_time_stop = stop;
 }
 
-// Long query chunks on a 16-bit cache: 2 = workgroups of kSharedWaves1 waves
-// with one tile each at two waves per SIMD (the default: 16 x 64-query
-// chunked prefill 122 us against 144 us for mode 1 and 145 us for mode 0),
-// 1 = kSharedWaves waves with two tiles each at one wave per SIMD (also where
-// the queries span fewer than kSharedWaves1 tiles), 0 = one wave per
-// workgroup (PA_DECODE_MQ_SHARED, for comparisons)
+// Long query chunks on a 16-bit cache (PA_DECODE_MQ_SHARED, for comparisons):
+// 3 = the prefill kernel, workgroups of kPrefillWaves waves with 32 x 32
+// tiles (the default from kSharedWaves1 16-column tiles on); 2 = workgroups
+// of kSharedWaves1 waves with one 16-column tile each at two waves per SIMD
+// (16 x 64-query chunked prefill 122 us against 144 us for mode 1 and 145 us
+// for mode 0); 1 = kSharedWaves waves with two tiles each at one wave per
+// SIMD (also where the queries span fewer than kSharedWaves1 tiles); 0 = one
+// wave per workgroup
 static int mq_shared_mode() {
   const char* v = std::getenv("PA_DECODE_MQ_SHARED");
   if (v && v[0] == '0') return 0;
   if (v && v[0] == '1') return 1;
-  return 2;
+  if (v && v[0] == '2') return 2;
+  return 3;
 }
 
 int decode_variant_override() {
@@ -223,12 +230,16 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   // queries spanning kSharedWaves or more tile pairs of a 16-bit cache: the
   // waves of a workgroup share each K/V chunk through LDS
   const int shared_mode = mq && !rs && (r.cache_dtype == PA_F16 || r.cache_dtype == PA_BF16) ? mq_shared_mode() : 0;
+  // the prefill kernel: 256 (query, head) columns per workgroup of kPrefillWaves waves
+  const bool prefill = shared_mode == 3 && col_tiles >= kSharedWaves1;
+  const int prefill_groups = (int)(((int64_t)nq * r.G + 32 * kPrefillWavesHost - 1) / (32 * kPrefillWavesHost));
   const bool shared1 = shared_mode == 2 && col_tiles >= kSharedWaves1;  // one tile per wave
-  const int tw = mq && col_tiles >= 2 && !shared1 ? 2 : 1;
-  const int tiles = (col_tiles + tw - 1) / tw;  // waves per (slice, KV head)
-  const bool two_waves = !valu && (shared1 || mfma_two_waves(r.cache_dtype, rs, tw));
+  const int tw = mq && col_tiles >= 2 && !shared1 && !prefill ? 2 : 1;
+  // waves per (slice, KV head)
+  const int tiles = prefill ? prefill_groups * kPrefillWavesHost : (col_tiles + tw - 1) / tw;
+  const bool two_waves = !valu && (prefill || shared1 || mfma_two_waves(r.cache_dtype, rs, tw));
   const bool shared = shared1 || (shared_mode >= 1 && tw == 2 && tiles >= kSharedWaves);
-  const int group_waves = shared1 ? kSharedWaves1 : (shared ? kSharedWaves : 1);
+  const int group_waves = prefill ? kPrefillWavesHost : (shared1 ? kSharedWaves1 : (shared ? kSharedWaves : 1));
   const int group_tiles = (tiles + group_waves - 1) / group_waves;  // workgroups per (slice, KV head)
   const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles,
                                       (int64_t)waves_per_cu(two_waves) * plan_cus(), nq, mq, two_waves);
@@ -312,8 +323,9 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
     a.new_k = fused_append ? reinterpret_cast<const uint8_t*>(r.new_k) + (size_t)s0 * new_row : nullptr;
     a.new_v = fused_append ? reinterpret_cast<const uint8_t*>(r.new_v) + (size_t)s0 * new_row : nullptr;
     const dim3 grid((unsigned)((int64_t)plan.nslices * r.Hkv * group_tiles));
-    const bool ok = valu ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream, ev)
-                         : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, tw, group_waves, grid, stream, ev);
+    const bool ok = valu      ? launch_decode_valu(a, ct, qt, r.D, r.bs, r.G, grid, stream, ev)
+                    : prefill ? launch_prefill(a, ct, qt, r.D, r.bs, grid, stream, ev)
+                              : launch_decode_mfma(a, ct, qt, r.D, r.bs, mq, tw, group_waves, grid, stream, ev);
     if (!ok) {
       set_error("pa_decode: no kernel built for cache dtype %d, q dtype %d, head_dim %d, block size %d, group %d (%s)",
                 ct, qt, r.D, r.bs, r.G, valu ? "valu" : "mfma");

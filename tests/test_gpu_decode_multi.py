@@ -121,31 +121,34 @@ def test_multi_query_more_sequences_than_one_launch_scans():
 
 @pytest.mark.parametrize("cache,D,bs,G", [("bf16", 128, 16, 4), ("f16", 64, 8, 8), ("bf16", 128, 32, 4),
                                           ("f16", 128, 16, 16)])
-@pytest.mark.parametrize("mode", ["1", "2"])
+@pytest.mark.parametrize("mode", ["1", "2", "3"])
 def test_shared_chunk_kernel_equals_one_wave_kernel(cache, D, bs, G, mode, monkeypatch):
     """Queries spanning several tiles run a kernel whose waves share each K/V
-    chunk through LDS: four waves of two tiles (mode 1) or eight waves of one
-    tile at two waves per SIMD (mode 2, the default).  Either reads the bytes
-    the one-wave kernel reads (PA_DECODE_MQ_SHARED=0) and does the same
-    arithmetic per tile, so they must agree bit for bit, and with the oracle.
-    Some sequences have fewer queries than the workgroup has tiles, so some
-    waves only load."""
+    chunk through LDS: four waves of two tiles (mode 1), eight waves of one
+    tile at two waves per SIMD (mode 2), or the prefill kernel's 32 x 32
+    tiles (mode 3, the default).  Modes 1 and 2 read the bytes the one-wave
+    kernel reads (PA_DECODE_MQ_SHARED=0) and do the same arithmetic per tile,
+    so they must agree with it bit for bit; every mode agrees with the
+    oracle.  Some sequences have fewer queries than the workgroup has
+    columns, so some waves only load."""
     lens = [40, 300, 1031, 77, 513, 64, 129, 2050]
     nqs = [32, 64, 40, 5, 64, 64, 1, 48]
     w = W.multi_query(f"mq_shared_{cache}_D{D}_bs{bs}_g{G}", 330 + G, lens, nqs, 2 * G, 2, D, bs, cache)
     monkeypatch.setenv("PA_DECODE_MQ_SHARED", mode)
     g, out = _check_multi(w, label=f"[shared chunks, mode {mode}]")
-    monkeypatch.setenv("PA_DECODE_MQ_SHARED", "0")
-    one = g.decode_multi().cpu().numpy()
-    assert np.array_equal(out.astype(np.float32), one)
+    if mode != "3":
+        monkeypatch.setenv("PA_DECODE_MQ_SHARED", "0")
+        one = g.decode_multi().cpu().numpy()
+        assert np.array_equal(out.astype(np.float32), one)
 
 
 @pytest.mark.parametrize("seed", range(6))
 def test_shared_chunk_kernels_on_random_shapes(seed, monkeypatch):
     """Seeded random batches (group 1-16, head_dim 64/128, block size 8/16/32,
     f16/bf16, empty sequences, sequences without queries, query counts up to
-    the length): both shared-chunk kernels equal the one-wave kernel bit for
-    bit, and the default one is within tolerance of the oracle."""
+    the length): both 16-column shared-chunk kernels equal the one-wave
+    kernel bit for bit, and the default (the prefill kernel) is within
+    tolerance of the oracle and gives the same bits on every call."""
     rng = np.random.default_rng(900 + seed)
     G = [1, 2, 4, 8, 16, 4][seed]
     D = [64, 128][seed % 2]
@@ -162,8 +165,22 @@ def test_shared_chunk_kernels_on_random_shapes(seed, monkeypatch):
     log(f"[random shapes seed={seed}] G={G} D={D} bs={bs} {cache} lens={lens} nqs={nqs}")
     g, out = _check_multi(w, label=f"[random {seed}]")
     res = {}
-    for mode in ("0", "1", "2"):
+    for mode in ("0", "1", "2", "3"):
         monkeypatch.setenv("PA_DECODE_MQ_SHARED", mode)
         res[mode] = g.decode_multi().cpu().numpy()
     assert np.array_equal(res["1"], res["0"]) and np.array_equal(res["2"], res["0"])
-    assert np.array_equal(out.astype(np.float32), res["2"])
+    assert np.array_equal(out.astype(np.float32), res["3"])
+
+
+@pytest.mark.parametrize("cache,D,bs,G,nq", [("bf16", 128, 16, 4, 64), ("f16", 128, 8, 8, 64), ("bf16", 64, 32, 4, 100),
+                                             ("f16", 64, 16, 16, 40), ("bf16", 128, 32, 1, 300)])
+def test_prefill_kernel_shapes(cache, D, bs, G, nq):
+    """The prefill kernel (256 (query, head) columns per workgroup of eight
+    waves, 32 x 32 tiles) on chunks that need one or several column groups
+    (nq * G up to 512), query chunks shorter than the sequence and equal to
+    it, ragged lengths around chunk and block boundaries, and sequences cut
+    by slices (long ones)."""
+    lens = [nq, nq + 1, 2 * nq + 31, 1000, 4097, 33, 0, 777]
+    nqs = [min(L, n) for L, n in zip(lens, [nq, nq, nq, nq, nq, nq, 0, nq // 2])]
+    w = W.multi_query(f"prefill_{cache}_D{D}_bs{bs}_g{G}_n{nq}", 950 + G + nq, lens, nqs, 2 * G, 2, D, bs, cache)
+    _check_multi(w, label="[prefill kernel]")

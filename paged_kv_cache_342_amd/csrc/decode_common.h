@@ -57,6 +57,9 @@ constexpr int kScanMaxMQ = 3072;
 // that eight workgroups' arrays fit the 160 KiB of LDS.
 constexpr int kScanMax2 = 2048;
 constexpr int kScanMaxMQ2 = 1536;
+// The prefill kernel keeps its query rows and five K/V stages in LDS next to
+// the arrays, which leaves room for this many sequences per launch.
+constexpr int kScanPrefill = 512;
 
 // Which MFMA kernels run two waves per SIMD: FP4.  Its waves are bound by
 // instruction issue at one wave per SIMD (5% of their cycles waiting on

@@ -20,6 +20,7 @@ bool valu_supports(int ct, int qt, int head_dim, int bs, int group);
 bool launch_prefill(const DecodeArgs& a, int ct, int qt, int head_dim, int bs, dim3 grid, hipStream_t stream,
                     const LaunchEvents& ev);
 // waves per workgroup of the prefill kernel (decode_prefill.hip): 256 columns
+// in 32-column tiles, two waves per SIMD
 constexpr int kPrefillWavesHost = 8;
 
 // Workgroups per (KV head, sequence) -- one for decode, more when its
@@ -138,7 +139,7 @@ static int waves_per_cu(bool two_waves) {
 }
 
 DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int64_t waves, int nq,
-                       bool multi_query, bool two_waves) {
+                       bool multi_query, bool two_waves, int scan_cap) {
   (void)bs;
   DecodePlan p{};
   const int64_t per = (int64_t)Hkv * head_tiles;
@@ -147,7 +148,7 @@ DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int he
   p.seg_cost = segment_cost();
   const int64_t chunks = ((int64_t)std::max(max_ctx, 1) + kChunk - 1) / kChunk + p.seg_cost;
   // the kernel's LDS scan arrays bound the sequences of one launch
-  int64_t sub = std::min<int64_t>(scan_capacity(multi_query, two_waves), INT_MAX / chunks);
+  int64_t sub = std::min<int64_t>(scan_cap > 0 ? scan_cap : scan_capacity(multi_query, two_waves), INT_MAX / chunks);
   p.sub_batch = (int)std::max<int64_t>(1, std::min<int64_t>(sub, std::max(B, 1)));
   const size_t Hq = (size_t)Hkv * G * std::max(nq, 1);  // partial rows per (slice, sequence)
   const size_t rows = (size_t)p.nslices + p.sub_batch;
@@ -231,23 +232,26 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   // waves of a workgroup share each K/V chunk through LDS
   const int shared_mode = mq && !rs && (r.cache_dtype == PA_F16 || r.cache_dtype == PA_BF16) ? mq_shared_mode() : 0;
   // the prefill kernel: 256 (query, head) columns per workgroup of kPrefillWaves waves
-  const bool prefill = shared_mode == 3 && col_tiles >= kSharedWaves1;
-  const int prefill_groups = (int)(((int64_t)nq * r.G + 32 * kPrefillWavesHost - 1) / (32 * kPrefillWavesHost));
+  // (it addresses a block with a 32-bit stride)
+  const bool prefill = shared_mode == 3 && col_tiles >= kSharedWaves1 &&
+                       (int64_t)r.Hkv * r.bs * r.D * 2 <= (int64_t)UINT32_MAX;
+  const int prefill_groups = (int)(((int64_t)nq * r.G + 255) / 256);
   const bool shared1 = shared_mode == 2 && col_tiles >= kSharedWaves1;  // one tile per wave
   const int tw = mq && col_tiles >= 2 && !shared1 && !prefill ? 2 : 1;
   // waves per (slice, KV head)
   const int tiles = prefill ? prefill_groups * kPrefillWavesHost : (col_tiles + tw - 1) / tw;
   const bool two_waves = !valu && (prefill || shared1 || mfma_two_waves(r.cache_dtype, rs, tw));
+  const int scan_cap = prefill ? kScanPrefill : scan_capacity(mq, two_waves);
   const bool shared = shared1 || (shared_mode >= 1 && tw == 2 && tiles >= kSharedWaves);
   const int group_waves = prefill ? kPrefillWavesHost : (shared1 ? kSharedWaves1 : (shared ? kSharedWaves : 1));
   const int group_tiles = (tiles + group_waves - 1) / group_waves;  // workgroups per (slice, KV head)
   const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles,
-                                      (int64_t)waves_per_cu(two_waves) * plan_cus(), nq, mq, two_waves);
+                                      (int64_t)waves_per_cu(two_waves) * plan_cus(), nq, mq, two_waves, scan_cap);
   if (r.workspace_bytes < plan.bytes) {
     set_error("pa_decode: workspace of %zu bytes needed, %zu given", plan.bytes, r.workspace_bytes);
     return PA_ERR_WORKSPACE;
   }
-  if (plan.sub_batch > scan_capacity(mq, two_waves)) {  // cannot happen: plan_decode caps it
+  if (plan.sub_batch > scan_cap) {  // cannot happen: plan_decode caps it
     set_error("pa_decode: internal error: %d sequences per launch exceed the kernel's scan arrays", plan.sub_batch);
     return PA_ERR_HIP;
   }

@@ -37,8 +37,9 @@ int device_cu_count();
 // multi_query: the launch uses the several-queries kernel (fewer sequences per launch).
 // two_waves: the kernel runs two waves per SIMD (twice the slices, half the
 // sequences per launch: mfma_two_waves()).
+// scan_cap: sequences one launch takes at most (0: scan_capacity()).
 DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int64_t waves, int nq,
-                       bool multi_query, bool two_waves);
+                       bool multi_query, bool two_waves, int scan_cap = 0);
 // Workspace bytes that cover every kernel choice and device for these sizes
 // (the most slices a launch can have, either occupancy).
 size_t decode_workspace_bound(int B, int Hkv, int G, int D, int bs, int max_ctx, int nq, bool multi_query);

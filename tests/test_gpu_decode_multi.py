@@ -119,6 +119,18 @@ def test_multi_query_more_sequences_than_one_launch_scans():
     _check_multi(w, seqs=sorted(set(seqs)))
 
 
+def test_prefill_kernel_more_sequences_than_one_launch_takes():
+    """600 sequences of up to 32 queries at G = 4 (128 columns a KV head, the
+    prefill kernel): more than the 512 a prefill launch takes (its query rows
+    and K/V stages fill the rest of LDS), so two launches share the call."""
+    rng = np.random.default_rng(52)
+    lens = [int(x) for x in rng.integers(32, 120, size=600)]
+    nqs = [min(L, int(n)) for L, n in zip(lens, rng.integers(20, 33, size=600))]
+    nqs[0] = 32
+    w = W.multi_query("prefill_many_seqs", 53, lens, nqs, 8, 2, 128, 16, "bf16")
+    _check_multi(w, seqs=[0, 1, 510, 511, 512, 513, 599], label="[two prefill launches]")
+
+
 @pytest.mark.parametrize("cache,D,bs,G", [("bf16", 128, 16, 4), ("f16", 64, 8, 8), ("bf16", 128, 32, 4),
                                           ("f16", 128, 16, 16)])
 @pytest.mark.parametrize("mode", ["1", "2", "3"])

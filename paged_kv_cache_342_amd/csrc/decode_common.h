@@ -49,6 +49,7 @@ inline void launch_with_events(K kernel, dim3 grid, dim3 block, hipStream_t stre
 }
 
 constexpr int kChunk = 32;        // positions per chunk, the unit of the split
+constexpr int kXcds = 8;          // accelerator dies (each with its own L2) that workgroups are dealt to in turn
 constexpr int kScanMax = 4096;    // sequences one launch scans in LDS
 // with several queries per sequence the first query rows are kept in LDS as
 // well; three arrays of this many entries leave room for four waves per CU

@@ -204,9 +204,20 @@ void decode_mfma_kernel(DecodeArgs a) {
   // wave -> (slice, head tile, KV head); the KV head varies fastest, so the
   // workgroups of one KV head land on the same XCD
   // (with NW waves per workgroup, head_tiles counts workgroups per slice and
-  // KV head, and wave wv takes tile pair NW * that + wv)
-  const int h = blockIdx.x % a.Hkv;
-  const int rest = blockIdx.x / a.Hkv;
+  // KV head, and wave wv takes tile pair NW * that + wv).
+  // With row scales the order is XCD-major instead: workgroups go to the
+  // XCDs in turn, so workgroup b runs on XCD b % kXcds and takes item
+  // (b % kXcds) * (N / kXcds) + b / kXcds, and every XCD takes a contiguous
+  // run of items (KV head fastest).  The scale rows of KV heads 2p and
+  // 2p + 1 share one 128-byte line, which is then fetched by one XCD's L2
+  // rather than two.
+  int item = blockIdx.x;
+  if constexpr (RS) {
+    const int n = (int)gridDim.x;
+    if (n % (2 * kXcds) == 0) item = (item % kXcds) * (n / kXcds) + item / kXcds;
+  }
+  const int h = item % a.Hkv;
+  const int rest = item / a.Hkv;
   const int ht = (rest % a.head_tiles) * NW + wv;
   const int k = rest / a.head_tiles;
 

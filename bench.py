@@ -220,10 +220,12 @@ def _identity_layout(w, batch, slots_new):
 
 
 def hbm_ceilings(dev, mib=512, reps=5):
-    """What plain library kernels reach on this device, timed like the step: a
-    device copy of `mib` MiB (read + written bytes counted) and a sum over 1 GiB
-    (read bytes), each after a read of another 1 GiB buffer evicts L2/MALL.
-    The median over `reps`, in GB/s."""
+    """What plain kernels reach on this device, timed like the step: a torch
+    device copy of `mib` MiB (read + written bytes counted), a torch sum over
+    1 GiB (read bytes), and the library's read probe (pa_read_probe: the
+    decode kernels' 16-byte nontemporal loads, each wave streaming its own
+    4 KiB chunks) over 1 GiB, each after a read of another 1 GiB buffer evicts
+    L2/MALL.  The median over `reps`, in GB/s."""
     import numpy as np
     import torch
 
@@ -247,10 +249,15 @@ def hbm_ceilings(dev, mib=512, reps=5):
 
     t_copy = timed(lambda: dst.copy_(src))
     t_read = timed(lambda: big.sum())
+    import paged_kv_cache_342_amd as pa
+    nbytes = big.numel() * 8
+    sink = torch.empty(256, dtype=torch.int32, device=dev)
+    t_probe = timed(lambda: pa.read_probe(big, 4096, sink))
     res = {"copy_gbs": round(2 * src.numel() / t_copy / 1e9, 1), "copy_bytes": 2 * src.numel(),
-           "read_gbs": round(big.numel() * 8 / t_read / 1e9, 1), "read_bytes": big.numel() * 8,
-           "kernels": "torch copy_ and sum"}
-    del evict, src, dst, big
+           "read_gbs": round(nbytes / t_read / 1e9, 1), "read_bytes": nbytes,
+           "probe_read_gbs": round(nbytes / t_probe / 1e9, 1),
+           "kernels": "torch copy_ and sum; pa_read_probe (4 KiB chunks, each wave streaming its own)"}
+    del evict, src, dst, big, sink
     return res
 
 
@@ -521,7 +528,8 @@ def main():
         f"(median {np.median(kern_ms) * 1e3:.1f}), wall/step incl. flush {wall / args.steps * 1e3:.3f} ms")
 
     ceil = hbm_ceilings(dev)
-    log(f"plain copy {ceil['copy_gbs']} GB/s (read + write), plain read {ceil['read_gbs']} GB/s")
+    log(f"plain copy {ceil['copy_gbs']} GB/s (read + write), plain read {ceil['read_gbs']} GB/s, "
+        f"read probe {ceil['probe_read_gbs']} GB/s")
 
     bm = block_manager_bench(w)
     log(f"block manager: {bm['host_us_per_step']} us per step on the host, tail waste {bm['tail_waste']:.4f}")
@@ -567,7 +575,8 @@ def main():
         "step_us_with_kernel_events": round(ms_step_kev * 1e3, 2),
         "graph_replay_us_per_step": None if graph_ms is None else round(graph_ms * 1e3, 2),
         "hbm_copy": {**ceil, "frac_of_copy": round(value / ceil["copy_gbs"], 4),
-                     "frac_of_read": round(value / ceil["read_gbs"], 4)},
+                     "frac_of_read": round(value / ceil["read_gbs"], 4),
+                     "frac_of_probe_read": round(value / ceil["probe_read_gbs"], 4)},
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm",
             "achieved": round(tflops if mfma_bound else achieved, 2),

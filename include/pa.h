@@ -516,6 +516,26 @@ pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* out);
  */
 pa_status pa_time_next_attention_kernel(void* start_event, void* stop_event);
 
+/*
+ * Read-bandwidth probe, for benchmarks: the rate at which the device streams
+ * bytes from HBM with the decode kernels' loads (16-byte nontemporal, 256
+ * workgroups of eight waves, each wave with two batches of eight 1 KiB
+ * loads in flight and whole chunks of chunk_bytes to itself), the measured
+ * ceiling that decode bytes per second are set against.  No attention
+ * arithmetic.
+ *   buf          device buffer (16-byte aligned); its first
+ *                floor(bytes / chunk_bytes) chunks are read once each
+ *   chunk_bytes  a positive multiple of 1024
+ *   sink         device buffer of at least 1024 bytes; it receives a fold of
+ *                the bytes read (one word per workgroup: the XOR of the
+ *                32-bit words it read), which keeps the loads from being
+ *                optimised away
+ * Asynchronous on stream; time it with events.  PA_ERR_INVALID_ARG for a
+ * null or misaligned buffer, a bad chunk size or a small sink.
+ */
+pa_status pa_read_probe(const void* buf, size_t bytes, int32_t chunk_bytes, void* sink, size_t sink_bytes,
+                        pa_stream_t stream);
+
 /* Static description of a status code. */
 const char* pa_status_string(pa_status s);
 

@@ -115,6 +115,8 @@ def _load(path: str) -> ctypes.CDLL:
     lib.pa_decode_append_noalloc.restype = ctypes.c_int
     lib.pa_time_next_attention_kernel.argtypes = [p, p]
     lib.pa_time_next_attention_kernel.restype = ctypes.c_int
+    lib.pa_read_probe.argtypes = [p, ctypes.c_size_t, i32, p, ctypes.c_size_t, p]
+    lib.pa_read_probe.restype = ctypes.c_int
     lib.pa_is_checked_build.argtypes = []
     lib.pa_is_checked_build.restype = ctypes.c_int32
     lib.pa_bm_create.argtypes = [i64, i32]
@@ -534,6 +536,20 @@ def time_next_attention_kernel(start: torch.cuda.Event, stop: torch.cuda.Event) 
         if not ev.cuda_event:  # torch creates the underlying event on its first record
             ev.record()
     _check(library().pa_time_next_attention_kernel(start.cuda_event, stop.cuda_event))
+
+
+def read_probe(buf: torch.Tensor, chunk_bytes: int = 4096, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Stream the bytes of `buf` (a contiguous device tensor) once through the
+    read-bandwidth probe in chunks of `chunk_bytes` (each wave reading whole
+    chunks); returns the sink (per workgroup, the XOR of the 32-bit words it
+    read).  For timing the device's read rate."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(256, dtype=torch.int32, device=buf.device)
+    _check(library().pa_read_probe(_ptr(buf), buf.numel() * buf.element_size(), chunk_bytes, _ptr(sink),
+                                   sink.numel() * sink.element_size(), _stream(buf)))
+    return sink
 
 
 def version() -> str:

@@ -26,7 +26,7 @@ LIB = os.path.join(PKG, "libpa.so")
 LIB_CHECKED = os.path.join(PKG, "libpa_checked.so")
 
 SOURCES = ["pa_api.hip", "pa_noalloc.hip", "decode_core.hip", "decode_mfma.hip", "decode_cascade.hip",
-           "decode_prefill.hip", "decode_valu.hip", "cache_ops.hip"]
+           "decode_prefill.hip", "decode_valu.hip", "cache_ops.hip", "read_probe.hip"]
 HOST_SOURCES = ["block_manager.cpp"]  # host-only C++, built with the host compiler
 CHECKED_SOURCES = ["pa_api.hip", "contract_check.hip"]  # compiled again with PA_CHECKED
 

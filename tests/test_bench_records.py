@@ -54,3 +54,21 @@ def test_records_are_dropped_when_the_sources_change(monkeypatch):
         assert bench.recorded_traffic(key) == _record()["workloads"][key]["hbm_bytes_per_call"]
     monkeypatch.setattr(bench, "decode_source_hash", lambda: "0" * 16)
     assert bench.recorded_traffic(key) is None
+
+
+def test_cascade_and_window_lines_find_their_records():
+    """The shared-prefix cascade line (--cascade) and the sinks-plus-window
+    line (--config llama70b --window 4,2048) are recorded under the workload
+    name with the bench's suffix; the cascade reads each prompt's prefix once,
+    so its bytes are well under the logical bytes of all samples' contexts,
+    and the window line reads about the bytes of the positions it attends."""
+    rec = _record()["workloads"]
+    for key in ("shared_prefix+cascade", "llama70b+window4,2048"):
+        assert key in rec, f"no recorded traffic under {key!r}"
+        assert os.path.exists(os.path.join(ROOT, rec[key]["summary"]))
+    w = bench.select_workload("shared_prefix", 0, False, 0)
+    cas = rec["shared_prefix+cascade"]
+    assert cas["algorithmic_kv_bytes"] == w.kv_bytes()
+    assert cas["hbm_bytes_per_call"] < 0.5 * w.kv_bytes()
+    win = rec["llama70b+window4,2048"]
+    assert 0.9 * win["algorithmic_kv_bytes"] < win["hbm_bytes_per_call"] < 1.5 * win["algorithmic_kv_bytes"]

@@ -4,6 +4,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "decode_common.h"
 #include "pa_internal.h"
@@ -70,28 +71,40 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeArgs a) {
     const int head = h * a.G + i;
     float M = -INFINITY, den = 0.f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < np; p0 += kMergeUnroll) {
-      f32x2 ml[kMergeUnroll];
-      f32x4 x[kMergeUnroll];
+    // pieces in batches of U, their loads issued before any is used
+    auto merge = [&](auto unroll) {
+      constexpr int U = decltype(unroll)::value;
+      for (int p0 = 0; p0 < np; p0 += U) {
+        f32x2 ml[U];
+        f32x4 x[U];
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        const int p = min(p0 + u, np - 1);
-        const int64_t row = part_row(a, kf + p, s, jq, head);
-        ml[u] = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * row);
-        x[u] = *reinterpret_cast<const f32x4*>(a.part_acc + row * D + d);
-      }
+        for (int u = 0; u < U; ++u) {
+          const int p = min(p0 + u, np - 1);
+          const int64_t row = part_row(a, kf + p, s, jq, head);
+          ml[u] = *reinterpret_cast<const f32x2*>(a.part_ml + 2 * row);
+          x[u] = *reinterpret_cast<const f32x4*>(a.part_acc + row * D + d);
+        }
 #pragma unroll
-      for (int u = 0; u < kMergeUnroll; ++u) {
-        if (p0 + u < np && ml[u][0] > -INFINITY) {
-          const float Mn = fmaxf(M, ml[u][0]);
-          const float ca = fast_exp2(M - Mn);
-          const float cb = fast_exp2(ml[u][0] - Mn);
-          den = den * ca + ml[u][1] * cb;
-          num = num * ca + x[u] * cb;
-          M = Mn;
+        for (int u = 0; u < U; ++u) {
+          if (p0 + u < np && ml[u][0] > -INFINITY) {
+            const float Mn = fmaxf(M, ml[u][0]);
+            const float ca = fast_exp2(M - Mn);
+            const float cb = fast_exp2(ml[u][0] - Mn);
+            den = den * ca + ml[u][1] * cb;
+            num = num * ca + x[u] * cb;
+            M = Mn;
+          }
         }
       }
-    }
+    };
+    // (np is the same for the whole workgroup; a batch never loads a piece twice
+    // for the common counts of 2 to 4)
+    if (np <= 2)
+      merge(std::integral_constant<int, 2>());
+    else if (np <= 4)
+      merge(std::integral_constant<int, 4>());
+    else
+      merge(std::integral_constant<int, kMergeUnroll>());
     if constexpr (STATE) {
       const int64_t row = (int64_t)(qrow0 + jq) * a.Hkv * a.G + head;
       *reinterpret_cast<f32x4*>(a.state_acc + row * D + d) = num;

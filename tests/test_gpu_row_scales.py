@@ -184,12 +184,15 @@ def test_decode_with_row_scales_pv_precision(D, q, cd):
 
 
 @pytest.mark.parametrize("cd", ["fp8", "fp4"])
-def test_decode_with_row_scales_heavy_tail_full_size_sampled(cd):
-    """The heavy-tailed batch (256 sequences, log-normal lengths) with rows
-    spread over six decades of magnitude, checked on sampled sequences."""
-    w = W.heavy_tail(bs=16)
-    if cd == "fp4":
-        w = W.custom("heavy_tail_fp4", w.seed, w.context_lens, w.Hq, w.Hkv, w.D, w.bs, "fp4", w.q_dtype)
+@pytest.mark.parametrize("base", ["heavy_tail", "llama8b"])
+def test_decode_with_row_scales_full_size_sampled(base, cd):
+    """The heavy-tailed batch (256 sequences, log-normal lengths) and the
+    8B-shaped batch (64 sequences of 512 to 4,096 positions) at full size, as
+    the row-scale and FP4 bench lines run them, with rows spread over six
+    decades of magnitude, checked on sampled sequences."""
+    w = W.heavy_tail(bs=16) if base == "heavy_tail" else W.llama8b()
+    if cd == "fp4" or base == "llama8b":
+        w = W.custom(f"{base}_{cd}", w.seed, w.context_lens, w.Hq, w.Hkv, w.D, w.bs, cd, w.q_dtype)
     k, v, slots = _rows(w, 3.0, 90)
     (kc, vc, kss, vss), (okc, ovc, oks, ovs) = _pools(w, k, v, slots)
     qd = storage_to_torch(w.query(), w.q_dtype).cuda()
@@ -202,7 +205,7 @@ def test_decode_with_row_scales_heavy_tail_full_size_sampled(cd):
                           w.q_dtype, seqs=seqs, cache_dtype=cd)
     ma, rel = errors(out[seqs], ref)
     bound = _bound(w, w.query(), okc, oks, ovc, ovs, seqs)
-    log(f"[row scales heavy tail {cd}] max_abs={ma:.2e} (bound {bound:.2e}) rel_l2={rel:.2e}")
+    log(f"[row scales {base} {cd}] max_abs={ma:.2e} (bound {bound:.2e}) rel_l2={rel:.2e}")
     assert np.isfinite(out).all() and ma <= bound and rel <= 1e-3
 
 

@@ -63,10 +63,11 @@ def test_window_sweep(cache, q, D, bs):
 @pytest.mark.parametrize("make,sink,window", [
     (lambda: W.llama8b(), 4, 512),
     (lambda: W.llama70b(), 4, 1024),
+    (lambda: W.llama70b(), 4, 2048),
     (lambda: W.llama70b(), 64, 2000),
     (lambda: W.heavy_tail(bs=16), 8, 256),
     (lambda: W.heavy_tail(bs=8), 0, 100),
-], ids=["llama8b_4_512", "llama70b_4_1024", "llama70b_64_2000", "heavy_tail_8_256", "heavy_tail_bs8_0_100"])
+], ids=["llama8b_4_512", "llama70b_4_1024", "llama70b_4_2048", "llama70b_64_2000", "heavy_tail_8_256", "heavy_tail_bs8_0_100"])
 def test_window_full_size_sampled(make, sink, window):
     w = make()
     order = np.argsort(w.context_lens)

@@ -196,3 +196,15 @@ def test_prefill_kernel_shapes(cache, D, bs, G, nq):
     nqs = [min(L, n) for L, n in zip(lens, [nq, nq, nq, nq, nq, nq, 0, nq // 2])]
     w = W.multi_query(f"prefill_{cache}_D{D}_bs{bs}_g{G}_n{nq}", 950 + G + nq, lens, nqs, 2 * G, 2, D, bs, cache)
     _check_multi(w, label="[prefill kernel]")
+
+
+@pytest.mark.parametrize("G,nq", [(3, 100), (5, 60), (6, 90)])
+def test_prefill_kernel_groups_that_do_not_divide_its_columns(G, nq):
+    """Group sizes 3, 5 and 6 through the prefill kernel: its 256 (query, head)
+    columns per workgroup then end inside a query, whose heads fall into two
+    column groups (and a group's last wave may hold dead columns)."""
+    lens = [nq, 2 * nq + 7, 1000, 513, 0, 3000]
+    nqs = [min(L, nq) for L in lens]
+    w = W.multi_query(f"prefill_g{G}", 970 + G, lens, nqs, 2 * G, 2, 128, 16, "bf16")
+    _check_multi(w, label=f"[prefill kernel, G={G}]")
+

@@ -212,7 +212,7 @@ def test_decode_edge_sweep(cache, q, D, bs):
             _check_decode(w, batch=batch, variant=v)
 
 
-@pytest.mark.parametrize("G", [16, 24, 32])
+@pytest.mark.parametrize("G", [3, 5, 6, 16, 24, 32])
 def test_decode_many_heads_per_kv_head(G):
     w = W.custom(f"heads{G}", 7, [5, 300, 777], G, 1, 128, 16, "bf16")
     _check_decode(w)

@@ -506,13 +506,18 @@ pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* out);
 /*
  * Kernel timing, for benchmarks.  start_event and stop_event are hipEvent_t
  * handles the caller created (either may be NULL).  The next pa_decode,
- * pa_decode_append, pa_decode_scaled or pa_decode_multi call on this thread
- * that launches its kernels records start_event when its first attention
- * kernel begins and stop_event when its last attention kernel ends, on the
- * call's stream (the start and stop events of hipExtLaunchKernel), and the
- * pair is then forgotten.  The elapsed time between them is the attention
- * kernel alone: the split merge and an FP8 append lie outside it unless a
- * batch runs as several launches (more than 4,096 sequences).  Always PA_OK.
+ * pa_decode_append, pa_decode_scaled, pa_decode_multi, pa_decode_window or
+ * pa_decode_shared_prefix call on this thread that launches its kernels
+ * records start_event when its first attention kernel begins and stop_event
+ * when its last attention kernel ends, on the call's stream (the start and
+ * stop events of hipExtLaunchKernel), and the pair is then forgotten.  The
+ * elapsed time between them is the attention kernel alone (for
+ * pa_decode_shared_prefix: its prefix pass through its suffix pass, the
+ * merge between them included): the split merge and an FP8 append lie
+ * outside it unless a batch runs as several launches (more sequences than
+ * one launch takes: 4,096 for decode, 3,072 with several queries per
+ * sequence, 2,048 for FP4, 512 for long query chunks on the prefill kernel).
+ * Always PA_OK.
  */
 pa_status pa_time_next_attention_kernel(void* start_event, void* stop_event);
 

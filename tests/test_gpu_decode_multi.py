@@ -208,3 +208,12 @@ def test_prefill_kernel_groups_that_do_not_divide_its_columns(G, nq):
     w = W.multi_query(f"prefill_g{G}", 970 + G, lens, nqs, 2 * G, 2, 128, 16, "bf16")
     _check_multi(w, label=f"[prefill kernel, G={G}]")
 
+
+
+def test_prefill_kernel_at_the_largest_query_count():
+    """1,024 queries per sequence (the most pa_decode_multi takes) at group 4:
+    4,096 (query, head) columns, sixteen 256-column groups of the prefill
+    kernel per KV head, over a whole-sequence prefill and a chunk of a longer
+    sequence."""
+    w = W.multi_query("prefill_max_queries", 990, [1024, 1500, 40], [1024, 1024, 40], 8, 2, 128, 16, "bf16")
+    _check_multi(w, label="[prefill kernel, 1024 queries]")

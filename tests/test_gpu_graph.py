@@ -79,3 +79,35 @@ def test_fp8_row_scale_decode_in_a_graph():
 
     _replays_match(step, out, "decode_scaled")
     assert np.isfinite(out.cpu().numpy()).all()
+
+
+def test_window_decode_in_a_graph():
+    w = W.llama70b(B=6)
+    g = GpuBatch(w)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pa.decode_workspace_size(w.B, w.Hkv, w.group, w.D, w.bs, w.max_context_len), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        pa.decode_window(g.q, g.kc, g.vc, g.tables, g.lens, w.scale, 4, 1024, max_context_len=w.max_context_len,
+                         out=out, workspace=ws)
+
+    _replays_match(step, out, "decode_window")
+
+
+def test_shared_prefix_decode_in_a_graph():
+    """Both passes, the merge between them and the final merge in one graph."""
+    w = W.shared_prefix(prompts=3, samples=4, prefix=700, max_tail=100)
+    g = GpuBatch(w)
+    samples, plen = w.meta["samples"], w.meta["shared_len"]
+    group_start = torch.tensor(np.arange(len(plen) + 1) * samples, dtype=torch.int32, device="cuda")
+    prefix_lens = torch.tensor(np.asarray(plen), dtype=torch.int32, device="cuda")
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(pa.decode_shared_prefix_workspace_size(w.B, len(plen), samples, w.Hkv, w.group, w.D, w.bs,
+                                                            w.max_context_len), dtype=torch.uint8, device="cuda")
+
+    def step():
+        pa.decode_shared_prefix(g.q, g.kc, g.vc, g.tables, g.lens, group_start, prefix_lens, samples, w.scale,
+                                max_context_len=w.max_context_len, out=out, workspace=ws)
+
+    _replays_match(step, out, "decode_shared_prefix")

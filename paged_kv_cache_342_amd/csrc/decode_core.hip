@@ -245,9 +245,11 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   // waves of a workgroup share each K/V chunk through LDS
   const int shared_mode = mq && !rs && (r.cache_dtype == PA_F16 || r.cache_dtype == PA_BF16) ? mq_shared_mode() : 0;
   // the prefill kernel: 256 (query, head) columns per workgroup of kPrefillWaves waves
-  // (it addresses a block with a 32-bit stride)
+  // (it addresses a block with a 32-bit stride, and scales its scores inside
+  // the exponential, which needs a scale > 0; other scales take the
+  // 16-column kernels)
   const bool prefill = shared_mode == 3 && col_tiles >= kSharedWaves1 &&
-                       (int64_t)r.Hkv * r.bs * r.D * 2 <= (int64_t)UINT32_MAX;
+                       (int64_t)r.Hkv * r.bs * r.D * 2 <= (int64_t)UINT32_MAX && r.scale > 0.f;
   const int prefill_groups = (int)(((int64_t)nq * r.G + 255) / 256);
   const bool shared1 = shared_mode == 2 && col_tiles >= kSharedWaves1;  // one tile per wave
   const int tw = mq && col_tiles >= 2 && !shared1 && !prefill ? 2 : 1;

@@ -286,13 +286,12 @@ void prefill_kernel(DecodeArgs a) {
       }
     };
     // online softmax of chunk c's scores (in place: sc holds S^T of the
-    // chunk and leaves with the scaled, masked scores)
+    // chunk and leaves with the masked scores, still unscaled: the weights
+    // apply the scale, which the launch guarantees is > 0, so the largest
+    // scaled score is the scaled largest score)
     auto scores = [&](int c, f32x16& sc) {
       // the lane's slot r is seen if 8 (r / 4) + r % 4 < lim
       const int lim = min(tok_end, qlim + 1) - (tok0 + kChunk * c) - 4 * g2;
-      const float qs = a.qk_scale_log2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] *= qs;
       if (wave_any(lim < 28)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sc[r] = 8 * (r >> 2) + (r & 3) < lim ? sc[r] : -INFINITY;
@@ -300,6 +299,7 @@ void prefill_kernel(DecodeArgs a) {
       float mx = sc[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      mx *= a.qk_scale_log2;
       // both lanes of a column hold the same m; it only moves when a score
       // passes it by more than the threshold
       if (wave_any(mx > m + kRescaleThreshold)) {
@@ -313,14 +313,19 @@ void prefill_kernel(DecodeArgs a) {
     };
     // weights of slots 2 e, 2 e + 1 of product t (the lane's score
     // registers 8 t + 2 e, + 1) as a 16-bit pair (hi) and the pair of what
-    // rounding left (lo); mu is the running maximum made finite (a column
-    // that has seen nothing yet keeps m = -inf: its scores are all -inf and
-    // their weights 0)
-    auto weight_pair = [&](const f32x16& sc, float mu, int t, int e, i32x4& phi, i32x4& plo) {
-      const float q0 = fast_exp2(sc[8 * t + 2 * e] - mu), q1 = fast_exp2(sc[8 * t + 2 * e + 1] - mu);
+    // rounding left (lo); nmu is minus the running maximum made finite (a
+    // column that has seen nothing yet keeps m = -inf: its scores are all
+    // -inf and their weights 0)
+    auto weight_pair = [&](const f32x16& sc, float nmu, int t, int e, i32x4& phi, i32x4& plo) {
+      const float qs = a.qk_scale_log2;
+      const float q0 = fast_exp2(fmaf(sc[8 * t + 2 * e], qs, nmu));
+      const float q1 = fast_exp2(fmaf(sc[8 * t + 2 * e + 1], qs, nmu));
       l += q0 + q1;
       if constexpr (kBf16) {
-        const uint32_t hi = pack_bf16(q0, q1);
+        uint32_t hi = pack_bf16(q0, q1);
+        // opaque to the optimiser, which would otherwise convert q0 a second
+        // time for the low half instead of shifting the pair
+        asm("" : "+v"(hi));
         phi[e] = (int)hi;
         plo[e] = (int)pack_bf16(q0 - __uint_as_float(hi << 16), q1 - __uint_as_float(hi & 0xFFFF0000u));
       } else {
@@ -353,7 +358,7 @@ void prefill_kernel(DecodeArgs a) {
     auto softmax_pv = [&](int c, f32x16& sc, auto with_qk, int cn, f32x16& s_new) {
       constexpr bool kQk = decltype(with_qk)::value;
       scores(c, sc);
-      const float mu = fmaxf(m, -__FLT_MAX__);
+      const float nmu = -fmaxf(m, -__FLT_MAX__);
       const uint32_t sbv = uniform(lds0 + (c % kStages) * kStageBytes);
       i32x4 phi0, plo0, phi1, plo1;
       __builtin_amdgcn_sched_barrier(0);
@@ -373,11 +378,11 @@ void prefill_kernel(DecodeArgs a) {
           }
           s_new = mfma32x32<CT>(ko[kk], qo[kk], s_new);
           __builtin_amdgcn_sched_barrier(0);
-          if ((kk * 4) % KS == 0) weight_pair(sc, mu, 0, kk * 4 / KS, phi0, plo0);  // the four pairs over the KS products
+          if ((kk * 4) % KS == 0) weight_pair(sc, nmu, 0, kk * 4 / KS, phi0, plo0);  // the four pairs over the KS products
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) weight_pair(sc, mu, 0, e, phi0, plo0);
+        for (int e = 0; e < 4; ++e) weight_pair(sc, nmu, 0, e, phi0, plo0);
       }
       __builtin_amdgcn_sched_barrier(0);
       // product 0 of PV beside the product-1 weights
@@ -392,10 +397,10 @@ void prefill_kernel(DecodeArgs a) {
           acc[E] = mfma32x32<CT>(vo[E], phi0, acc[E]);
           if constexpr (kBf16) acc[E] = mfma32x32<CT>(vo[E], plo0, acc[E]);
           __builtin_amdgcn_sched_barrier(0);
-          weight_pair(sc, mu, 1, E, phi1, plo1);
+          weight_pair(sc, nmu, 1, E, phi1, plo1);
         }
 #pragma unroll
-        for (int e = DB; e < 4; ++e) weight_pair(sc, mu, 1, e, phi1, plo1);
+        for (int e = DB; e < 4; ++e) weight_pair(sc, nmu, 1, e, phi1, plo1);
       }
       __builtin_amdgcn_sched_barrier(0);
       // product 1 of PV

@@ -217,3 +217,38 @@ def test_prefill_kernel_at_the_largest_query_count():
     sequence."""
     w = W.multi_query("prefill_max_queries", 990, [1024, 1500, 40], [1024, 1024, 40], 8, 2, 128, 16, "bf16")
     _check_multi(w, label="[prefill kernel, 1024 queries]")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_prefill_kernel_slices_of_many_short_sequences(seed):
+    """300 short sequences (0-200 positions, 0-32 queries, some without
+    queries and some empty) at group 4: a workgroup's slice then walks
+    several sequences in a row, with one to seven 32-position chunks each,
+    and requests a sequence's first chunks and query rows while it still
+    works on the one before.  Every sequence against the oracle."""
+    rng = np.random.default_rng(1200 + seed)
+    lens = [int(x) for x in rng.integers(0, 201, size=300)]
+    nqs = [min(L, int(n)) for L, n in zip(lens, rng.integers(0, 33, size=300))]
+    for i in range(0, 300, 7):
+        nqs[i] = 0
+    lens[5] = 0
+    nqs[5] = 0
+    lens[1] = max(lens[1], 64)
+    nqs[1] = 32  # 128 columns a KV head: the prefill kernel
+    w = W.multi_query(f"prefill_short_seqs{seed}", 1210 + seed, lens, nqs, 8, 2, 128, 16, "bf16")
+    g, out = _check_multi(w, label="[prefill kernel, many short sequences]")
+    again = g.decode_multi().cpu().numpy()
+    assert np.array_equal(out.astype(np.float32), again)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.088, 1e-3, 0.5])
+def test_prefill_shapes_at_any_scale(scale):
+    """Query chunks the prefill kernel takes, at scales of either sign: the
+    prefill kernel applies a positive scale inside its exponentials; a zero
+    or negative one (the weights then favour the smallest scores, or are all
+    equal) goes to the 16-column kernels.  Every case against the oracle."""
+    lens = [64, 300, 1031, 2050]
+    nqs = [64, 64, 40, 64]
+    w = W.multi_query(f"prefill_scale_{scale}", 1300, lens, nqs, 8, 2, 128, 16, "bf16")
+    w.scale = float(scale)
+    _check_multi(w, label=f"[scale {scale}]")

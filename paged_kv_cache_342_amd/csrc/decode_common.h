@@ -62,16 +62,21 @@ constexpr int kScanMaxMQ2 = 1536;
 // the arrays, which leaves room for this many sequences per launch.
 constexpr int kScanPrefill = 512;
 
-// Which MFMA kernels run two waves per SIMD: FP4.  Its waves are bound by
-// instruction issue at one wave per SIMD (5% of their cycles waiting on
-// memory), and its registers fit the 256 of two waves without spilling; a
-// second wave per SIMD took the FP4 decode of the 8B-shaped and the
-// heavy-tailed batches 15-16% faster.  fp8 with a scale per tensor also
-// fits, but measured 4% slower there (twice the slices, so more segments
-// per wave).  The host sizes launches (scan capacity, slices) with the same
-// rule.
-__host__ __device__ constexpr bool mfma_two_waves(int cache_code, bool row_scales, int tiles_per_wave) {
-  return cache_code == 4 && row_scales && tiles_per_wave == 1;
+// Which MFMA kernels run two waves per SIMD.  FP4 with row scales: its waves
+// are bound by instruction issue at one wave per SIMD (5% of their cycles
+// waiting on memory), and its registers fit the 256 of two waves without
+// spilling; a second wave per SIMD took the FP4 decode of the 8B-shaped and
+// the heavy-tailed batches 15-16% faster.  fp8 with a scale per tensor at
+// block size 8, one query per sequence and not a cascade pass (plain; a
+// window included, so that a window covering every position still gives
+// decode's bits): a chunk spans four blocks there, and the second wave hides
+// their loads (heavy-tailed batch 107 -> 99 us); at block sizes 16 and 32 it
+// was 1-2% slower (twice the slices, so more segments per wave).  The host
+// sizes launches (scan capacity, slices) with the same rule.
+__host__ __device__ constexpr bool mfma_two_waves(int cache_code, bool row_scales, int tiles_per_wave,
+                                                  int block_size, bool plain) {
+  return tiles_per_wave == 1 && ((cache_code == 4 && row_scales) ||
+                                 (cache_code == 3 && !row_scales && plain && block_size == 8));
 }
 __host__ __device__ constexpr int scan_capacity(bool multi_query, bool two_waves) {
   return two_waves ? (multi_query ? kScanMaxMQ2 : kScanMax2) : (multi_query ? kScanMaxMQ : kScanMax);

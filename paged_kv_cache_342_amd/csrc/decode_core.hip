@@ -255,7 +255,7 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const int tw = mq && col_tiles >= 2 && !shared1 && !prefill ? 2 : 1;
   // waves per (slice, KV head)
   const int tiles = prefill ? prefill_groups * kPrefillWavesHost : (col_tiles + tw - 1) / tw;
-  const bool two_waves = !valu && (prefill || shared1 || mfma_two_waves(r.cache_dtype, rs, tw));
+  const bool two_waves = !valu && (prefill || shared1 || mfma_two_waves(r.cache_dtype, rs, tw, r.bs, !mq));
   const int scan_cap = prefill ? kScanPrefill : scan_capacity(mq, two_waves);
   const bool shared = shared1 || (shared_mode >= 1 && tw == 2 && tiles >= kSharedWaves);
   const int group_waves = prefill ? kPrefillWavesHost : (shared1 ? kSharedWaves1 : (shared ? kSharedWaves : 1));

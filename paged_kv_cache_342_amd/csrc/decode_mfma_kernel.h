@@ -117,9 +117,9 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <class CT, bool RS, int TW, int NW>
+template <class CT, bool RS, int TW, int NW, int BS, bool PLAIN>
 struct MfmaWaves {
-  static constexpr int value = (NW == kSharedWaves1 || mfma_two_waves(CT::code, RS, TW)) ? 2 : 1;
+  static constexpr int value = (NW == kSharedWaves1 || mfma_two_waves(CT::code, RS, TW, BS, PLAIN)) ? 2 : 1;
 };
 
 // NW > 1 (several queries per sequence, 16-bit caches): a workgroup of NW
@@ -156,7 +156,8 @@ constexpr int kSuffixPass = 2;
 
 template <class CT, class QT, int D, int BS, bool MQ, bool RS, int TW, int NW = 1, bool WIN = false,
           int CAS = kPlainPass>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MfmaWaves<CT, RS, TW, NW>::value)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(MfmaWaves<CT, RS, TW, NW, BS, !MQ && CAS == kPlainPass>::value)))
 void decode_mfma_kernel(DecodeArgs a) {
   static_assert(!WIN || (!MQ && !RS && NW == 1), "windows: one query per sequence, a scale per tensor");
   static_assert(CAS != kPrefixPass || (MQ && !RS && NW == 1), "the prefix pass is a several-queries launch");
@@ -180,7 +181,8 @@ void decode_mfma_kernel(DecodeArgs a) {
   constexpr bool kCanAppend = !kFp8 && !kFp4;  // new rows are stored as given
   constexpr int kRowLanes = RB / 16;  // lanes that hold one row, 16 bytes each
 
-  constexpr int kScan = scan_capacity(MQ || kStarts, MfmaWaves<CT, RS, TW, NW>::value == 2);
+  constexpr int kScan =
+      scan_capacity(MQ || kStarts, MfmaWaves<CT, RS, TW, NW, BS, !MQ && CAS == kPlainPass>::value == 2);
   __shared__ int cum[kScan + 1];
   __shared__ int lens[kScan];
   __shared__ int qrow[(MQ || kStarts) ? kScan + 1 : 1];

@@ -479,61 +479,75 @@ void decode_mfma_kernel(DecodeArgs a) {
         }
       }
       i32x4 pop[TW], plo[TW];
+      // The softmax of the chunk's scores, written for a chunk some of whose
+      // positions a column does not see (masked) and for one whose positions
+      // every column sees: with one query per sequence and no window, every
+      // chunk of a segment but its last (the selects and checks skipped).
+      auto softmax = [&](auto masked) {
+        constexpr bool kM = decltype(masked)::value;
 #pragma unroll
-      for (int t = 0; t < TW; ++t) {
-        // ---- online softmax for this lane's column (head) of tile t, positions j
-        float sc[8];
-        float mx = -INFINITY;
+        for (int t = 0; t < TW; ++t) {
+          // ---- online softmax for this lane's column (head) of tile t, positions j
+          float sc[8];
+          float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float raw_s = (j < 4 ? s0[t][j & 3] : s1[t][j & 3]) * a.qk_scale_log2;
-          if constexpr (RS) raw_s *= scl.k[j >> 2][j & 3];
-          const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
-          const bool seen = ctok + tc < tok_end && (!MQ || ctok + tc <= qlim[t]) &&
-                            (!WIN || ctok + tc < win_sink || ctok + tc + win_shift >= win_lo);
-          sc[j] = seen ? raw_s : -INFINITY;
-          mx = fmaxf(mx, sc[j]);
-        }
-        if (wave_any(mx > m[t] + kRescaleThreshold)) {
-          mx = fmaxf(mx, shfl_xor(mx, 16));
-          mx = fmaxf(mx, shfl_xor(mx, 32));
-          const float mn = fmaxf(m[t], mx);
-          // under MQ or a window a column may have seen no position yet (mn = -inf)
-          const float alpha = (kMasked && mn == -INFINITY) ? 1.f : fast_exp2(m[t] - mn);
+          for (int j = 0; j < 8; ++j) {
+            float raw_s = (j < 4 ? s0[t][j & 3] : s1[t][j & 3]) * a.qk_scale_log2;
+            if constexpr (RS) raw_s *= scl.k[j >> 2][j & 3];
+            const int tc = 16 * (j >> 2) + 4 * gq + (j & 3);
+            const bool seen = !kM || (ctok + tc < tok_end && (!MQ || ctok + tc <= qlim[t]) &&
+                                      (!WIN || ctok + tc < win_sink || ctok + tc + win_shift >= win_lo));
+            sc[j] = seen ? raw_s : -INFINITY;
+            mx = fmaxf(mx, sc[j]);
+          }
+          if (wave_any(mx > m[t] + kRescaleThreshold)) {
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            const float mn = fmaxf(m[t], mx);
+            // under MQ or a window a column may have seen no position yet (mn = -inf)
+            const float alpha = (kMasked && mn == -INFINITY) ? 1.f : fast_exp2(m[t] - mn);
 #pragma unroll
-          for (int i = 0; i < W; ++i) acc[t][i] *= alpha;
-          l[t] *= alpha;
-          m[t] = mn;
-        }
-        float p[8];
+            for (int i = 0; i < W; ++i) acc[t][i] *= alpha;
+            l[t] *= alpha;
+            m[t] = mn;
+          }
+          float p[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = (kMasked && sc[j] == -INFINITY) ? 0.f : fast_exp2(sc[j] - m[t]);
-          l[t] += p[j];
-        }
-        // ---- P as the B operand of PV (weighted by the V rows' scales under
-        // RS; a masked position's scale may belong to a slot never written, so
-        // its weight is set, not computed)
-        float pw[8];
+          for (int j = 0; j < 8; ++j) {
+            p[j] = (kMasked && sc[j] == -INFINITY) ? 0.f : fast_exp2(sc[j] - m[t]);
+            l[t] += p[j];
+          }
+          // ---- P as the B operand of PV (weighted by the V rows' scales under
+          // RS; a masked position's scale may belong to a slot never written, so
+          // its weight is set, not computed)
+          float pw[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if constexpr (RS)
-            pw[j] = sc[j] == -INFINITY ? 0.f : p[j] * scl.v[j >> 2][j & 3];
-          else
-            pw[j] = p[j];
-        }
+          for (int j = 0; j < 8; ++j) {
+            if constexpr (RS)
+              pw[j] = (kM && sc[j] == -INFINITY) ? 0.f : p[j] * scl.v[j >> 2][j & 3];
+            else
+              pw[j] = p[j];
+          }
 #pragma unroll
-        for (int jp = 0; jp < 4; ++jp) {
-          if constexpr (kBf16V) {
-            const uint32_t hi = pack_bf16(pw[2 * jp], pw[2 * jp + 1]);
-            const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
-            pop[t][jp] = (int)hi;
-            plo[t][jp] = (int)pack_bf16(pw[2 * jp] - h0, pw[2 * jp + 1] - h1);
-          } else {
-            pop[t][jp] = (int)pack_f16(pw[2 * jp], pw[2 * jp + 1]);
+          for (int jp = 0; jp < 4; ++jp) {
+            if constexpr (kBf16V) {
+              uint32_t hi = pack_bf16(pw[2 * jp], pw[2 * jp + 1]);
+              // opaque to the optimiser, which would otherwise convert the
+              // first weight a second time instead of shifting the pair
+              asm("" : "+v"(hi));
+              const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xFFFF0000u);
+              pop[t][jp] = (int)hi;
+              plo[t][jp] = (int)pack_bf16(pw[2 * jp] - h0, pw[2 * jp + 1] - h1);
+            } else {
+              pop[t][jp] = (int)pack_f16(pw[2 * jp], pw[2 * jp + 1]);
+            }
           }
         }
-      }
+      };
+      if (!MQ && !WIN && ctok + kChunk <= tok_end)
+        softmax(std::false_type());
+      else
+        softmax(std::true_type());
       // ---- V^T as the A operand: 16-bit values per position, then transpose
       uint32_t vt[8][W / 2];
 #pragma unroll

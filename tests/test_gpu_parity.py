@@ -446,3 +446,25 @@ def test_decode_more_sequences_than_one_launch_scans():
     log(f"[4100 sequences] max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert np.isfinite(out).all()
     assert ma <= 2e-3 and rel <= 1e-3
+
+
+def test_fp8_block_size_8_more_sequences_than_one_launch_scans():
+    """fp8 at block size 8 runs two waves per SIMD, whose launches scan 2,048
+    sequences: 2,100 sequences run as two launches, checked on a sample around
+    the boundary; a window covering every position gives the same bits (the
+    window kernel runs at the same occupancy and launch split)."""
+    lens = [int(x) for x in np.random.default_rng(14).integers(0, 60, size=2100)]
+    w = W.custom("many_seqs_fp8_bs8", 15, lens, 8, 2, 128, 8, "fp8")
+    g = GpuBatch(w)
+    out = g.decode()
+    got = out.cpu().numpy().astype(np.float64)
+    seqs = [0, 1, 2046, 2047, 2048, 2049, 2099] + [int(i) for i in np.nonzero(np.array(lens) == 0)[0][:2]]
+    kc, vc = OH.build_pools(w, seqs=seqs)
+    ref = OH.decode(w, kc, vc, seqs=seqs)
+    ma, _ = errors(got[seqs], ref)
+    log(f"[2100 sequences, fp8 bs 8] max_abs={ma:.3e}")
+    assert np.isfinite(got).all()
+    assert ma <= 3e-2
+    win = pa.decode_window(g.q, g.kc, g.vc, g.tables, g.lens, w.scale, 0, 1 << 20, max_context_len=w.max_context_len,
+                           k_scale=w.k_scale, v_scale=w.v_scale, out_dtype=torch.float32)
+    assert torch.equal(win.view(torch.int32), out.view(torch.int32))

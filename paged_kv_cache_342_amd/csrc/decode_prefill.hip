@@ -10,11 +10,11 @@
 // column / G, its head column % G).
 //   - At a sequence's start each wave sends its 32 query rows to LDS.
 //   - K and V rows of each 32-position chunk go from HBM into one of
-//     kStages LDS stages kAhead chunks before K is used.  Every wave issues
-//     the same instructions for every chunk, so waiting on the vector memory
-//     counter until only the later chunks' instructions are outstanding,
-//     then a barrier, makes a chunk visible; block ids come through scalar
-//     loads, which that counter does not see.  Rows keep their natural
+//     kStages LDS stages, two per even step, two and three steps before K
+//     is used.  Every even step waits on the vector memory counter for all
+//     of the wave's requests, then a barrier makes the two chunks visible to
+//     every wave; odd steps neither wait nor synchronise.  Block ids come
+//     through scalar loads, which that counter does not see.  Rows keep their natural
 //     layout with the 16-byte pieces of each row permuted (an XOR of the
 //     piece index with a function of the row), so that the operand reads
 //     below hit every bank once.
@@ -142,7 +142,6 @@ void prefill_kernel(DecodeArgs a) {
   constexpr int kTensorBytes = kChunk * RB;   // a chunk's K (or V) rows; also a wave's 32 query rows
   constexpr int kStageBytes = 2 * kTensorBytes;  // K rows, then V rows
   constexpr int kStages = 5;
-  constexpr int kAhead = kStages - 2;         // the DMA of chunk i + kAhead is issued at step i
 
   constexpr int kScan = kScanPrefill;
   __shared__ int cum[kScan + 1];
@@ -420,13 +419,10 @@ void prefill_kernel(DecodeArgs a) {
 
     // The wave's query rows go to LDS by DMA (a row per column, the layout
     // of the K rows; a column past the queries reads the first query row).
-    // Then step i: chunk i's rows are in LDS (this wave's instructions are
-    // done once at most those of the later chunks are outstanding; the
-    // barrier makes every wave's visible and ends every read of step i - 1);
-    // the DMA of chunk i + kAhead goes into the stage chunk i - 2 left; then
-    // S of chunk i beside the softmax and PV of chunk i - 1.  The last step
-    // waits for every DMA of the segment, so the next one starts with its
-    // stages free.
+    // Then step i computes S of chunk i beside the softmax and PV of chunk
+    // i - 1 (it reads the stages of chunks i - 1 and i), and every chunk's
+    // DMA is waited for by an even step no later than its own, so the next
+    // segment starts with nothing outstanding.
     __builtin_amdgcn_s_barrier();  // every wave is done with the stages of the last segment
 #pragma unroll
     for (int n = 0; n < kChunk / kRowsPerDma; ++n) {
@@ -439,42 +435,49 @@ void prefill_kernel(DecodeArgs a) {
       const int piece = (lane % PR) ^ swz_k<PR>(row);
       dma16(reinterpret_cast<const uint8_t*>(a.q) + (qr * Hq + qh) * RB + 16 * piece, qlds + 1024 * n);
     }
-    // block ids of the first kAhead + 1 chunks (their scalar loads issued
-    // together), then the DMA of the first kAhead chunks
-    int ids0[kAhead + 1][kDmaPerWave];
+    // block ids of the first four chunks (their scalar loads issued
+    // together), then the DMA of the first two
+    int ids0[2][kDmaPerWave], idn[2][kDmaPerWave];
 #pragma unroll
-    for (int c = 0; c <= kAhead; ++c) chunk_ids(c, ids0[c]);
+    for (int c = 0; c < 2; ++c) {
+      chunk_ids(c, ids0[c]);
+      chunk_ids(c + 2, idn[c]);
+    }
 #pragma unroll
-    for (int c = 0; c < kAhead; ++c)
+    for (int c = 0; c < 2; ++c)
       if (c < nchunks) dma(c, ids0[c]);
-    // table entries of the chunk a step sends (ida, idb alternate between
-    // the steps, so no loaded value is copied before it is used)
-    int ida[kDmaPerWave], idb[kDmaPerWave];
-#pragma unroll
-    for (int u = 0; u < kDmaPerWave; ++u) ida[u] = ids0[kAhead][u];
     f32x16 sa, sb;
-    auto step = [&](int i, auto first, f32x16& s_prev, f32x16& s_new, const int* ids_use, int* ids_load) {
-      // this wave's DMAs issued after those of chunk i: min(kAhead - 1,
-      // nchunks - 1 - i) chunks' worth
-      wait_vm_groups<kDmaPerWave, kAhead - 1>(nchunks - 1 - i);
-      __builtin_amdgcn_s_barrier();
-      if (i + kAhead < nchunks) {
-        chunk_ids(i + kAhead + 1, ids_load);  // scalar loads, used by the next step
-        dma(i + kAhead, ids_use);
+    // Even steps wait for every DMA the wave issued (chunks i and i + 1,
+    // requested at step i - 2), and the barrier makes all waves' rows
+    // visible and ends every read of steps i - 2 and i - 1; they then send
+    // chunks i + 2 and i + 3 into the stages chunks i - 3 and i - 2 left.
+    // Odd steps need neither: their chunk landed before the last barrier.
+    // They load the block ids the next even step sends (idn is read at the
+    // start of an even step and loaded again at the odd step after it, so
+    // no loaded value is copied).
+    auto step = [&](int i, auto even, auto first, f32x16& s_prev, f32x16& s_new) {
+      if constexpr (decltype(even)::value) {
+        wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        if (i + 2 < nchunks) dma(i + 2, idn[0]);
+        if (i + 3 < nchunks) dma(i + 3, idn[1]);
+      } else {
+        chunk_ids(i + 3, idn[0]);  // scalar loads, used by step i + 1
+        chunk_ids(i + 4, idn[1]);
       }
       if constexpr (decltype(first)::value)
         qk(0, s_new);
       else
         softmax_pv(i - 1, s_prev, std::true_type(), i, s_new);
     };
-    step(0, std::true_type(), sb, sa, ida, idb);
+    step(0, std::true_type(), std::true_type(), sb, sa);
     int i = 1;
     for (; i + 1 < nchunks; i += 2) {
-      step(i, std::false_type(), sa, sb, idb, ida);
-      step(i + 1, std::false_type(), sb, sa, ida, idb);
+      step(i, std::false_type(), std::false_type(), sa, sb);
+      step(i + 1, std::true_type(), std::false_type(), sb, sa);
     }
     if (i < nchunks) {  // i = nchunks - 1: S of chunk i - 1 in sa
-      step(i, std::false_type(), sa, sb, idb, ida);
+      step(i, std::false_type(), std::false_type(), sa, sb);
       softmax_pv(i, sb, std::false_type(), 0, sa);
     } else {            // i = nchunks: S of chunk i - 1 in sa
       softmax_pv(i - 1, sa, std::false_type(), 0, sb);

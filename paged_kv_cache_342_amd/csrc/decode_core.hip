@@ -135,11 +135,22 @@ int device_cu_count() {
 // compute units a launch plans with: the device's, at most kPlanMaxCUs
 static int plan_cus() { return std::min(device_cu_count(), kPlanMaxCUs); }
 
-// virtual chunks a sequence is charged on the line for its fixed costs
-static int segment_cost() {
+// virtual chunks a sequence is charged on the line for its fixed costs: the
+// kernel's own charge unless PA_DECODE_SEGMENT_COST gives one
+static int segment_cost(int charge) {
   const char* v = std::getenv("PA_DECODE_SEGMENT_COST");
   const int n = v ? std::atoi(v) : -1;
-  return n >= 0 && n <= 64 ? n : 2;
+  return n >= 0 && n <= 64 ? n : charge;
+}
+
+// The charge per sequence: 2 chunks, and 3 for fp8 caches at one wave per
+// SIMD with one query per sequence, whose loop runs ~1.5 us a chunk against a
+// segment's fixed costs.  Measured on the heavy-tailed fp8 batch (A/B on one
+// machine), 3 against 2: block size 16 kernel 95.0 -> 92.7 us, block size 32
+// 92.7 -> 89.8 us, with a scale per row 109.3 -> 107.8 us; 4 and 1 were
+// worse, and the 16-bit lines and fp8 at two waves per SIMD were best at 2.
+static int sequence_charge(int cache_dtype, bool two_waves, bool multi_query) {
+  return cache_dtype == PA_FP8_E4M3 && !two_waves && !multi_query ? 3 : 2;
 }
 
 // waves the grid gives each CU: one per SIMD, or two for the kernels that
@@ -152,13 +163,13 @@ static int waves_per_cu(bool two_waves) {
 }
 
 DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int64_t waves, int nq,
-                       bool multi_query, bool two_waves, int scan_cap) {
+                       bool multi_query, bool two_waves, int scan_cap, int charge) {
   (void)bs;
   DecodePlan p{};
   const int64_t per = (int64_t)Hkv * head_tiles;
   p.nslices = (int)std::max<int64_t>(1, (waves + per - 1) / per);
   p.min_slice = 4;
-  p.seg_cost = segment_cost();
+  p.seg_cost = segment_cost(charge);
   const int64_t chunks = ((int64_t)std::max(max_ctx, 1) + kChunk - 1) / kChunk + p.seg_cost;
   // the kernel's LDS scan arrays bound the sequences of one launch
   int64_t sub = std::min<int64_t>(scan_cap > 0 ? scan_cap : scan_capacity(multi_query, two_waves), INT_MAX / chunks);
@@ -261,7 +272,8 @@ pa_status decode_launch(const DecodeRequest& r, hipStream_t stream) {
   const int group_waves = prefill ? kPrefillWavesHost : (shared1 ? kSharedWaves1 : (shared ? kSharedWaves : 1));
   const int group_tiles = (tiles + group_waves - 1) / group_waves;  // workgroups per (slice, KV head)
   const DecodePlan plan = plan_decode(r.B, r.Hkv, r.G, r.D, r.bs, r.plan_ctx, tiles,
-                                      (int64_t)waves_per_cu(two_waves) * plan_cus(), nq, mq, two_waves, scan_cap);
+                                      (int64_t)waves_per_cu(two_waves) * plan_cus(), nq, mq, two_waves, scan_cap,
+                                      sequence_charge(r.cache_dtype, two_waves, mq));
   if (r.workspace_bytes < plan.bytes) {
     set_error("pa_decode: workspace of %zu bytes needed, %zu given", plan.bytes, r.workspace_bytes);
     return PA_ERR_WORKSPACE;

@@ -38,8 +38,11 @@ int device_cu_count();
 // two_waves: the kernel runs two waves per SIMD (twice the slices, half the
 // sequences per launch: mfma_two_waves()).
 // scan_cap: sequences one launch takes at most (0: scan_capacity()).
+// charge: chunks each sequence is charged on the line for its fixed costs
+// (PA_DECODE_SEGMENT_COST overrides it); a larger charge never enlarges the
+// workspace.
 DecodePlan plan_decode(int B, int Hkv, int G, int D, int bs, int max_ctx, int head_tiles, int64_t waves, int nq,
-                       bool multi_query, bool two_waves, int scan_cap = 0);
+                       bool multi_query, bool two_waves, int scan_cap = 0, int charge = 2);
 // Workspace bytes that cover every kernel choice and device for these sizes
 // (the most slices a launch can have, either occupancy).
 size_t decode_workspace_bound(int B, int Hkv, int G, int D, int bs, int max_ctx, int nq, bool multi_query);

@@ -516,7 +516,8 @@ pa_status pa_bm_get_stats(const pa_block_manager* bm, pa_bm_stats* out);
  * merge between them included): the split merge and an FP8 append lie
  * outside it unless a batch runs as several launches (more sequences than
  * one launch takes: 4,096 for decode, 3,072 with several queries per
- * sequence, 2,048 for FP4, 512 for long query chunks on the prefill kernel).
+ * sequence, 2,048 for FP4 and for fp8 at block size 8, 512 for long query
+ * chunks on the prefill kernel).
  * Always PA_OK.
  */
 pa_status pa_time_next_attention_kernel(void* start_event, void* stop_event);
